@@ -1,0 +1,293 @@
+"""Pins of the oracle's scalar codecs, random stream and rotation.
+
+Each test checks the oracle against something other than itself: the grid the
+pages print, hand-derived fixtures, an independent library (PyTorch's float8
+casts, ATen's Philox engine, SciPy's Hadamard matrix), published known-answer
+vectors, or a differently derived algorithm.
+"""
+import math
+import os
+import struct
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+from golden_io import fields, rows
+
+
+def f32(x):
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def f32_bits(x):
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def bits_f32(u):
+    return struct.unpack("<f", struct.pack("<I", u))[0]
+
+
+# ------------------------------------------------------------------ E2M1
+def test_e2m1_grid_is_the_pages_grid(orc):
+    # Robots Atlas, "FP4", Components / E2M1 format: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    assert [orc.e2m1_value(c) for c in range(8)] == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert [orc.e2m1_value(8 | c) for c in range(8)] == [-0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
+    assert math.copysign(1.0, orc.e2m1_value(8)) == -1.0
+
+
+def test_e2m1_rtn_midpoints_fixture(orc):
+    for a, code, val in rows("e2m1_rtn_ties.txt"):
+        assert orc.e2m1_rtn_mag(float(a)) == int(code), a
+        assert orc.e2m1_value(int(code)) == float(val)
+
+
+def _rtn_by_mantissa_rounding(a):
+    """Independent derivation: E2M1 has one mantissa bit, so for a >= 1 round
+    the fp32 significand to 1 bit (round half to even via integer carry); below
+    1 the spacing is 0.5 (numpy rint is half-to-even)."""
+    if a < 1.0:
+        return float(np.rint(np.float32(a) * np.float32(2))) / 2.0
+    u = f32_bits(a)
+    u = (u + 0x1FFFFF + ((u >> 22) & 1)) & 0xFFC00000
+    return min(bits_f32(u), 6.0)
+
+
+def test_e2m1_rtn_matches_mantissa_rounding(orc):
+    vals = set()
+    for e in range(-12, 3):                    # binades 2^-12 .. 2^2 (covers (0, 6])
+        for m in range(0, 1 << 23, 1 << 12):   # 2048 significands per binade
+            v = bits_f32(((e + 127) << 23) | m)
+            if v <= 6.0:
+                vals.add(v)
+    for mid in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+        u = f32_bits(mid)
+        vals.update({mid, bits_f32(u - 1), bits_f32(u + 1)})
+    vals.update({0.0, 6.0})
+    for a in sorted(vals):
+        got = orc.e2m1_value(orc.e2m1_rtn_mag(a))
+        assert got == _rtn_by_mantissa_rounding(a), a
+
+
+# ------------------------------------------------------------------ E4M3
+def test_e4m3_decode_matches_torch(orc):
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    for b in range(256):
+        v = orc.e4m3_value(b)
+        if math.isnan(t[b]):
+            assert math.isnan(v), b
+        else:
+            assert v == float(t[b]), b
+    assert orc.e4m3_value(0x7E) == 448.0          # largest finite value
+
+
+def _e4m3_sweep():
+    vals = set()
+    for e in range(-20, 9):
+        for m in range(0, 1 << 23, 1 << 14):
+            v = bits_f32(((e + 127) << 23) | m)
+            if v <= 464.0:
+                vals.add(v)
+    # every midpoint between neighbouring E4M3 values, and one ulp either side
+    pos = sorted({float(v) for v in torch.arange(0x7F, dtype=torch.uint8)
+                  .view(torch.float8_e4m3fn).float().numpy()})
+    for lo, hi in zip(pos, pos[1:]):
+        mid = f32((lo + hi) / 2)
+        u = f32_bits(mid)
+        vals.update({mid, bits_f32(u - 1), bits_f32(u + 1)})
+    vals.update({0.0, 448.0, 464.0})
+    return sorted(vals)
+
+
+def test_e4m3_encode_matches_torch_cast(orc):
+    # PyTorch's float8_e4m3fn cast rounds to nearest even and agrees with a
+    # saturating encoder on [0, 464] (above 464 it gives NaN, which the
+    # block-scale rule never asks for).
+    vals = _e4m3_sweep()
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, r in zip(vals, ref):
+        assert orc.e4m3_encode(v) == int(r), v
+
+
+def test_e4m3_encode_saturates(orc):
+    for v in (448.0, 449.0, 463.99, 464.0, 465.0, 1e6, 3.0e38):
+        assert orc.e4m3_encode(v) == 0x7E
+
+
+# ------------------------------------------------------------------ E8M0
+def test_e8m0_decode_matches_torch(orc):
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).float().numpy()
+    for b in range(255):
+        assert orc.e8m0_value(b) == float(t[b]) or (b == 0 and orc.e8m0_value(0) == 2.0 ** -127)
+    assert math.isnan(orc.e8m0_value(255))
+
+
+def test_e8m0_exponent_integer_form(orc):
+    # Independent derivation of the round-up rule: write amax = m * 2^E with
+    # m in [1, 2). Then 6 * 2^e >= amax holds first at e = E - 2 when m <= 1.5
+    # and at e = E - 1 otherwise; clamp below at -127.
+    rng = np.random.default_rng(5)
+    vals = list(np.float32(rng.uniform(0.5, 2.0, 4000)) * np.float32(2.0) **
+                rng.integers(-140, 120, 4000).astype(np.float32))
+    for E in range(-126, 127):
+        for m in (1.0, 1.5, f32(1.5 + 2 ** -22), 1.25, f32(2 - 2 ** -23)):
+            vals.append(f32(m * 2.0 ** E))
+    vals += [0.0, 1e-45, 6.0, 3.0, f32(3.0 + 2 ** -21), 3.4e38]
+    for a in vals:
+        a = float(np.float32(a))
+        if a == 0.0 or not np.isfinite(a):
+            exp = -127
+        else:
+            m, E = math.frexp(a)      # a = m * 2^E, m in [0.5, 1)
+            m, E = m * 2, E - 1       # m in [1, 2)
+            exp = E - 2 if m <= 1.5 else E - 1
+            exp = max(exp, -127)
+        assert orc.e8m0_exponent(a) == exp, a
+
+
+# ------------------------------------------------------------------ bf16
+def test_bf16_rounding_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32) * 10.0 **
+                        rng.integers(-30, 30, 5000).astype(np.float32),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    for v, r in zip(x, ref):
+        assert orc.f32_to_bf16_rne(float(v)) == int(r)
+
+
+# ------------------------------------------------------------------ Philox
+def test_philox_known_answer_vectors(orc):
+    for r in rows("philox4x32_10_kat.txt"):
+        v = [int(t, 16) for t in r]
+        assert orc.philox4x32_10(v[0:4], v[4:6]) == v[6:10]
+
+
+ATEN_DRIVER = r"""
+#include <ATen/core/PhiloxRNGEngine.h>
+#include <cstdio>
+#include <cstdint>
+int main() {
+  unsigned long long seed, sub, off;
+  while (std::scanf("%llx %llx %llx", &seed, &sub, &off) == 3) {
+    at::philox_engine e(seed, sub, off);
+    unsigned a = e(), b = e(), c = e(), d = e();
+    std::printf("%08x %08x %08x %08x\n", a, b, c, d);
+  }
+}
+"""
+
+
+def test_philox_matches_aten_engine(orc):
+    # ATen's header-only Philox4x32-10: key = seed, counter = (offset lo/hi,
+    # subsequence lo/hi). Compiled here with g++; a library run, not a retype.
+    inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    if not os.path.exists(os.path.join(inc, "ATen", "core", "PhiloxRNGEngine.h")):
+        pytest.skip("ATen headers not installed")
+    rng = np.random.default_rng(11)
+    cases = rng.integers(0, 2 ** 63, size=(4000, 3), dtype=np.uint64) * np.uint64(2) + \
+        rng.integers(0, 2, size=(4000, 3), dtype=np.uint64)
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "drv.cpp")
+        exe = os.path.join(d, "drv")
+        with open(src, "w") as f:
+            f.write(ATEN_DRIVER)
+        subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, src, "-o", exe], check=True)
+        inp = "\n".join(f"{int(s):x} {int(u):x} {int(o):x}" for s, u, o in cases)
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    for (s, u, o), line in zip(cases, out.strip().split("\n")):
+        s, u, o = int(s), int(u), int(o)
+        ctr = [o & 0xFFFFFFFF, o >> 32, u & 0xFFFFFFFF, u >> 32]
+        key = [s & 0xFFFFFFFF, s >> 32]
+        assert orc.philox4x32_10(ctr, key) == [int(t, 16) for t in line.split()]
+
+
+def test_sr_draws_are_uniform_and_distinct_per_seed(orc):
+    n = 1 << 15
+    d0 = np.array([orc.sr_draw16(7, i) for i in range(n)])
+    d1 = np.array([orc.sr_draw16(8, i) for i in range(n)])
+    assert d0.min() >= 0 and d0.max() < 65536
+    counts = np.bincount(d0 >> 12, minlength=16)         # 16 bins, chi-square
+    chi2 = (((counts - n / 16) ** 2) / (n / 16)).sum()
+    assert chi2 < 50.0                                    # 15 dof: p ~ 1e-5
+    assert np.mean(d0 == d1) < 0.001
+    assert abs(np.corrcoef(d0[:-1], d0[1:])[0, 1]) < 0.03
+
+
+# ------------------------------------------------------------------ stochastic rounding
+def test_sr_decision_fixture(orc):
+    for a, h, code in rows("sr_decisions.txt"):
+        assert orc.e2m1_sr_mag(f32(float(a)), int(h)) == int(code), (a, h)
+
+
+def test_sr_support_and_fixed_points(orc):
+    grid = [orc.e2m1_value(c) for c in range(8)]
+    for a in [0.1, 0.3, 0.6, 0.9, 1.2, 1.6, 1.9, 2.2, 2.7, 3.3, 3.9, 4.4, 5.5, 5.99]:
+        a = f32(a)
+        lo = max(g for g in grid if g <= a)
+        hi = min(g for g in grid if g > a)
+        for h in (0, 1, 12345, 32768, 65534, 65535):
+            assert grid[orc.e2m1_sr_mag(a, h)] in (lo, hi)
+    for c, g in enumerate(grid):
+        for h in (0, 32768, 65535):
+            assert orc.e2m1_sr_mag(g, h) == c
+
+
+def test_sr_is_unbiased(orc):
+    # Over N draws of the element stream the mean of the rounded value equals
+    # a within 5 standard errors (plus the 2^-16 resolution of the draw).
+    n = 40000
+    for a in [0.25, 0.1, 0.75, 1.1, 1.75, 2.5, 3.3, 5.0, 5.99, 1e-6]:
+        a = f32(a)
+        vals = np.array([orc.e2m1_value(orc.e2m1_sr_mag(a, orc.sr_draw16(3, i)))
+                         for i in range(n)])
+        sd = max(vals.std(), 1e-12)
+        step = max(vals) - min(vals)
+        assert abs(vals.mean() - a) <= 5 * sd / math.sqrt(n) + step * 2 ** -16 + 1e-12, a
+
+
+# ------------------------------------------------------------------ Hadamard
+def test_rotation_constant():
+    c = np.float32(2.0 ** -2.5)
+    assert f32_bits(float(c)) == 0x3E3504F3
+
+
+def test_fwht_is_sylvester_hadamard(orc):
+    from scipy.linalg import hadamard
+    H = hadamard(32)                               # Sylvester construction
+    assert np.array_equal(H @ H.T, 32 * np.eye(32, dtype=H.dtype))
+    c = np.float32(2.0 ** -2.5)
+    rng = np.random.default_rng(2)
+    for trial in range(200):
+        signs = int(rng.integers(0, 2 ** 32))
+        x = rng.integers(-(2 ** 18), 2 ** 18, 32).astype(np.int64)
+        D = np.array([-1 if (signs >> j) & 1 else 1 for j in range(32)], dtype=np.int64)
+        exact = H @ (D * x)                        # integer, |.| < 2^23: exact in fp32
+        expect = exact.astype(np.float32) * c      # one rounding
+        got = orc.fwht32(x.astype(np.float32), signs)
+        assert np.array_equal(got, expect), trial
+
+
+def test_fwht_orthonormal_and_invertible(orc):
+    from scipy.linalg import hadamard
+    H = hadamard(32).astype(np.float64)
+    rng = np.random.default_rng(3)
+    for _ in range(100):
+        signs = int(rng.integers(0, 2 ** 32))
+        x = rng.standard_normal(32).astype(np.float32)
+        y = orc.fwht32(x, signs).astype(np.float64)
+        D = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(32)])
+        ref = (H @ (D * x.astype(np.float64))) * 2.0 ** -2.5
+        assert np.max(np.abs(y - ref)) <= 6 * 2.0 ** -24 * np.linalg.norm(x)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x)) <= 1e-5 * np.linalg.norm(x)
+        back = D * (H.T @ y) * 2.0 ** -2.5          # inverse: D H^T c
+        assert np.max(np.abs(back - x)) <= 1e-5 * np.linalg.norm(x)
+
+
+def test_hadamard_mask_is_a_separate_philox_counter(orc):
+    # word 0 of counter (0,0,0,1), which the element stream (c2 = c3 = 0) never uses
+    for seed in (0, 1, 3, 2 ** 40 + 5):
+        w = orc.philox4x32_10([0, 0, 0, 1], [seed & 0xFFFFFFFF, seed >> 32])[0]
+        assert orc.hadamard_signs(seed) == w

@@ -1,0 +1,218 @@
+"""Pins of the oracle's tensor quantizer and dequantizer.
+
+Hand-derived worked examples (tests/golden/), invariants that follow from the
+format definitions (Robots Atlas, "FP4", Components and How it works), the
+statistics of stochastic rounding (FP4 All the Way, Key points), and exact
+special cases.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from golden_io import fields
+
+
+def unpack(codes):
+    lo = codes & 0x0F
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def load_worked(name, nblk, B):
+    f = fields(name)
+    x = np.zeros((1, nblk * B), dtype=np.float32)
+    c = np.zeros(nblk * B, dtype=np.uint8)
+    for b in range(nblk):
+        xs = [float(v) for v in f[f"x{b}"]]
+        cs = [int(v, 16) for v in f[f"c{b}"]]
+        x[0, b * B:b * B + len(xs)] = xs
+        c[b * B:b * B + len(cs)] = cs
+    return f, x, c
+
+
+def test_nvfp4_worked_example(orc):
+    f, x, c = load_worked("nvfp4_worked.txt", 7, 16)
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4)
+    assert q["amax"] == float(f["amax"][0]) and q["sg"] == float(f["sg"][0])
+    assert list(q["scales"][0]) == [int(v, 16) for v in f["scales"]]
+    assert list(unpack(q["codes"])[0]) == list(c)
+    assert list(q["codes"][0, 8:16]) == [int(v, 16) for v in f["packed1"]]
+
+
+def test_mxfp4_worked_example(orc):
+    f, x, c = load_worked("mxfp4_worked.txt", 4, 32)
+    q = orc.quantize(x, fmt=orc.FMT_MXFP4)
+    assert list(q["scales"][0]) == [int(v, 16) for v in f["scales"]]
+    assert list(unpack(q["codes"])[0]) == list(c)
+
+
+def test_mxfp4_hadamard_worked_example(orc):
+    f, x, c = load_worked("mxfp4_hadamard_worked.txt", 2, 32)
+    q = orc.quantize(x, fmt=orc.FMT_MXFP4, had_on=True, had_signs=int(f["mask"][0], 16))
+    assert list(q["scales"][0]) == [int(v, 16) for v in f["scales"]]
+    assert list(unpack(q["codes"])[0]) == list(c)
+
+
+def _randn(shape, seed, outliers=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32)
+    if outliers:
+        cols = rng.permutation(shape[1])[: max(1, shape[1] // 100)]
+        x[:, cols] *= 20
+    return x
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_amax_element_lands_on_the_top_of_the_grid(orc, fmt):
+    # NVFP4 with a normal E4M3 scale: the block maximum maps to within 2^-4
+    # (relative) of 6, so it rounds to 6. MXFP4 (round-up power of two): the
+    # maximum maps into (3, 6], so it rounds to 3, 4 or 6.
+    x = _randn((64, 512), 1, outliers=True)
+    q = orc.quantize(x, fmt=fmt)
+    B = 16 if fmt == 0 else 32
+    mags = unpack(q["codes"]) & 7
+    xb = np.abs(x).reshape(64, -1, B)
+    arg = xb.argmax(axis=2)
+    top = np.take_along_axis(mags.reshape(64, -1, B), arg[..., None], axis=2)[..., 0]
+    if fmt == 0:
+        normal = (q["scales"] >> 3) & 15 != 0
+        assert np.all(top[normal] == 7)
+    else:
+        assert np.all(np.isin(top, [5, 6, 7]))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_rtn_error_bound(orc, fmt):
+    # |x - x_hat| <= half the local grid step times the block's scale for
+    # values inside the grid range (plus fp32 rounding of x * r).
+    x = _randn((32, 256), 2, outliers=True)
+    q = orc.quantize(x, fmt=fmt)
+    deq = orc.dequantize_f64(q)
+    B = 16 if fmt == 0 else 32
+    s = np.repeat(q["scales"].astype(np.int64), B, axis=1)
+    if fmt == 0:
+        d = np.array([orc.e4m3_value(int(v)) for v in range(256)])[s] * q["sg"]
+    else:
+        d = 2.0 ** (s - 127)
+    v = np.abs(x / d)
+    step = np.select([v < 2, v < 4], [0.5, 1.0], 2.0)
+    inside = v <= 6.0
+    err = np.abs(x - deq)
+    assert np.all(err[inside] <= 0.5 * step[inside] * d[inside] * (1 + 1e-6) + 1e-30)
+    if fmt == 0:      # clipped values (NVFP4 only, |v| <= 6.4) err by at most 0.4 d
+        assert np.all(err[~inside] <= 0.4 * d[~inside] * (1 + 1e-6))
+    else:
+        assert np.all(inside)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("k", [-7, 3, 11])
+def test_power_of_two_scale_invariance(orc, fmt, k):
+    x = _randn((16, 256), 3)
+    q0 = orc.quantize(x, fmt=fmt)
+    q1 = orc.quantize(x * np.float32(2.0 ** k), fmt=fmt)
+    assert np.array_equal(q0["codes"], q1["codes"])
+    if fmt == 0:
+        assert np.array_equal(q0["scales"], q1["scales"])
+        assert q1["sg"] == q0["sg"] * 2.0 ** k
+    else:
+        assert np.array_equal(q0["scales"].astype(int) + k, q1["scales"].astype(int))
+
+
+@pytest.mark.parametrize("fmt,rnd,had", [(0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 1)])
+def test_rows_axis_equals_cols_axis_of_the_transpose(orc, fmt, rnd, had):
+    x = _randn((96, 64), 4)
+    a = orc.quantize(x, axis=orc.AXIS_ROWS, fmt=fmt, rnd=rnd, seed=9, had_on=had,
+                     had_signs=0x1234567)
+    b = orc.quantize(np.ascontiguousarray(x.T), axis=orc.AXIS_COLS, fmt=fmt, rnd=rnd,
+                     seed=9, had_on=had, had_signs=0x1234567)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
+def test_bf16_input_equals_its_fp32_value(orc):
+    x = _randn((32, 128), 5)
+    bits = orc.f32_to_bf16_bits(x)
+    a = orc.quantize(bits, fmt=0, rnd=1, seed=3)
+    b = orc.quantize(orc.bf16_bits_to_f32(bits), fmt=0, rnd=1, seed=3)
+    assert np.array_equal(a["codes"], b["codes"]) and a["sg"] == b["sg"]
+
+
+def test_given_amax_equals_computed_amax(orc):
+    x = _randn((32, 128), 6)
+    a = orc.quantize(x, fmt=0)
+    b = orc.quantize(x, fmt=0, amax=float(np.abs(x).max()))
+    assert np.array_equal(a["codes"], b["codes"]) and a["sg"] == b["sg"]
+    assert a["amax"] == float(np.abs(x).max())
+    assert a["sg"] == float(np.float32(np.abs(x).max()) / np.float32(2688.0))
+
+
+def test_zero_tensor(orc):
+    x = np.zeros((16, 64), dtype=np.float32)
+    q = orc.quantize(x, fmt=0)
+    assert q["amax"] == 0.0 and q["sg"] == 1.0
+    assert not q["codes"].any() and not q["scales"].any()
+    m = orc.quantize(x, fmt=1)
+    assert not m["codes"].any() and np.all(m["scales"] == 0)
+
+
+def test_non_finite_input_is_rejected(orc):
+    x = np.ones((16, 64), dtype=np.float32)
+    x[3, 5] = np.inf
+    with pytest.raises(ValueError):
+        orc.quantize(x)
+    x[3, 5] = np.nan
+    with pytest.raises(ValueError):
+        orc.quantize(x, fmt=1)
+
+
+def test_mxfp4_requantize_is_idempotent(orc):
+    x = _randn((32, 256), 7, outliers=True)
+    d1 = orc.dequantize_f32(orc.quantize(x, fmt=1))
+    d2 = orc.dequantize_f32(orc.quantize(d1, fmt=1))
+    assert np.array_equal(d1, d2)
+
+
+def test_dequantize_f32_is_one_rounding_of_the_exact_value(orc):
+    x = _randn((32, 256), 8, outliers=True)
+    for fmt in (0, 1):
+        q = orc.quantize(x, fmt=fmt)
+        assert np.array_equal(orc.dequantize_f32(q), orc.dequantize_f64(q).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_sr_tensor_is_unbiased(orc, fmt):
+    # Over independent seeds, each element rounds up (to the upper grid
+    # neighbour of v = x * r) with probability p = (v - lo) / (hi - lo): the
+    # count of ups is Binomial(n, p) up to the 2^-16 resolution of the draw.
+    x = _randn((8, 64), 9)
+    n = 400
+    B = 16 if fmt == 0 else 32
+    q = orc.quantize(x, fmt=fmt)
+    s = np.repeat(q["scales"].astype(np.int64), B, axis=1)
+    if fmt == 0:
+        d = (np.array([orc.e4m3_value(int(v)) for v in range(256)])[s] * q["sg"]).astype(np.float32)
+        r = np.where(d == 0, np.float32(0), np.float32(1) / d)
+    else:
+        r = (2.0 ** (127 - s)).astype(np.float32)
+    v = np.abs(x * r)                                     # fp32, as the quantizer computes it
+    grid = np.array([orc.e2m1_value(c) for c in range(8)])
+    inside = v < 6.0
+    lo_i = np.clip(np.searchsorted(grid, v, side="right") - 1, 0, 6)
+    lo, hi = grid[lo_i], grid[lo_i + 1]
+    p = np.where(inside, (v - lo) / (hi - lo), 0.0)
+    ups = np.zeros(x.shape)
+    for sd in range(n):
+        mags = unpack(orc.quantize(x, fmt=fmt, rnd=orc.SR, seed=1000 + sd)["codes"]) & 7
+        ups += grid[mags] == hi
+    k, mu = ups[inside], n * p[inside]
+    var = n * p[inside] * (1 - p[inside])
+    assert np.all(np.abs(k - mu) <= 5 * np.sqrt(var) + 1.0)
+    assert abs((k - mu).sum()) <= 5 * math.sqrt(var.sum()) + 1.0
+
+
+def test_sr_index_offset_shifts_the_stream(orc):
+    x = _randn((4, 64), 10)
+    full = orc.quantize(np.vstack([x, x]), fmt=1, rnd=orc.SR, seed=4)
+    second = orc.quantize(x, fmt=1, rnd=orc.SR, seed=4, index_offset=4 * 64)
+    assert np.array_equal(full["codes"][4:], second["codes"])
