@@ -1,0 +1,189 @@
+// abi.cpp -- the C ABI of libfp4 (declared in include/fp4.h): argument
+// validation, then kernel launches on the caller's stream. Nothing is
+// launched when validation fails; the library never allocates or synchronizes.
+#include "fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "fp4_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int block_of(int32_t fmt) { return fmt == FP4_NVFP4 ? 16 : 32; }
+bool valid_fmt(int32_t fmt) { return fmt == FP4_NVFP4 || fmt == FP4_MXFP4; }
+bool valid_dtype(int d) { return d == FP4_DTYPE_F32 || d == FP4_DTYPE_BF16; }
+
+fp4_status hip_status() {
+  return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+// Work counts are kept in 32 bits inside the kernels.
+bool fits_tasks(int64_t R, int64_t C) {
+  const int64_t spr = (C + 511) / 512;
+  return R <= (int64_t)0xFFFFFFFF / (spr > 0 ? spr : 1);
+}
+
+fp4_status check_matrix(const void* src, int dt, int64_t R, int64_t C, int64_t ld) {
+  if (!src) return FP4_ERR_NULL;
+  if (!valid_dtype(dt)) return FP4_ERR_ARG;
+  if (R <= 0 || C <= 0 || C % 8 != 0 || ld < C) return FP4_ERR_SHAPE;
+  if (!aligned16(src) || ld % 8 != 0) return FP4_ERR_ALIGN;
+  if (!fits_tasks(R, C)) return FP4_ERR_SHAPE;
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp4_codes_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 2 != 0) return 0;
+  return (size_t)rows * (size_t)(cols / 2);
+}
+
+size_t fp4_scales_bytes(int64_t rows, int64_t cols, int32_t fmt) {
+  if (rows <= 0 || cols <= 0 || !valid_fmt(fmt) || cols % block_of(fmt) != 0) return 0;
+  return (size_t)rows * (size_t)(cols / block_of(fmt));
+}
+
+uint32_t fp4_hadamard_signs(uint64_t seed) {
+  // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) at counter (0, 0, 0, 1), word 0.
+  uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 1;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+const char* fp4_status_str(fp4_status s) {
+  switch (s) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_NULL: return "null pointer";
+    case FP4_ERR_SHAPE: return "bad shape";
+    case FP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP4_ERR_ARG: return "bad enum argument";
+    case FP4_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+fp4_status fp4_tensor_amax(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                           float* amax, fp4_stream_t stream) {
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if (!amax) return FP4_ERR_NULL;
+  fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, amax, reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                        fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                        int amax_ready, fp4_tensor* out, fp4_stream_t stream) {
+  if (!out) return FP4_ERR_NULL;
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
+  if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ARG;
+  if (!valid_fmt(out->fmt)) return FP4_ERR_ARG;
+  if (!out->codes || !out->scales) return FP4_ERR_NULL;
+  if (!aligned16(out->codes) || !aligned16(out->scales)) return FP4_ERR_ALIGN;
+  const bool nv = out->fmt == FP4_NVFP4;
+  if (nv && (!out->amax || !out->tscale)) return FP4_ERR_NULL;
+  if (out->had_on && nv) return FP4_ERR_UNSUPPORTED;
+  const int B = block_of(out->fmt);
+  const int64_t blocked = axis == FP4_AXIS_ROWS ? R : C;
+  if (blocked % B != 0) return FP4_ERR_SHAPE;
+  if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
+  if (axis == FP4_AXIS_ROWS && (R + 4 * B - 1) / (4 * B) * ((C + 63) / 64) > 0x7FFFFFFF)
+    return FP4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nv && !amax_ready) {
+    fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
+    st = hip_status();
+    if (st != FP4_OK) return st;
+  }
+  QuantArgs a;
+  a.src = src;
+  a.bf16 = src_t == FP4_DTYPE_BF16;
+  a.R = R;
+  a.C = C;
+  a.ld = ld;
+  a.rows_axis = axis == FP4_AXIS_ROWS;
+  a.fmt = out->fmt;
+  a.sr = rnd == FP4_SR;
+  a.seed = seed;
+  a.offset = index_offset;
+  a.had_on = out->had_on != 0;
+  a.signs = out->had_signs;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.amax = out->amax;
+  a.tscale = out->tscale;
+  fp4i_launch_quant(a, s);
+  out->rows = a.rows_axis ? C : R;
+  out->cols = a.rows_axis ? R : C;
+  return hip_status();
+}
+
+fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
+                          fp4_stream_t stream) {
+  if (!q || !dst) return FP4_ERR_NULL;
+  if (!valid_dtype(dst_t) || !valid_fmt(q->fmt)) return FP4_ERR_ARG;
+  if (!q->codes || !q->scales) return FP4_ERR_NULL;
+  if (q->fmt == FP4_NVFP4 && !q->tscale) return FP4_ERR_NULL;
+  if (q->rows <= 0 || q->cols <= 0 || q->cols % block_of(q->fmt) != 0 || ld < q->cols)
+    return FP4_ERR_SHAPE;
+  if (!fits_tasks(q->rows, q->cols)) return FP4_ERR_SHAPE;
+  if (!aligned16(dst) || ld % 8 != 0 || !aligned16(q->codes)) return FP4_ERR_ALIGN;
+  fp4i_launch_dequant(q->codes, q->scales, q->tscale, q->fmt, q->rows, q->cols,
+                      dst_t == FP4_DTYPE_BF16, dst, ld, reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C,
+                    int64_t ldc, fp4_stream_t stream) {
+  if (!A || !B || !C) return FP4_ERR_NULL;
+  if (!valid_dtype(out_t) || !valid_fmt(A->fmt) || !valid_fmt(B->fmt)) return FP4_ERR_ARG;
+  if (!A->codes || !A->scales || !B->codes || !B->scales) return FP4_ERR_NULL;
+  if (A->fmt != B->fmt) return FP4_ERR_UNSUPPORTED;
+  if ((A->had_on != 0) != (B->had_on != 0)) return FP4_ERR_UNSUPPORTED;
+  if (A->had_on && A->had_signs != B->had_signs) return FP4_ERR_UNSUPPORTED;
+  if (A->fmt == FP4_NVFP4 && (!A->tscale || !B->tscale)) return FP4_ERR_NULL;
+  if (A->rows <= 0 || B->rows <= 0 || A->cols <= 0 || A->cols != B->cols || A->cols % 128 != 0)
+    return FP4_ERR_SHAPE;
+  if ((A->rows + 127) / 128 * ((B->rows + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
+  if (ldc < B->rows) return FP4_ERR_SHAPE;
+  if (!aligned16(A->codes) || !aligned16(B->codes) || !aligned16(A->scales) || !aligned16(B->scales))
+    return FP4_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(C) & (out_t == FP4_DTYPE_F32 ? 3u : 1u)) != 0) return FP4_ERR_ALIGN;
+  GemmArgs g;
+  g.a_codes = A->codes;
+  g.a_scales = A->scales;
+  g.b_codes = B->codes;
+  g.b_scales = B->scales;
+  g.a_tscale = A->tscale;
+  g.b_tscale = B->tscale;
+  g.M = A->rows;
+  g.N = B->rows;
+  g.K = A->cols;
+  g.fmt = A->fmt;
+  g.bf16out = out_t == FP4_DTYPE_BF16;
+  g.c = C;
+  g.ldc = ldc;
+  fp4i_launch_gemm(g, reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+}  // extern "C"

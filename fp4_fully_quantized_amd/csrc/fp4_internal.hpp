@@ -1,0 +1,43 @@
+// fp4_internal.hpp -- launchers shared between the C-ABI layer and the kernel
+// translation units of libfp4 (not part of the public interface).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct QuantArgs {
+  const void* src;
+  bool bf16;
+  int64_t R, C, ld;      // source matrix, row-major
+  bool rows_axis;        // blocks along R (output is the transpose)
+  int fmt;               // 0 NVFP4, 1 MXFP4
+  bool sr;
+  uint64_t seed, offset;
+  bool had_on;
+  uint32_t signs;
+  uint8_t* codes;
+  uint8_t* scales;
+  const float* amax;     // NVFP4: device tensor amax (already computed)
+  float* tscale;         // NVFP4: receives s_g
+};
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* a_tscale;  // NVFP4 only
+  const float* b_tscale;
+  int64_t M, N, K;
+  int fmt;
+  bool bf16out;
+  void* c;
+  int64_t ldc;
+};
+
+void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
+                      hipStream_t s);
+void fp4i_launch_quant(const QuantArgs& a, hipStream_t s);
+void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
+                         int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
+                         hipStream_t s);
+void fp4i_launch_gemm(const GemmArgs& g, hipStream_t s);

@@ -1,0 +1,402 @@
+// quant.hip -- tensor amax, block-scaled FP4 quantize (both axes) and dequantize
+// for gfx950.
+//
+// What is computed (Robots Atlas, "FP4", How it works and Components; FP4 All
+// the Way, Key points; Quartet, Approach):
+//   NVFP4  s_g = amax/2688; per 16-block byte = E4M3_rne((amax_b/6)/s_g),
+//          r = 1/(sdec*s_g); codes = E2M1(x*r)
+//   MXFP4  optional 32-wide random-sign Hadamard; per 32-block e = the
+//          smallest e with 6*2^e >= amax_b; codes = E2M1(x*2^-e)
+//   RTN or SR (16-bit Philox4x32-10 draws keyed by seed and element index).
+//
+// Memory-bound passes: every element is read once from HBM with 16-byte loads
+// and written once as a nibble; block scales are one byte per block.
+//  * k_amax        wave-strided 16-byte loads, per-lane max, wave and workgroup
+//                  reduction, one atomicMax per workgroup on the float bits.
+//  * k_quant_cols  blocks along the contiguous axis: each lane owns 8
+//                  consecutive elements (one 16-byte bf16 load), a block spans
+//                  2 (NVFP4) or 4 (MXFP4) lanes; the block amax and the
+//                  Hadamard's cross-lane stages use DPP quad permutes; each
+//                  lane stores one dword of 8 codes (256 contiguous bytes per
+//                  wave).
+//  * k_quant_rows  blocks along rows (the transposed orientation used by dgrad
+//                  and wgrad operands): a 64(or 128) x 64 tile is loaded with
+//                  coalesced 16-byte row loads, staged through LDS as FP32,
+//                  and each thread quantizes one block down a column.
+//  * k_dequant     8 elements per lane.
+#include "fp4_device.hpp"
+#include "fp4_internal.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int NV = 0;
+constexpr int MX = 1;
+
+__global__ void k_zero1(float* p) { *p = 0.0f; }
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_amax(const void* __restrict__ src, int64_t C, int64_t ld,
+                                               uint32_t spr, uint32_t ntasks, float* amax) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t nwaves = gridDim.x * 4u;
+  float m = 0.0f;
+  for (uint32_t t = wave; t < ntasks; t += nwaves) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t r = tu / spr;
+    const uint32_t seg = tu - r * spr;
+    const int64_t col = (int64_t)seg * 512 + lane * 8;
+    if (col < C) {
+      float x[8];
+      load8<BF16>(static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float part[4];
+  if (lane == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(b));
+  }
+}
+
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+
+// Block scale of one block with amax m. Returns the scale byte, sets the
+// element multiplier r.
+template <int FMT>
+__device__ __forceinline__ uint32_t block_scale(float m, float sg, float& r) {
+  if constexpr (FMT == NV) {
+    float q = m / 6.0f;
+    q = q / sg;
+    uint32_t byte = e4m3_encode(q);
+    float d = e4m3_decode(byte) * sg;
+    r = (d == 0.0f) ? 0.0f : 1.0f / d;
+    return byte;
+  } else {
+    int e = e8m0_exponent(m);
+    r = pow2_neg(e);
+    return (uint32_t)(e + 127);
+  }
+}
+
+template <int FMT, int RND, bool BF16, bool HAD>
+__global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t C, int64_t ld,
+                                                     uint32_t spr, uint32_t ntasks,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ amax, float* tscale,
+                                                     uint64_t seed, uint64_t offset, uint32_t signs) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int B = FMT == NV ? 16 : 32;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t nwaves = gridDim.x * 4u;
+  float sg = 1.0f;
+  if constexpr (FMT == NV) {
+    sg = nv_tensor_scale(*amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
+  }
+  const int sub = lane & 3;  // position of this lane's 8 elements inside a 32-block
+  for (uint32_t t = wave; t < ntasks; t += nwaves) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t r = tu / spr;
+    const uint32_t seg = tu - r * spr;
+    const int64_t col = (int64_t)seg * 512 + lane * 8;
+    const bool active = col < C;
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active) load8<BF16>(static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES, x);
+    if constexpr (HAD) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((signs >> (8 * sub + i)) & 1u) x[i] = -x[i];
+      fwht8_local(x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float p = dpp_xor1(x[i]);
+        x[i] = (sub & 1) ? p - x[i] : x[i] + p;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float p = dpp_xor2(x[i]);
+        x[i] = (sub & 2) ? p - x[i] : x[i] + p;
+      }
+      const float c = hadamard_norm();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = x[i] * c;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+    m = fmaxf(m, dpp_xor1(m));
+    if constexpr (FMT == MX) m = fmaxf(m, dpp_xor2(m));
+    float rcp;
+    const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = x[i] * rcp;
+    uint32_t w;
+    if constexpr (RND == 0) {
+      w = e2m1_rtn_pack8(v);
+    } else {
+      uint32_t h[8];
+      sr_draws8(seed, (offset + (uint64_t)r * (uint64_t)C + (uint64_t)col) >> 3, h);
+      w = e2m1_sr_pack8(v, h);
+    }
+    if (active) {
+      *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (C / 2) + col / 2) = w;
+      if ((lane & (B / 8 - 1)) == 0) scales[(int64_t)r * (C / B) + col / B] = (uint8_t)sbyte;
+    }
+  }
+}
+
+// Full 32-point butterfly (stages 1, 2, 4, 8, 16) on a 32-block held by one thread.
+__device__ __forceinline__ void fwht32_local(float x[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Transposed quantize: blocks along rows. Tile = TR rows x 64 columns of the
+// input; thread (c = tid % 64, p = tid / 64) quantizes the block of B rows
+// p*B .. p*B+B-1 of column c. Output row c_glob (of R elements) receives it.
+template <int FMT, int RND, bool BF16, bool HAD>
+__global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src, int64_t R, int64_t C,
+                                                     int64_t ld, uint32_t tiles_c,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ amax, float* tscale,
+                                                     uint64_t seed, uint64_t offset, uint32_t signs) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int B = FMT == NV ? 16 : 32;
+  constexpr int TR = 4 * B;
+  constexpr int TC = 64;
+  constexpr int PITCH = TC + 1;
+  __shared__ float tile[TR * PITCH];
+
+  float sg = 1.0f;
+  if constexpr (FMT == NV) {
+    sg = nv_tensor_scale(*amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
+  }
+  const uint32_t tr = blockIdx.x / tiles_c;
+  const uint32_t tc = blockIdx.x - tr * tiles_c;
+  const int64_t r0 = (int64_t)tr * TR;
+  const int64_t c0 = (int64_t)tc * TC;
+
+  // Coalesced load: each row of the tile is TC elements = 8 (bf16) or 16 (fp32) 16-byte chunks.
+  constexpr int CPR = TC / 8;  // 8-element chunks per tile row
+  for (int idx = threadIdx.x; idx < TR * CPR; idx += 256) {
+    const int rr = idx / CPR;
+    const int cc = (idx - rr * CPR) * 8;
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (r0 + rr < R && c0 + cc < C)
+      load8<BF16>(static_cast<const char*>(src) + ((r0 + rr) * ld + c0 + cc) * ES, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[rr * PITCH + cc + i] = x[i];
+  }
+  __syncthreads();
+
+  const int c = threadIdx.x & 63;
+  const int p = threadIdx.x >> 6;
+  const int64_t cg = c0 + c;
+  const int64_t rg = r0 + (int64_t)p * B;
+  if (cg >= C || rg >= R) return;
+
+  float x[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) x[i] = tile[(p * B + i) * PITCH + c];
+  if constexpr (HAD) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if ((signs >> i) & 1u) x[i] = -x[i];
+    fwht32_local(x);
+    const float hc = hadamard_norm();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = x[i] * hc;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
+  float rcp;
+  const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+  uint32_t w[B / 8];
+#pragma unroll
+  for (int g = 0; g < B / 8; ++g) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
+    if constexpr (RND == 0) {
+      w[g] = e2m1_rtn_pack8(v);
+    } else {
+      uint32_t h[8];
+      sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+      w[g] = e2m1_sr_pack8(v, h);
+    }
+  }
+  uint8_t* dst = codes + cg * (R / 2) + rg / 2;
+  if constexpr (B == 16) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  scales[cg * (R / B) + rg / B] = (uint8_t)sbyte;
+}
+
+template <int FMT, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
+                                                  const uint8_t* __restrict__ scales,
+                                                  const float* __restrict__ tscale, int64_t cols,
+                                                  uint32_t spr, uint32_t ntasks, void* dst, int64_t ld) {
+  constexpr int B = FMT == NV ? 16 : 32;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t nwaves = gridDim.x * 4u;
+  const float sg = (FMT == NV) ? *tscale : 1.0f;
+  for (uint32_t t = wave; t < ntasks; t += nwaves) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t r = tu / spr;
+    const uint32_t seg = tu - r * spr;
+    const int64_t col = (int64_t)seg * 512 + lane * 8;
+    if (col >= cols) continue;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (int64_t)r * (cols / 2) + col / 2);
+    const uint32_t sb = scales[(int64_t)r * (cols / B) + col / B];
+    float y[8];
+    {
+      auto q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+      auto q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+      auto q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+      auto q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+      y[0] = q0[0]; y[1] = q0[1]; y[2] = q1[0]; y[3] = q1[1];
+      y[4] = q2[0]; y[5] = q2[1]; y[6] = q3[0]; y[7] = q3[1];
+    }
+    if constexpr (FMT == NV) {
+      const float sdec = e4m3_decode(sb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = (y[i] * sdec) * sg;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = __builtin_ldexpf(y[i], (int)sb - 127);
+    }
+    if constexpr (BF16OUT) {
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t a = __float_as_uint(y[2 * i]), b = __float_as_uint(y[2 * i + 1]);
+        a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+        b = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+        o[i] = a | (b << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + (int64_t)r * ld + col) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      float* d = static_cast<float*>(dst) + (int64_t)r * ld + col;
+      reinterpret_cast<float4*>(d)[0] = make_float4(y[0], y[1], y[2], y[3]);
+      reinterpret_cast<float4*>(d)[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+}
+
+constexpr uint32_t kMaxGrid = 256 * 16;
+
+uint32_t strided_grid(uint64_t ntasks) {
+  uint64_t wgs = (ntasks + 3) / 4;
+  return (uint32_t)(wgs < kMaxGrid ? (wgs ? wgs : 1) : kMaxGrid);
+}
+
+template <int FMT, int RND, bool BF16, bool HAD>
+void launch_cols(const QuantArgs& a, hipStream_t s) {
+  const uint32_t spr = (uint32_t)((a.C + 511) / 512);
+  const uint32_t ntasks = (uint32_t)(a.R * spr);
+  hipLaunchKernelGGL((k_quant_cols<FMT, RND, BF16, HAD>), dim3(strided_grid(ntasks)), dim3(256), 0, s,
+                     a.src, a.C, a.ld, spr, ntasks, a.codes, a.scales, a.amax, a.tscale, a.seed,
+                     a.offset, a.signs);
+}
+
+template <int FMT, int RND, bool BF16, bool HAD>
+void launch_rows(const QuantArgs& a, hipStream_t s) {
+  constexpr int B = FMT == NV ? 16 : 32;
+  const uint32_t tiles_c = (uint32_t)((a.C + 63) / 64);
+  const uint32_t tiles_r = (uint32_t)((a.R + 4 * B - 1) / (4 * B));
+  hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD>), dim3(tiles_c * tiles_r), dim3(256), 0, s,
+                     a.src, a.R, a.C, a.ld, tiles_c, a.codes, a.scales, a.amax, a.tscale, a.seed,
+                     a.offset, a.signs);
+}
+
+template <int FMT, int RND, bool BF16, bool HAD>
+void launch_axis(const QuantArgs& a, hipStream_t s) {
+  if (a.rows_axis)
+    launch_rows<FMT, RND, BF16, HAD>(a, s);
+  else
+    launch_cols<FMT, RND, BF16, HAD>(a, s);
+}
+
+template <int FMT, int RND>
+void launch_src(const QuantArgs& a, hipStream_t s) {
+  if constexpr (FMT == MX) {
+    if (a.had_on) {
+      if (a.bf16) launch_axis<FMT, RND, true, true>(a, s);
+      else launch_axis<FMT, RND, false, true>(a, s);
+      return;
+    }
+  }
+  if (a.bf16) launch_axis<FMT, RND, true, false>(a, s);
+  else launch_axis<FMT, RND, false, false>(a, s);
+}
+
+}  // namespace
+
+void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax);
+  const uint32_t spr = (uint32_t)((C + 511) / 512);
+  const uint32_t ntasks = (uint32_t)(R * spr);
+  if (bf16)
+    hipLaunchKernelGGL(k_amax<true>, dim3(strided_grid(ntasks)), dim3(256), 0, s, src, C, ld, spr,
+                       ntasks, amax);
+  else
+    hipLaunchKernelGGL(k_amax<false>, dim3(strided_grid(ntasks)), dim3(256), 0, s, src, C, ld, spr,
+                       ntasks, amax);
+}
+
+void fp4i_launch_quant(const QuantArgs& a, hipStream_t s) {
+  if (a.fmt == NV) {
+    if (a.sr) launch_src<NV, 1>(a, s);
+    else launch_src<NV, 0>(a, s);
+  } else {
+    if (a.sr) launch_src<MX, 1>(a, s);
+    else launch_src<MX, 0>(a, s);
+  }
+}
+
+void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
+                         int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
+                         hipStream_t s) {
+  const uint32_t spr = (uint32_t)((cols + 511) / 512);
+  const uint32_t ntasks = (uint32_t)(rows * spr);
+  const dim3 g(strided_grid(ntasks)), b(256);
+  if (fmt == NV) {
+    if (bf16out) hipLaunchKernelGGL((k_dequant<NV, true>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
+    else hipLaunchKernelGGL((k_dequant<NV, false>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
+  } else {
+    if (bf16out) hipLaunchKernelGGL((k_dequant<MX, true>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
+    else hipLaunchKernelGGL((k_dequant<MX, false>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
+  }
+}

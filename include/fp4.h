@@ -1,0 +1,170 @@
+/*
+ * fp4.h -- C ABI of the MI355X (gfx950) FP4 quantize + FP4 GEMM library (libfp4.so).
+ *
+ * The library implements the data-parallel hot path of fully quantized FP4
+ * training of linear layers:
+ *   - block-scaled FP4 quantization of training tensors, in the two formats of
+ *     Robots Atlas, "FP4", section Components:
+ *       NVFP4: 16-element blocks of E2M1 values, an E4M3 scale per block and an
+ *              FP32 scale per tensor (two-level scaling, section How it works);
+ *       MXFP4: 32-element blocks of E2M1 values, an E8M0 (power-of-two) scale;
+ *   - round-to-nearest for the forward pass and stochastic rounding for the
+ *     backward and update passes ("FP4 All the Way: Fully Quantized Training of
+ *     LLMs", Key points), the random stream being Philox4x32-10 keyed by
+ *     (seed, element index);
+ *   - the block-wise random-sign Hadamard rotation of MXFP4 operands
+ *     ("Quartet: Native FP4 Training Can Be Optimal for Large Language Models",
+ *     Approach);
+ *   - the three linear-layer GEMMs in FP4 with FP32 accumulation (Quartet,
+ *     summary; Robots Atlas "FP4", How it works / Execution paradigm):
+ *       forward  Y  = X  W^T : A = X  (blocks along K = in-features),
+ *                              B = W  (blocks along K)
+ *       dgrad    dX = dY W   : A = dY (blocks along out-features),
+ *                              B = W quantized along axis ROWS, i.e. W^T
+ *       wgrad    dW = dY^T X : A = dY quantized along axis ROWS, i.e. dY^T,
+ *                              B = X quantized along axis ROWS, i.e. X^T
+ *
+ * Conventions (fixed where the pages are silent):
+ *   E2M1 code  S|E1E0|M, bias 1; element 2t of a row in the low nibble of byte t.
+ *   NVFP4      s_g = amax / 2688 (6 * 448; 1 when amax = 0); block byte = E4M3
+ *              round-to-nearest-even, saturating at 448, of (amax_b / 6) / s_g;
+ *              element v = x * (1 / (sdec * s_g)), the reciprocal rounded once.
+ *   MXFP4      block exponent e = the smallest e with 6 * 2^e >= amax_b
+ *              (>= -127); byte = e + 127; v = x * 2^-e.
+ *   RTN        nearest E2M1 magnitude, ties to even, saturating at 6.
+ *   SR         a grid value is kept; else lo < |v| < hi rounds up iff
+ *              h / 65536 < (|v| - lo) / (hi - lo), with h the 16-bit draw of
+ *              the element: Philox4x32-10, key = seed, counter = (i / 8, 0, 0)
+ *              as (lo32, hi32, 0, 0), word (i / 2) % 4, low half for even i;
+ *              i = row-major index in the quantized orientation + index_offset.
+ *   Hadamard   per 32-block along the blocked axis: negate x_j where bit j of
+ *              had_signs is set, Sylvester FWHT (stages 1, 2, 4, 8, 16, FP32),
+ *              multiply by fp32(2^-2.5). The same mask must be used for both
+ *              GEMM operands so the rotation cancels.
+ *
+ * Memory and ownership: every pointer argument named "device" is a device
+ * pointer the caller allocated (and keeps ownership of); the library never
+ * allocates, frees or synchronizes. All work is enqueued in order on the
+ * given HIP stream (0 = the null stream). Calls are reentrant.
+ *
+ * Errors: every call validates its arguments first; on a non-OK status
+ * nothing has been enqueued and no output has been touched, except
+ * FP4_ERR_HIP, which reports a failed launch (outputs then undefined).
+ * Non-finite inputs are outside the contract: their outputs are unspecified.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fp4_stream_t; /* the same type as hipStream_t */
+
+typedef enum fp4_status {
+    FP4_OK = 0,
+    FP4_ERR_NULL = 1,        /* a required pointer is NULL */
+    FP4_ERR_SHAPE = 2,       /* a dimension <= 0, or not a multiple the call requires */
+    FP4_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks 16-byte alignment */
+    FP4_ERR_UNSUPPORTED = 4, /* a combination the library does not implement */
+    FP4_ERR_ARG = 5,         /* an enum value out of range */
+    FP4_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+} fp4_status;
+
+typedef enum fp4_dtype { FP4_DTYPE_F32 = 0, FP4_DTYPE_BF16 = 1 } fp4_dtype;
+typedef enum fp4_format { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
+typedef enum fp4_rounding { FP4_RTN = 0, FP4_SR = 1 } fp4_rounding;
+/* FP4_AXIS_COLS: blocks run along the contiguous axis C; quantized orientation [R][C].
+ * FP4_AXIS_ROWS: blocks run along R; quantized orientation is the transpose [C][R]. */
+typedef enum fp4_axis { FP4_AXIS_COLS = 0, FP4_AXIS_ROWS = 1 } fp4_axis;
+
+/* A quantized matrix in its quantized orientation: rows x cols, blocks of B
+ * (16 NVFP4, 32 MXFP4) consecutive elements along cols.
+ *   codes  device, rows * cols / 2 bytes, row-major [rows][cols/2]
+ *   scales device, rows * cols / B bytes, row-major [rows][cols/B]
+ *          (E4M3 bytes for NVFP4, E8M0 bytes for MXFP4)
+ *   amax   device FP32 scalar: the tensor amax (NVFP4; NULL for MXFP4)
+ *   tscale device FP32 scalar: the tensor scale s_g (NVFP4; NULL for MXFP4)
+ * codes and scales must be 16-byte aligned. */
+typedef struct fp4_tensor {
+    uint8_t* codes;
+    uint8_t* scales;
+    float* amax;
+    float* tscale;
+    int64_t rows;
+    int64_t cols;
+    int32_t fmt;        /* fp4_format */
+    int32_t had_on;     /* 1: values are in the Hadamard-rotated domain (MXFP4 only) */
+    uint32_t had_signs; /* the rotation's sign mask when had_on */
+    uint32_t reserved;
+} fp4_tensor;
+
+/* Bytes of codes / scales for a quantized rows x cols matrix (0 on bad input). */
+size_t fp4_codes_bytes(int64_t rows, int64_t cols);
+size_t fp4_scales_bytes(int64_t rows, int64_t cols, int32_t fmt);
+
+/* The Hadamard sign mask of a seed: word 0 of Philox4x32-10 at counter
+ * (0, 0, 0, 1) under key = seed (a counter the element stream never uses).
+ * Host-only, no device work. */
+uint32_t fp4_hadamard_signs(uint64_t seed);
+
+/* Human-readable name of a status. */
+const char* fp4_status_str(fp4_status s);
+
+/* Tensor amax: *amax = max |x| over the R x C matrix src (row-major, leading
+ * dimension ld elements, FP32 or bf16; device). amax is a device FP32 scalar.
+ * The NVFP4 tensor scale depends on it (Robots Atlas "FP4", How it works:
+ * the per-tensor FP32 scale). Requires R, C >= 1, C % 8 == 0, ld >= C,
+ * ld % 8 == 0, src 16-byte aligned. */
+fp4_status fp4_tensor_amax(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                           float* amax, fp4_stream_t stream);
+
+/* Quantize the R x C matrix src (row-major, leading dimension ld, FP32 or bf16;
+ * device) into *out.
+ *   axis         FP4_AXIS_COLS: blocks along C, out is R x C;
+ *                FP4_AXIS_ROWS: blocks along R, out is C x R (the transpose).
+ *   rnd          FP4_RTN or FP4_SR.
+ *   seed, index_offset  the SR stream (ignored for RTN).
+ *   amax_ready   NVFP4: 1 if *out->amax already holds this tensor's amax (from
+ *                fp4_tensor_amax or an earlier quantize of the same tensor in
+ *                the other orientation); 0 to compute it first. Ignored for MXFP4.
+ *   out          caller-filled descriptor: codes, scales, fmt, had_on,
+ *                had_signs and, for NVFP4, amax and tscale. The call writes
+ *                out->rows and out->cols; *out->tscale receives s_g.
+ * Requires: R, C >= 1; the blocked dimension a multiple of B (C for COLS, R
+ * for ROWS); C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned;
+ * had_on only with MXFP4. */
+fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                        fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                        int amax_ready, fp4_tensor* out, fp4_stream_t stream);
+
+/* Dequantize q to dst (device, q->rows x q->cols row-major, leading dimension
+ * ld >= cols, FP32 or bf16):
+ *   NVFP4: (e2m1 * sdec) * s_g, the last product rounded once to FP32;
+ *   MXFP4: e2m1 * 2^e (exact); values stay in the rotated domain when had_on.
+ * A bf16 output is the FP32 value rounded to nearest even.
+ * Requires ld % 8 == 0 and dst 16-byte aligned. */
+fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
+                          fp4_stream_t stream);
+
+/* C[i][j] = alpha * sum_k A_hat[i][k] * B_hat[j][k] with FP32 accumulation,
+ * where A_hat, B_hat are the dequantized operands (both blocked along the
+ * shared contraction axis K), M = A->rows, N = B->rows, K = A->cols = B->cols,
+ * alpha = (*A->tscale) * (*B->tscale) for NVFP4 and 1 for MXFP4.
+ *   MXFP4 runs on the gfx950 block-scaled FP4 MFMA with the E8M0 bytes as its
+ *   scale operands. NVFP4 decodes e2m1 * E4M3 exactly into bf16 in registers
+ *   (at most 6 significant bits) and runs the bf16 MFMA.
+ * C: device, M x N row-major, leading dimension ldc >= N, FP32 or bf16
+ * (rounded to nearest even once, after alpha).
+ * Requires: same fmt, had_on and had_signs on both operands; K % 128 == 0;
+ * M, N >= 1 (any value); ldc >= N (any value); C aligned to its element size. */
+fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C,
+                    int64_t ldc, fp4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_H */

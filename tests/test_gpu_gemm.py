@@ -1,0 +1,136 @@
+"""GPU parity of the FP4 GEMMs against the oracle's FP64 product of the
+dequantized operands: |y - ref| <= 1e-5 * sum_k |a_k b_k| per element (FP32
+output; a bf16 output adds its own rounding 2^-8 |ref|). Operands are quantized
+by the oracle and uploaded, so the GEMM is tested on its own; one case runs
+the GPU quantizer end to end."""
+import numpy as np
+import pytest
+
+from gpu_util import q_from_oracle, say, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import fp4_fully_quantized_amd as m
+    m.lib()
+    return m
+
+
+def _data(shape, seed, std=1.0, outliers=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(std)
+    if outliers:
+        x[:, rng.permutation(shape[1])[: max(1, shape[1] // 100)]] *= 20
+    from oracle.oracle import f32_to_bf16_bits
+    return f32_to_bf16_bits(x)
+
+
+def _run(fp4, orc, qa, qb, out, signs=None):
+    import torch
+    A = q_from_oracle(qa, had_signs=signs)
+    B = q_from_oracle(qb, had_signs=signs)
+    y = fp4.gemm(A, B, dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    yh = to_host(y)
+    if out == "bf16":
+        yh = orc.bf16_bits_to_f32(yh)
+    return yh
+
+
+SHAPES = [(200, 136, 256), (77, 300, 384), (256, 256, 128), (1, 1, 128), (513, 129, 1024)]
+
+
+@pytest.mark.parametrize("fmt,had", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_matches_oracle(fp4, orc, fmt, had, out, M, N, K):
+    say("gemm", M, N, K, "fmt", fmt, "had", had, "out", out)
+    signs = orc.hadamard_signs(9) if had else 0
+    qa = orc.quantize(_data((M, K), 1, outliers=True), fmt=fmt, had_on=had, had_signs=signs)
+    qb = orc.quantize(_data((N, K), 2, std=0.02), fmt=fmt, had_on=had, had_signs=signs)
+    y = _run(fp4, orc, qa, qb, out, signs if had else None)
+    ref, S = orc.gemm_ref(qa, qb)
+    ok, worst = orc.gemm_check(y, ref, S, out)
+    assert ok, f"worst error {worst:.3g} of the bound"
+
+
+def test_gemm_zero_operand_gives_exact_zero(fp4, orc):
+    qa = orc.quantize(np.zeros((64, 256), dtype=np.float32))
+    qb = orc.quantize(_data((64, 256), 3))
+    y = _run(fp4, orc, qa, qb, "fp32")
+    assert np.all(y == 0.0)
+
+
+def test_gpu_quantizer_into_gemm_end_to_end(fp4, orc):
+    import torch
+    xh, wh = _data((320, 512), 4, outliers=True), _data((192, 512), 5, std=0.02)
+    X, W = to_device(xh), to_device(wh)
+    y = fp4.gemm(fp4.quantize(X), fp4.quantize(W), dtype=torch.float32)
+    ref, S = orc.gemm_ref(orc.quantize(xh), orc.quantize(wh))
+    ok, worst = orc.gemm_check(to_host(y), ref, S, "fp32")
+    assert ok, worst
+
+
+def _rows_of(q, rows):
+    d = dict(q)
+    d["codes"], d["scales"], d["rows"] = q["codes"][rows], q["scales"][rows], len(rows)
+    return d
+
+
+def _sample_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
+                                     rng.integers(0, M, 64)]))
+
+
+# Full Llama-7B-shaped GEMMs (32768 tokens, 4096 in, 11008 out): the forward
+# on NVFP4 and MXFP4+Hadamard operands, dgrad and wgrad on SR operands.
+FULL = [
+    ("fwd-nvfp4", "bf16"),
+    ("fwd-mxfp4", "bf16"),
+    ("dgrad", "fp32"),
+    ("wgrad", "fp32"),
+]
+
+
+@pytest.mark.parametrize("which,out", FULL)
+def test_full_size_gemm_sampled_rows(fp4, orc, which, out):
+    from fp4_fully_quantized_amd import workloads
+    import torch
+    say("full-size gemm", which, out)
+    dev = lambda role: to_host(workloads.device_tensor("llama7b", role))
+    signs = 0
+    if which.startswith("fwd"):
+        fmt = 0 if which == "fwd-nvfp4" else 1
+        had = fmt == 1
+        signs = orc.hadamard_signs(3) if had else 0
+        xh, wh = dev("X"), dev("W")
+        qa = orc.quantize(xh, fmt=fmt, had_on=had, had_signs=signs)
+        qb = orc.quantize(wh, fmt=fmt, had_on=had, had_signs=signs)
+        del xh, wh
+    elif which == "dgrad":
+        had = False
+        dyh, wh = dev("dY"), dev("W")
+        qa = orc.quantize(dyh, axis=0, rnd=1, seed=(2 << 8) | 1)
+        qb = orc.quantize(wh, axis=1, rnd=1, seed=(2 << 8) | 4)
+        del dyh, wh
+    else:
+        had = False
+        dyh, xh = dev("dY"), dev("X")
+        qa = orc.quantize(dyh, axis=1, rnd=1, seed=(2 << 8) | 2)
+        qb = orc.quantize(xh, axis=1, rnd=1, seed=(2 << 8) | 3)
+        del dyh, xh
+    A = q_from_oracle(qa, had_signs=signs if had else None)
+    B = q_from_oracle(qb, had_signs=signs if had else None)
+    y = fp4.gemm(A, B, dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    rows = _sample_rows(qa["rows"], 17)
+    yh = to_host(y[torch.from_numpy(rows).cuda()])
+    if out == "bf16":
+        yh = orc.bf16_bits_to_f32(yh)
+    ref, S = orc.gemm_ref(_rows_of(qa, rows), qb)
+    ok, worst = orc.gemm_check(yh, ref, S, out)
+    say("worst error / bound", worst)
+    assert ok, worst

@@ -1,0 +1,131 @@
+"""GPU parity of amax, quantize (both axes, both formats, RTN/SR, Hadamard)
+and dequantize against the CPU oracle: bit-exact codes, scale bytes, tensor
+amax and tensor scale."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_same_quant, q_from_oracle, q_to_host, say, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import fp4_fully_quantized_amd as m
+    m.lib()          # raises if the HIP library is not built
+    return m
+
+
+def _mixed(shape, seed, bf16=True):
+    """Heavy-tailed data with outlier columns and the degenerate cases of the
+    block-scale rules: an all-zero block and row, signed zeros, values tiny
+    enough to underflow the E4M3 scale, and a huge block."""
+    rng = np.random.default_rng(seed)
+    R, C = shape
+    x = rng.standard_t(3, size=shape).astype(np.float32)
+    x[:, rng.permutation(C)[: max(1, C // 100)]] *= 20
+    x[0, :32] = 0.0
+    x[1, :] = 0.0
+    x[2, 0:32:2] = -0.0
+    x[3, 32:64] *= 1e-6
+    x[4, 64:96] *= 300.0
+    x[5 % R, :] = rng.choice([0.25, 0.75, 1.25, -2.5, 5.0, 6.0, 0.0], size=C).astype(np.float32)
+    if bf16:
+        from oracle.oracle import f32_to_bf16_bits
+        return f32_to_bf16_bits(x)
+    return x
+
+
+CASES = []
+for fmt in (0, 1):
+    for rnd in (0, 1):
+        for axis in (0, 1):
+            for had in ((False, True) if fmt == 1 else (False,)):
+                for bf16 in (True, False):
+                    CASES.append((fmt, rnd, axis, had, bf16))
+
+
+@pytest.mark.parametrize("fmt,rnd,axis,had,bf16", CASES)
+@pytest.mark.parametrize("shape", [(96, 1056), (256, 256), (32, 64)])
+def test_quantize_matches_oracle(fp4, orc, fmt, rnd, axis, had, bf16, shape):
+    say("quantize", shape, "fmt", fmt, "rnd", rnd, "axis", axis, "had", had, "bf16", bf16)
+    xh = _mixed(shape, 7 + shape[0], bf16)
+    signs = orc.hadamard_signs(5) if had else 0
+    want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=11, index_offset=64,
+                        had_on=had, had_signs=signs)
+    x = to_device(xh)
+    q = fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=11, index_offset=64,
+                     had_signs=signs if had else None)
+    assert_same_quant(q_to_host(q), want, "quantize")
+
+
+def test_amax_ready_reuses_the_given_amax(fp4, orc):
+    import torch
+    xh = _mixed((64, 512), 3)
+    x = to_device(xh)
+    a = fp4.quantize(x, axis=0)
+    b = fp4.quantize(x, axis=1, rnd=1, seed=2, amax_from=a)
+    want = orc.quantize(xh, axis=1, rnd=1, seed=2)
+    assert_same_quant(q_to_host(b), want, "rows with amax reuse")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    fp4.fp4_tensor_amax(x, amax)
+    assert float(amax.cpu()[0]) == orc.tensor_amax(xh)
+
+
+def test_strided_source(fp4, orc):
+    import torch
+    xh = _mixed((64, 1024), 4)
+    full = to_device(xh)
+    view = full[:, 256:768]                      # leading dimension 1024, 512 columns
+    want = orc.quantize(np.ascontiguousarray(xh[:, 256:768]), fmt=1, rnd=1, seed=1)
+    q = fp4.quantize(view, fmt=1, rnd=1, seed=1)
+    assert_same_quant(q_to_host(q), want, "strided")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("bf16out", [False, True])
+def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
+    import torch
+    xh = _mixed((96, 1056), 5)
+    qo = orc.quantize(xh, fmt=fmt, had_on=fmt == 1, had_signs=123)
+    q = q_from_oracle(qo, had_signs=123 if fmt == 1 else None)
+    y = fp4.dequantize(q, dtype=torch.bfloat16 if bf16out else torch.float32)
+    want = orc.dequantize_f32(qo)
+    if bf16out:
+        assert np.array_equal(to_host(y), orc.f32_to_bf16_bits(want))
+    else:
+        assert np.array_equal(to_host(y), want)
+
+
+# ------------------------------------------------------------- full sizes
+FULL = [
+    # (workload, role, axis, fmt, rnd, had)  -- the passes of the Llama-7B layer step
+    ("llama7b", "X", 0, 0, 0, False),
+    ("llama7b", "W", 0, 0, 0, False),
+    ("llama7b", "dY", 0, 0, 1, False),
+    ("llama7b", "dY", 1, 0, 1, False),
+    ("llama7b", "X", 1, 0, 1, False),
+    ("llama7b", "W", 1, 0, 1, False),
+    ("llama7b", "X", 0, 1, 0, True),
+    ("llama7b", "W", 0, 1, 0, True),
+]
+
+
+@pytest.mark.parametrize("wl,role,axis,fmt,rnd,had", FULL)
+def test_full_size_quantize_matches_oracle(fp4, orc, wl, role, axis, fmt, rnd, had):
+    import torch
+    from fp4_fully_quantized_amd import workloads
+    say("full-size quantize", wl, role, "axis", axis, "fmt", fmt, "rnd", rnd, "had", had)
+    x = workloads.device_tensor(wl, role)
+    signs = fp4.fp4_hadamard_signs(3) if had else None
+    q = fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=(1 << 8) | (axis + 1),
+                     had_signs=signs)
+    torch.cuda.synchronize()
+    got = q_to_host(q)
+    xh = to_host(x)
+    del q, x
+    want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=(1 << 8) | (axis + 1),
+                        had_on=had, had_signs=signs or 0)
+    assert_same_quant(got, want, f"{wl} {role}")
