@@ -163,7 +163,7 @@ fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, v
   if (A->fmt == FP4_NVFP4 && (!A->tscale || !B->tscale)) return FP4_ERR_NULL;
   if (A->rows <= 0 || B->rows <= 0 || A->cols <= 0 || A->cols != B->cols || A->cols % 128 != 0)
     return FP4_ERR_SHAPE;
-  if ((A->rows + 127) / 128 * ((B->rows + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
+  if (!fp4i_gemm_fits(A->rows, B->rows, A->cols)) return FP4_ERR_SHAPE;
   if (ldc < B->rows) return FP4_ERR_SHAPE;
   if (!aligned16(A->codes) || !aligned16(B->codes) || !aligned16(A->scales) || !aligned16(B->scales))
     return FP4_ERR_ALIGN;

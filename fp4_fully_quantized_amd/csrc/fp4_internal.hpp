@@ -40,4 +40,5 @@ void fp4i_launch_quant(const QuantArgs& a, hipStream_t s);
 void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);
+bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K);
 void fp4i_launch_gemm(const GemmArgs& g, hipStream_t s);

@@ -16,11 +16,24 @@
 //   it is exact in f16: codes are decoded with v_cvt_scalef32_pk_f16_fp4
 //   (scale 1), multiplied by sdec with v_pk_mul_f16 (exact), and fed to
 //   v_mfma_f32_32x32x16_f16. alpha = s_gA * s_gB is applied in the epilogue.
+//   For the f16 MFMA the K order inside an instruction is free as long as A
+//   and B agree: lane half g of substep s carries K values 32g + 8s .. +7 of a
+//   64-value group, so each lane reads 16 contiguous bytes per group.
 //
-// Tiling: 256 threads = 4 waves (2 x 2), workgroup tile BM x BN, K tile of 128
-// values (64 bytes of codes per row), double-buffered in LDS with the 16-byte
-// chunks of each row XOR-swizzled against bank conflicts. Global loads of the
-// next K tile are issued before the MFMAs of the current one.
+// Tiling: 256 threads = 4 waves (2 x 2), workgroup tile 256 x 256 (each wave
+// owns 128 x 128 = 4 x 4 MFMA fragments, accumulators in AGPRs), K tile BK
+// (256 values when K allows, else 128). Global loads are buffer loads (the
+// descriptor's size bound turns rows past M or N into zeros), issued one K
+// tile ahead into VGPRs and written to the other half of a double-buffered
+// LDS tile after the current tile's MFMAs. In LDS the 16-byte chunks of each
+// row are XOR-swizzled by (row / 2) so that the 32 rows read by one ds_read_b128
+// hit distinct banks; the block-scale bytes are permuted on the way in so that
+// each lane fetches the scales of all its substeps with one LDS read (MXFP4:
+// the MFMA's op_sel picks the substep's byte). Operand fragments of the next
+// substep are read while the current substep's MFMAs run. Workgroups are mapped
+// to tiles so that the ones resident on one XCD (dispatch is round-robin over
+// the 8 XCDs) cover a compact group of tile rows and share operand panels in
+// that XCD's L2.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 
@@ -30,94 +43,148 @@ namespace {
 
 constexpr int NV = 0;
 constexpr int MX = 1;
-constexpr int BK = 128;   // K values per tile
-constexpr int ROWB = 64;  // code bytes per row per tile
+constexpr int NXCD = 8;
+constexpr int BM = 256, BN = 256;
+constexpr int WM = 128, WN = 128;
+constexpr int FM = 4, FN = 4;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 
-template <int FMT, int BM, int BN, bool BF16OUT>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
-                                               const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
-                                               const float* __restrict__ a_ts, const float* __restrict__ b_ts,
-                                               int64_t M, int64_t N, int64_t K, uint32_t tiles_n,
-                                               void* __restrict__ cout, int64_t ldc) {
-  constexpr int SCB = FMT == NV ? 8 : 4;  // scale bytes per row per tile
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int CHUNKS = (BM + BN) * 4;           // 16-byte chunks per tile
-  constexpr int CPT = CHUNKS / 256;               // chunks per thread
-  constexpr int SROWS_PT = (BM + BN) / 256;       // scale rows per thread
-  static_assert(CHUNKS % 256 == 0 && (BM + BN) % 256 == 0, "tile");
+// Scaled FP4 MFMA; S selects the byte of the lanes' scale words (op_sel).
+template <int S>
+__device__ __forceinline__ v16f mfma_mx(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, S, sa, S, sb);
+}
+__device__ __forceinline__ v16f mfma_mx_sel(int s, const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return s == 0 ? mfma_mx<0>(a, b, c, sa, sb)
+       : s == 1 ? mfma_mx<1>(a, b, c, sa, sb)
+       : s == 2 ? mfma_mx<2>(a, b, c, sa, sb)
+                : mfma_mx<3>(a, b, c, sa, sb);
+}
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][(BM + BN) * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][(BM + BN) * SCB];
+template <int FMT, int BK>
+struct Cfg {
+  static constexpr int ROWB = BK / 2;               // code bytes per row per K tile
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int SB = FMT == NV ? 16 : 32;    // elements per scale byte
+  static constexpr int SCB = BK / SB;               // scale bytes per row per K tile
+  static constexpr int ROWS = BM + BN;
+  static constexpr int CODE_LOADS = ROWS * CPR / 256;   // 16-byte loads per thread
+  static constexpr int RPL = 256 / CPR;                 // rows covered by one load round
+  static constexpr int SCALE_LOADS = ROWS * SCB / 16 / 256 > 0 ? ROWS * SCB / 16 / 256 : 1;
+  static constexpr int LDS_CODES = ROWS * ROWB;
+  static constexpr int LDS_SCALES = ROWS * SCB;
+};
+
+// Scale bytes of one row permuted so that lane half g finds the bytes of all
+// its substeps contiguous (see the file comment).
+template <int FMT, int BK>
+__device__ __forceinline__ uint4 permute_scales(uint4 v) {
+  if constexpr (FMT == NV && BK == 256) {
+    // 16 blocks; half g uses blocks {2g,2g+1, 2g+4,2g+5, 2g+8,2g+9, 2g+12,2g+13}
+    return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                      __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+  } else if constexpr (FMT == NV) {
+    // 8 blocks in v.x, v.y; half g uses {2g, 2g+1, 2g+4, 2g+5}
+    return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), 0, 0);
+  } else if constexpr (BK == 256) {
+    // 8 blocks in v.x, v.y; half g uses {g, g+2, g+4, g+6}
+    return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u), __builtin_amdgcn_perm(v.y, v.x, 0x07050301u), 0, 0);
+  } else {
+    // 4 blocks in v.x; half g uses {g, g+2}
+    return make_uint4(__builtin_amdgcn_perm(0u, v.x, 0x03010200u), 0, 0, 0);
+  }
+}
+
+template <int FMT, int BK, bool BF16OUT>
+__global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+                                                  const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
+                                                  const float* __restrict__ a_ts, const float* __restrict__ b_ts,
+                                                  uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_m,
+                                                  uint32_t tiles_n, uint32_t per_xcd, uint32_t group_m,
+                                                  void* __restrict__ cout, int64_t ldc) {
+  using C = Cfg<FMT, BK>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][C::LDS_CODES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][C::LDS_SCALES];
+
+  // ---- tile of this workgroup
+  const uint32_t xcd = blockIdx.x % NXCD;
+  const uint32_t t = xcd * per_xcd + blockIdx.x / NXCD;
+  if (t >= tiles_m * tiles_n) return;
+  const uint32_t per_group = group_m * tiles_n;
+  const uint32_t grp = t / per_group;
+  const uint32_t first_m = grp * group_m;
+  const uint32_t gsize = min(group_m, tiles_m - first_m);
+  const uint32_t in_grp = t - grp * per_group;
+  const uint32_t tm = first_m + in_grp % gsize;
+  const uint32_t tn = in_grp / gsize;
+  const uint32_t m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t tm = blockIdx.x / tiles_n;
-  const uint32_t tn = blockIdx.x - tm * tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kb_row = K / 2;                       // code bytes per operand row
-  const int64_t ks_row = K / (FMT == NV ? 16 : 32);   // scale bytes per operand row
+  const uint32_t kb_row = K / 2;
+  const uint32_t ks_row = K / C::SB;
   const int nk = (int)(K / BK);
 
-  // Per-thread global sources (rows clamped into range; clamped rows are never stored).
-  const uint8_t* gsrc[CPT];
-  int ldst[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int q = tid + 256 * j;
-    const int row = q >> 2, c = q & 3;
-    int64_t grow;
-    const uint8_t* base;
-    if (row < BM) {
-      grow = m0 + row; if (grow >= M) grow = M - 1;
-      base = ac + grow * kb_row;
-    } else {
-      grow = n0 + (row - BM); if (grow >= N) grow = N - 1;
-      base = bc + grow * kb_row;
-    }
-    gsrc[j] = base + c * 16;
-    ldst[j] = row * ROWB + ((c ^ swz(row)) * 16);
-  }
-  const uint8_t* ssrc[SROWS_PT];
-  int sdst[SROWS_PT];
-#pragma unroll
-  for (int j = 0; j < SROWS_PT; ++j) {
-    const int row = tid + 256 * j;
-    int64_t grow;
-    const uint8_t* base;
-    if (row < BM) {
-      grow = m0 + row; if (grow >= M) grow = M - 1;
-      base = as + grow * ks_row;
-    } else {
-      grow = n0 + (row - BM); if (grow >= N) grow = N - 1;
-      base = bs + grow * ks_row;
-    }
-    ssrc[j] = base;
-    sdst[j] = row * SCB;
-  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ac, M * kb_row);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(bc, N * kb_row);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as, M * ks_row);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs, N * ks_row);
 
-  uint4 creg[CPT];
-  uint2 sreg[SROWS_PT];
+  // Code loads: load j covers tile rows RPL*j + tid/CPR, chunk tid%CPR.
+  const int lrow = tid / C::CPR, lchk = tid % C::CPR;
+  const uint32_t goff_a = (m0 + lrow) * kb_row + lchk * 16;
+  const uint32_t goff_b = (n0 + lrow) * kb_row + lchk * 16;
+  const int lds_w = lrow * C::ROWB + ((lchk ^ ((lrow >> 1) & (C::CPR - 1))) * 16);
+  constexpr int JA = BM / C::RPL;   // loads that cover A rows
+  // Scale loads: one row per thread (A rows, then B rows).
+  const uint32_t soff_a = (m0 + tid) * ks_row;
+  const uint32_t soff_b = (n0 + tid) * ks_row;
+
+  uint4 creg[C::CODE_LOADS];
+  uint4 sreg[2];
   auto gload = [&](int kt) {
+    const uint32_t kc = (uint32_t)kt * C::ROWB;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) creg[j] = *reinterpret_cast<const uint4*>(gsrc[j] + (int64_t)kt * ROWB);
-#pragma unroll
-    for (int j = 0; j < SROWS_PT; ++j) {
-      if constexpr (SCB == 8) sreg[j] = *reinterpret_cast<const uint2*>(ssrc[j] + (int64_t)kt * SCB);
-      else sreg[j].x = *reinterpret_cast<const uint32_t*>(ssrc[j] + (int64_t)kt * SCB);
+    for (int j = 0; j < C::CODE_LOADS; ++j) {
+      if (j < JA) creg[j] = bload16(ra, goff_a + (uint32_t)(j * C::RPL) * kb_row + kc);
+      else creg[j] = bload16(rb, goff_b + (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
+    }
+    const uint32_t ks = (uint32_t)kt * C::SCB;
+    if constexpr (C::SCB == 16) {
+      sreg[0] = bload16(rsa, soff_a + ks);
+      sreg[1] = bload16(rsb, soff_b + ks);
+    } else if constexpr (C::SCB == 8) {
+      uint2 x = bload8(rsa, soff_a + ks), y = bload8(rsb, soff_b + ks);
+      sreg[0] = make_uint4(x.x, x.y, 0, 0);
+      sreg[1] = make_uint4(y.x, y.y, 0, 0);
+    } else {
+      sreg[0] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(soff_a + ks), 0, 0), 0, 0, 0);
+      sreg[1] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsb, (int)(soff_b + ks), 0, 0), 0, 0, 0);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) *reinterpret_cast<uint4*>(&lds_c[buf][ldst[j]]) = creg[j];
+    for (int j = 0; j < C::CODE_LOADS; ++j)
+      *reinterpret_cast<uint4*>(&lds_c[buf][lds_w + j * C::RPL * C::ROWB]) = creg[j];
 #pragma unroll
-    for (int j = 0; j < SROWS_PT; ++j) {
-      if constexpr (SCB == 8) *reinterpret_cast<uint2*>(&lds_s[buf][sdst[j]]) = sreg[j];
-      else *reinterpret_cast<uint32_t*>(&lds_s[buf][sdst[j]]) = sreg[j].x;
+    for (int h = 0; h < 2; ++h) {
+      uint8_t* p = &lds_s[buf][(tid + 256 * h) * C::SCB];
+      const uint4 v = permute_scales<FMT, BK>(sreg[h]);
+      if constexpr (C::SCB == 16) *reinterpret_cast<uint4*>(p) = v;
+      else if constexpr (C::SCB == 8) *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
+      else *reinterpret_cast<uint32_t*>(p) = v.x;
     }
   };
 
@@ -129,8 +196,17 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ ac, co
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int g = lane >> 5;   // K half of the MFMA operand this lane supplies
+  const int g = lane >> 5;   // which half of the MFMA operand's K this lane supplies
   const int lr = lane & 31;  // operand row inside a 32-row fragment
+  // LDS byte offsets of this lane's fragment rows (A rows, then B rows).
+  int arow[FM], brow[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = wm * WM + i * 32 + lr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) brow[j] = BM + wn * WN + j * 32 + lr;
+  auto frag_addr = [&](int row, int chunk) {
+    return row * C::ROWB + ((chunk ^ ((row >> 1) & (C::CPR - 1))) * 16);
+  };
 
   gload(0);
   lstore(0);
@@ -139,85 +215,132 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ ac, co
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* Ac = lds_c[buf];
-    const uint8_t* Bc = lds_c[buf] + BM * ROWB;
-    const uint8_t* Asc = lds_s[buf];
-    const uint8_t* Bsc = lds_s[buf] + BM * SCB;
+    const uint8_t* L = lds_c[buf];
+    const uint8_t* S = lds_s[buf];
     if constexpr (FMT == MX) {
+      constexpr int NS = BK / 64;   // substeps (one K=64 MFMA each)
+      uint32_t sa[FM], sb[FN];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int chunk = 2 * s + g;
-        v8i a[FM], b[FN];
-        int sa[FM], sb[FN];
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (NS == 4) sa[i] = *reinterpret_cast<const uint32_t*>(S + arow[i] * C::SCB + 4 * g);
+        else sa[i] = *reinterpret_cast<const uint16_t*>(S + arow[i] * C::SCB + 2 * g);
+      }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = wm * WM + i * 32 + lr;
-          uint4 v = *reinterpret_cast<const uint4*>(Ac + row * ROWB + ((chunk ^ swz(row)) * 16));
-          a[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sa[i] = Asc[row * SCB + chunk];
-        }
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (NS == 4) sb[j] = *reinterpret_cast<const uint32_t*>(S + brow[j] * C::SCB + 4 * g);
+        else sb[j] = *reinterpret_cast<const uint16_t*>(S + brow[j] * C::SCB + 2 * g);
+      }
+      uint4 a[2][FM], b[2][FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * WN + j * 32 + lr;
-          uint4 v = *reinterpret_cast<const uint4*>(Bc + row * ROWB + ((chunk ^ swz(row)) * 16));
-          b[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sb[j] = Bsc[row * SCB + chunk];
-        }
+      for (int i = 0; i < FM; ++i) a[0][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g));
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) b[0][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < NS) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            a[cur ^ 1][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], 2 * (s + 1) + g));
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0,
-                                                                          sa[i], 0, sb[j]);
-      }
-    } else {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int chunk = g + 2 * c2;
-        uint4 av[FM], bv[FN];
-        uint32_t asb[FM], bsb[FN];
+            b[cur ^ 1][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], 2 * (s + 1) + g));
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int row = wm * WM + i * 32 + lr;
-          av[i] = *reinterpret_cast<const uint4*>(Ac + row * ROWB + ((chunk ^ swz(row)) * 16));
-          asb[i] = *reinterpret_cast<const uint16_t*>(Asc + row * SCB + 2 * chunk);
+          const v8i av = {(int)a[cur][i].x, (int)a[cur][i].y, (int)a[cur][i].z, (int)a[cur][i].w, 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const v8i bv = {(int)b[cur][j].x, (int)b[cur][j].y, (int)b[cur][j].z, (int)b[cur][j].w, 0, 0, 0, 0};
+            acc[i][j] = mfma_mx_sel(s, av, bv, acc[i][j], (int)sa[i], (int)sb[j]);
+          }
+        }
+      }
+    } else {
+      constexpr int NC = BK / 64;   // chunk pairs; each is 4 substeps of K=16
+      uint32_t sa[FM][2], sb[FN][2];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (NC == 4) {
+          const uint2 v = *reinterpret_cast<const uint2*>(S + arow[i] * C::SCB + 8 * g);
+          sa[i][0] = v.x; sa[i][1] = v.y;
+        } else {
+          sa[i][0] = *reinterpret_cast<const uint32_t*>(S + arow[i] * C::SCB + 4 * g);
+          sa[i][1] = 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (NC == 4) {
+          const uint2 v = *reinterpret_cast<const uint2*>(S + brow[j] * C::SCB + 8 * g);
+          sb[j][0] = v.x; sb[j][1] = v.y;
+        } else {
+          sb[j][0] = *reinterpret_cast<const uint32_t*>(S + brow[j] * C::SCB + 4 * g);
+          sb[j][1] = 0;
+        }
+      }
+      uint4 a[2][FM], b[2][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[0][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[0][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g));
+#pragma unroll
+      for (int c2 = 0; c2 < NC; ++c2) {
+        const int cur = c2 & 1;
+        if (c2 + 1 < NC) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            a[cur ^ 1][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g + 2 * (c2 + 1)));
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            b[cur ^ 1][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g + 2 * (c2 + 1)));
+        }
+        // The two E4M3 scales of this chunk (blocks 2c, 2c+1 of chunk c), as f16 pairs.
+        v2h da[FM][2], db[FN][2];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const uint32_t w = sa[i][c2 >> 1];
+          const float lo = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2) : __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+          const float hi = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 3) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+          da[i][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
+          da[i][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int row = wn * WN + j * 32 + lr;
-          bv[j] = *reinterpret_cast<const uint4*>(Bc + row * ROWB + ((chunk ^ swz(row)) * 16));
-          bsb[j] = *reinterpret_cast<const uint16_t*>(Bsc + row * SCB + 2 * chunk);
+          const uint32_t w = sb[j][c2 >> 1];
+          const float lo = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2) : __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+          const float hi = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 3) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+          db[j][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
+          db[j][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          v8h a[FM], b[FN];
+          v8h av[FM], bv[FN];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const uint32_t w = s == 0 ? av[i].x : s == 1 ? av[i].y : s == 2 ? av[i].z : av[i].w;
-            const _Float16 sd = (_Float16)e4m3_decode((asb[i] >> (8 * (s >> 1))) & 0xFFu);
-            const v2h sd2 = {sd, sd};
-            v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
-            v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
-            v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
-            v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
-            a[i] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+            const uint32_t w = s == 0 ? a[cur][i].x : s == 1 ? a[cur][i].y : s == 2 ? a[cur][i].z : a[cur][i].w;
+            const v2h sd2 = da[i][s >> 1];
+            const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
+            const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
+            const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
+            const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
+            av[i] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
           }
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const uint32_t w = s == 0 ? bv[j].x : s == 1 ? bv[j].y : s == 2 ? bv[j].z : bv[j].w;
-            const _Float16 sd = (_Float16)e4m3_decode((bsb[j] >> (8 * (s >> 1))) & 0xFFu);
-            const v2h sd2 = {sd, sd};
-            v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
-            v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
-            v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
-            v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
-            b[j] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+            const uint32_t w = s == 0 ? b[cur][j].x : s == 1 ? b[cur][j].y : s == 2 ? b[cur][j].z : b[cur][j].w;
+            const v2h sd2 = db[j][s >> 1];
+            const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
+            const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
+            const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
+            const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
+            bv[j] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
           }
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -234,42 +357,58 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ ac, co
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn * WN + j * 32 + lr;
+      const uint32_t col = n0 + wn * WN + j * 32 + lr;
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const uint32_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         if (row >= M) continue;
         float y = acc[i][j][r];
         if constexpr (FMT == NV) y = y * alpha;
         if constexpr (BF16OUT) {
           uint32_t u = __float_as_uint(y);
           u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-          static_cast<uint16_t*>(cout)[row * ldc + col] = (uint16_t)u;
+          static_cast<uint16_t*>(cout)[(int64_t)row * ldc + col] = (uint16_t)u;
         } else {
-          static_cast<float*>(cout)[row * ldc + col] = y;
+          __builtin_nontemporal_store(y, static_cast<float*>(cout) + (int64_t)row * ldc + col);
         }
       }
     }
   }
 }
 
-template <int FMT, int BM, int BN>
+template <int FMT, int BK>
 void launch(const GemmArgs& g, hipStream_t s) {
   const uint32_t tiles_m = (uint32_t)((g.M + BM - 1) / BM);
   const uint32_t tiles_n = (uint32_t)((g.N + BN - 1) / BN);
-  const dim3 grid(tiles_m * tiles_n), block(256);
+  const uint32_t tiles = tiles_m * tiles_n;
+  const uint32_t per_xcd = (tiles + NXCD - 1) / NXCD;
+  const uint32_t group_m = 8;
+  const dim3 grid(per_xcd * NXCD), block(256);
   if (g.bf16out)
-    hipLaunchKernelGGL((k_gemm<FMT, BM, BN, true>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
-                       g.b_scales, g.a_tscale, g.b_tscale, g.M, g.N, g.K, tiles_n, g.c, g.ldc);
+    hipLaunchKernelGGL((k_gemm<FMT, BK, true>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
+                       g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
+                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, BM, BN, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
-                       g.b_scales, g.a_tscale, g.b_tscale, g.M, g.N, g.K, tiles_n, g.c, g.ldc);
+    hipLaunchKernelGGL((k_gemm<FMT, BK, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
+                       g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
+                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc);
 }
 
 }  // namespace
 
+bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K) {
+  // Buffer offsets are 32-bit: each operand's codes must stay below 2^31 bytes.
+  return M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
+}
+
 void fp4i_launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.fmt == NV) launch<NV, 128, 128>(g, s);
-  else launch<MX, 128, 128>(g, s);
+  const bool k256 = g.K % 256 == 0;
+  if (g.fmt == NV) {
+    if (k256) launch<NV, 256>(g, s);
+    else launch<NV, 128>(g, s);
+  } else {
+    if (k256) launch<MX, 256>(g, s);
+    else launch<MX, 128>(g, s);
+  }
 }

@@ -160,7 +160,8 @@ fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64
  * C: device, M x N row-major, leading dimension ldc >= N, FP32 or bf16
  * (rounded to nearest even once, after alpha).
  * Requires: same fmt, had_on and had_signs on both operands; K % 128 == 0;
- * M, N >= 1 (any value); ldc >= N (any value); C aligned to its element size. */
+ * M, N >= 1 (any value); each operand's codes below 2^31 bytes (rows * K / 2);
+ * ldc >= N (any value); C aligned to its element size. */
 fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C,
                     int64_t ldc, fp4_stream_t stream);
 
