@@ -234,11 +234,17 @@ def main():
     quant_bytes = sum(o[3] for o in ops if o[1] == "q")
     quant_ms = sum(r["avg_ms"] for r, o in zip(per_op, ops) if o[1] == "q")
 
+    # HBM bytes per NVFP4 GEMM launch from the committed rocprofv3 counter runs,
+    # valid only while the GEMM sources are the ones the counters were taken on.
+    from fp4_fully_quantized_amd import profiling
+
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
-            traffic = json.load(f).get("nv_gemm_bytes_per_launch")
+            rec = json.load(f)
+        if rec.get("source_digest") == profiling.source_digest():
+            traffic = rec.get("nv_gemm_bytes_per_launch")
 
     out = {
         "metric": "FP4 quantize GB/s + FP4 GEMM TFLOPS (fwd/dgrad/wgrad), % of MI355X roofline",

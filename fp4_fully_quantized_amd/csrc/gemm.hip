@@ -154,13 +154,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
 
   uint4 creg[C::CODE_LOADS];
   uint4 sreg[2];
-  auto gload = [&](int kt) {
+  // Staging of one K tile: code load j (16 bytes) and the two scale rows.
+  auto gload_code = [&](int j, int kt) {
     const uint32_t kc = (uint32_t)kt * C::ROWB;
-#pragma unroll
-    for (int j = 0; j < C::CODE_LOADS; ++j) {
-      if (j < JA) creg[j] = bload16(ra, goff_a + (uint32_t)(j * C::RPL) * kb_row + kc);
-      else creg[j] = bload16(rb, goff_b + (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
-    }
+    if (j < JA) creg[j] = bload16(ra, goff_a + (uint32_t)(j * C::RPL) * kb_row + kc);
+    else creg[j] = bload16(rb, goff_b + (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
+  };
+  auto gload_scales = [&](int kt) {
     const uint32_t ks = (uint32_t)kt * C::SCB;
     if constexpr (C::SCB == 16) {
       sreg[0] = bload16(rsa, soff_a + ks);
@@ -174,10 +174,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
       sreg[1] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsb, (int)(soff_b + ks), 0, 0), 0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::CODE_LOADS; ++j)
-      *reinterpret_cast<uint4*>(&lds_c[buf][lds_w + j * C::RPL * C::ROWB]) = creg[j];
+  auto lstore_code = [&](int j, int buf) {
+    *reinterpret_cast<uint4*>(&lds_c[buf][lds_w + j * C::RPL * C::ROWB]) = creg[j];
+  };
+  auto lstore_scales = [&](int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint8_t* p = &lds_s[buf][(tid + 256 * h) * C::SCB];
@@ -186,6 +186,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
       else if constexpr (C::SCB == 8) *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
       else *reinterpret_cast<uint32_t*>(p) = v.x;
     }
+  };
+  // Write the staged tile to LDS buffer `buf` piece by piece, each piece
+  // followed by the global load of the same piece of tile `kt_next`.
+  auto stage = [&](int j, int buf, int kt_next) {
+    lstore_code(j, buf);
+    gload_code(j, kt_next);
+  };
+  auto stage_scales = [&](int buf, int kt_next) {
+    lstore_scales(buf);
+    gload_scales(kt_next);
   };
 
   v16f acc[FM][FN];
@@ -198,28 +208,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
 
   const int g = lane >> 5;   // which half of the MFMA operand's K this lane supplies
   const int lr = lane & 31;  // operand row inside a 32-row fragment
-  // LDS byte offsets of this lane's fragment rows (A rows, then B rows).
+  // LDS rows of this lane's fragments (A rows, then B rows).
   int arow[FM], brow[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) arow[i] = wm * WM + i * 32 + lr;
 #pragma unroll
   for (int j = 0; j < FN; ++j) brow[j] = BM + wn * WN + j * 32 + lr;
-  auto frag_addr = [&](int row, int chunk) {
-    return row * C::ROWB + ((chunk ^ ((row >> 1) & (C::CPR - 1))) * 16);
+  auto frag = [&](const uint8_t* L, int row, int chunk) {
+    return *reinterpret_cast<const uint4*>(L + row * C::ROWB + ((chunk ^ ((row >> 1) & (C::CPR - 1))) * 16));
   };
 
-  gload(0);
-  lstore(0);
+  // Pipeline: tile 0 in LDS buffer 0 and tile 1 in the staging registers
+  // before the loop. Iteration kt computes tile kt from buffer kt&1 while it
+  // writes tile kt+1 from the registers into the other buffer and loads tile
+  // kt+2 into the registers (clamped at the last tile: the extra loads and
+  // writes are never read). One barrier per iteration, placed before the last
+  // group of MFMAs, whose operand reads were issued before it; after it the
+  // first operands of tile kt+1 are read while those MFMAs run.
+#pragma unroll
+  for (int j = 0; j < C::CODE_LOADS; ++j) gload_code(j, 0);
+  gload_scales(0);
+#pragma unroll
+  for (int j = 0; j < C::CODE_LOADS; ++j) stage(j, 0, nk > 1 ? 1 : 0);
+  stage_scales(0, nk > 1 ? 1 : 0);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* L = lds_c[buf];
-    const uint8_t* S = lds_s[buf];
-    if constexpr (FMT == MX) {
-      constexpr int NS = BK / 64;   // substeps (one K=64 MFMA each)
-      uint32_t sa[FM], sb[FN];
+  if constexpr (FMT == MX) {
+    constexpr int NS = BK / 64;                          // substeps (one K=64 MFMA each)
+    constexpr int PER = (C::CODE_LOADS + NS - 2) / (NS - 1);  // staging pieces per substep
+    uint32_t sa[FM], sb[FN];
+    uint4 a[2][FM], b[2][FN];
+    auto read_scales = [&](const uint8_t* S) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if constexpr (NS == 4) sa[i] = *reinterpret_cast<const uint32_t*>(S + arow[i] * C::SCB + 4 * g);
@@ -230,122 +249,128 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
         if constexpr (NS == 4) sb[j] = *reinterpret_cast<const uint32_t*>(S + brow[j] * C::SCB + 4 * g);
         else sb[j] = *reinterpret_cast<const uint16_t*>(S + brow[j] * C::SCB + 2 * g);
       }
-      uint4 a[2][FM], b[2][FN];
+    };
+    auto read_frags = [&](const uint8_t* L, int s, int dst) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[0][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g));
+      for (int i = 0; i < FM; ++i) a[dst][i] = frag(L, arow[i], 2 * s + g);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[0][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g));
+      for (int j = 0; j < FN; ++j) b[dst][j] = frag(L, brow[j], 2 * s + g);
+    };
+    read_scales(lds_s[0]);
+    read_frags(lds_c[0], 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+      uint32_t sa_keep[FM], sb_keep[FN];  // scales of tile kt while tile kt+1's are read
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int cur = s & 1;
-        if (s + 1 < NS) {
+        if (s == NS - 1) {
+          __syncthreads();
+          // first operands of tile kt+1 (its buffer is complete after the barrier)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            a[cur ^ 1][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], 2 * (s + 1) + g));
+          for (int i = 0; i < FM; ++i) sa_keep[i] = sa[i];
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            b[cur ^ 1][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], 2 * (s + 1) + g));
+          for (int j = 0; j < FN; ++j) sb_keep[j] = sb[j];
+          read_scales(lds_s[buf ^ 1]);
+          read_frags(lds_c[buf ^ 1], 0, cur ^ 1);
+        } else {
+          read_frags(lds_c[buf], s + 1, cur ^ 1);
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (s * PER + q < C::CODE_LOADS) stage(s * PER + q, buf ^ 1, kn);
+          if (s == NS - 2) stage_scales(buf ^ 1, kn);
         }
+        const uint32_t* SA = (s == NS - 1) ? sa_keep : sa;
+        const uint32_t* SB = (s == NS - 1) ? sb_keep : sb;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const v8i av = {(int)a[cur][i].x, (int)a[cur][i].y, (int)a[cur][i].z, (int)a[cur][i].w, 0, 0, 0, 0};
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const v8i bv = {(int)b[cur][j].x, (int)b[cur][j].y, (int)b[cur][j].z, (int)b[cur][j].w, 0, 0, 0, 0};
-            acc[i][j] = mfma_mx_sel(s, av, bv, acc[i][j], (int)sa[i], (int)sb[j]);
+            acc[i][j] = mfma_mx_sel(s, av, bv, acc[i][j], (int)SA[i], (int)SB[j]);
           }
         }
       }
-    } else {
-      constexpr int NC = BK / 64;   // chunk pairs; each is 4 substeps of K=16
-      uint32_t sa[FM][2], sb[FN][2];
+    }
+  } else {
+    constexpr int NC = BK / 64;                          // chunk pairs; each is 4 substeps of K=16
+    constexpr int PER = (C::CODE_LOADS + NC - 2) / (NC - 1);
+    uint32_t sw[FM + FN][2];                             // scale words of the tile (A frags, then B)
+    uint4 raw[2][FM + FN];
+    auto read_scales = [&](const uint8_t* S) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int f = 0; f < FM + FN; ++f) {
+        const int row = f < FM ? arow[f] : brow[f - FM];
         if constexpr (NC == 4) {
-          const uint2 v = *reinterpret_cast<const uint2*>(S + arow[i] * C::SCB + 8 * g);
-          sa[i][0] = v.x; sa[i][1] = v.y;
+          const uint2 v = *reinterpret_cast<const uint2*>(S + row * C::SCB + 8 * g);
+          sw[f][0] = v.x; sw[f][1] = v.y;
         } else {
-          sa[i][0] = *reinterpret_cast<const uint32_t*>(S + arow[i] * C::SCB + 4 * g);
-          sa[i][1] = 0;
+          sw[f][0] = *reinterpret_cast<const uint32_t*>(S + row * C::SCB + 4 * g);
+          sw[f][1] = 0;
         }
       }
+    };
+    auto read_raw = [&](const uint8_t* L, int c2, int dst) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (NC == 4) {
-          const uint2 v = *reinterpret_cast<const uint2*>(S + brow[j] * C::SCB + 8 * g);
-          sb[j][0] = v.x; sb[j][1] = v.y;
-        } else {
-          sb[j][0] = *reinterpret_cast<const uint32_t*>(S + brow[j] * C::SCB + 4 * g);
-          sb[j][1] = 0;
-        }
-      }
-      uint4 a[2][FM], b[2][FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) a[0][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b[0][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g));
+      for (int f = 0; f < FM + FN; ++f) raw[dst][f] = frag(L, f < FM ? arow[f] : brow[f - FM], g + 2 * c2);
+    };
+    read_scales(lds_s[0]);
+    read_raw(lds_c[0], 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+      uint32_t sw_cur[FM + FN][2];
 #pragma unroll
       for (int c2 = 0; c2 < NC; ++c2) {
         const int cur = c2 & 1;
-        if (c2 + 1 < NC) {
+        if (c2 == 0) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            a[cur ^ 1][i] = *reinterpret_cast<const uint4*>(L + frag_addr(arow[i], g + 2 * (c2 + 1)));
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            b[cur ^ 1][j] = *reinterpret_cast<const uint4*>(L + frag_addr(brow[j], g + 2 * (c2 + 1)));
+          for (int f = 0; f < FM + FN; ++f) { sw_cur[f][0] = sw[f][0]; sw_cur[f][1] = sw[f][1]; }
         }
-        // The two E4M3 scales of this chunk (blocks 2c, 2c+1 of chunk c), as f16 pairs.
-        v2h da[FM][2], db[FN][2];
+        // The two E4M3 scales of this chunk pair (blocks 2c, 2c+1 of chunk c), as f16 pairs.
+        v2h sd[FM + FN][2];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const uint32_t w = sa[i][c2 >> 1];
+        for (int f = 0; f < FM + FN; ++f) {
+          const uint32_t w = sw_cur[f][c2 >> 1];
           const float lo = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2) : __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
           const float hi = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 3) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-          da[i][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
-          da[i][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
+          sd[f][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
+          sd[f][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
         }
+        if (c2 == NC - 1) {
+          __syncthreads();
+          read_scales(lds_s[buf ^ 1]);
+          read_raw(lds_c[buf ^ 1], 0, cur ^ 1);
+        } else {
+          read_raw(lds_c[buf], c2 + 1, cur ^ 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint32_t w = sb[j][c2 >> 1];
-          const float lo = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2) : __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-          const float hi = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 3) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-          db[j][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
-          db[j][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
+          for (int q = 0; q < PER; ++q)
+            if (c2 * PER + q < C::CODE_LOADS) stage(c2 * PER + q, buf ^ 1, kn);
+          if (c2 == NC - 2) stage_scales(buf ^ 1, kn);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          v8h av[FM], bv[FN];
+          v8h op[FM + FN];
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const uint32_t w = s == 0 ? a[cur][i].x : s == 1 ? a[cur][i].y : s == 2 ? a[cur][i].z : a[cur][i].w;
-            const v2h sd2 = da[i][s >> 1];
+          for (int f = 0; f < FM + FN; ++f) {
+            const uint32_t w = s == 0 ? raw[cur][f].x : s == 1 ? raw[cur][f].y : s == 2 ? raw[cur][f].z : raw[cur][f].w;
+            const v2h sd2 = sd[f][s >> 1];
             const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
             const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
             const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
             const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
-            av[i] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-          }
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const uint32_t w = s == 0 ? b[cur][j].x : s == 1 ? b[cur][j].y : s == 2 ? b[cur][j].z : b[cur][j].w;
-            const v2h sd2 = db[j][s >> 1];
-            const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
-            const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
-            const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
-            const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
-            bv[j] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+            op[f] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
           }
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i], op[FM + j], acc[i][j], 0, 0, 0);
         }
       }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   float alpha = 1.0f;
