@@ -48,6 +48,11 @@ constexpr int BM = 256, BN = 256;
 constexpr int WM = 128, WN = 128;
 constexpr int FM = 4, FN = 4;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -291,6 +296,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
             const v8i bv = {(int)b[cur][j].x, (int)b[cur][j].y, (int)b[cur][j].z, (int)b[cur][j].w, 0, 0, 0, 0};
             acc[i][j] = mfma_mx_sel(s, av, bv, acc[i][j], (int)SA[i], (int)SB[j]);
           }
+        }
+        // Instruction order for the scheduler: the next substep's LDS reads
+        // first, then the MFMAs with the staging writes and global loads
+        // threaded between them, so LDS and memory latency run under MFMAs.
+        if (s < NS - 1) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FM + FN, 0);
+#pragma unroll
+          for (int q = 0; q < PER; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM * FN - 2 * PER > 0 ? FM * FN - 2 * PER : 0, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (FM + FN), 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM * FN, 0);
         }
       }
     }

@@ -36,6 +36,9 @@ constexpr int MX = 1;
 
 __global__ void k_zero1(float* p) { *p = 0.0f; }
 
+// A wave task is a 2048-element segment of one row: each lane issues four
+// independent 16-byte (bf16) loads before reducing, to keep enough bytes in
+// flight per CU.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_amax(const void* __restrict__ src, int64_t C, int64_t ld,
                                                uint32_t spr, uint32_t ntasks, float* amax) {
@@ -48,13 +51,20 @@ __global__ __launch_bounds__(256) void k_amax(const void* __restrict__ src, int6
     const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
     const uint32_t r = tu / spr;
     const uint32_t seg = tu - r * spr;
-    const int64_t col = (int64_t)seg * 512 + lane * 8;
-    if (col < C) {
-      float x[8];
-      load8<BF16>(static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES, x);
+    const char* row = static_cast<const char*>(src) + (int64_t)r * ld * ES;
+    float x[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+    for (int k = 0; k < 4; ++k) {
+      const int64_t col = (int64_t)seg * 2048 + k * 512 + lane * 8;
+      if (col < C) load8<BF16>(row + col * ES, x[k]);
+      else
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[k][i] = 0.0f;
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[k][i]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -366,7 +376,7 @@ void launch_src(const QuantArgs& a, hipStream_t s) {
 void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
                       hipStream_t s) {
   hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax);
-  const uint32_t spr = (uint32_t)((C + 511) / 512);
+  const uint32_t spr = (uint32_t)((C + 2047) / 2048);
   const uint32_t ntasks = (uint32_t)(R * spr);
   if (bf16)
     hipLaunchKernelGGL(k_amax<true>, dim3(strided_grid(ntasks)), dim3(256), 0, s, src, C, ld, spr,
