@@ -5,6 +5,12 @@
 runs a plain device copy of a known size (1 GiB, bf16) a few times, so that
 the HBM byte counters read for it (FETCH_SIZE, WRITE_SIZE) can calibrate the
 same counters read for the library's kernels.
+
+    python -m fp4_fully_quantized_amd.profiling summarize OUT
+
+reads the rocprofv3 CSV output of the profiling commands listed in
+PROFILE_COMMANDS (under the folder OUT) and writes the text summaries and
+profiles/traffic.json that the benchmark's roofline figure reads.
 """
 import sys
 
@@ -23,17 +29,12 @@ def copy(reps: int = 3) -> None:
     print(f"copied {COPY_BYTES} bytes x {reps}", flush=True)
 
 
-if __name__ == "__main__":
-    if len(sys.argv) > 1 and sys.argv[1] == "copy":
-        copy()
-    else:
-        print(__doc__)
-
-
 # ---------------------------------------------------------------- summaries
 def short_name(name: str) -> str:
-    base = name.split("(")[0].replace("void ", "").replace("(anonymous namespace)::", "")
-    return base.strip()
+    base = name.replace("(anonymous namespace)::", "")
+    if base.startswith("void "):
+        base = base[5:]
+    return base.split("(")[0].strip()
 
 
 def kernel_stats_table(csv_path: str, top: int = 20) -> str:
@@ -73,3 +74,156 @@ def source_digest() -> str:
         with open(os.path.join(here, "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- the profile set
+# The commands whose output `summarize` reads, run from the repository root on one
+# MI355X after `cd /tmp && export TMPDIR=/tmp` (OUT = their output folder).
+PROFILE_COMMANDS = {
+    "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_bench -o bench -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
+             "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
+             "-d OUT/pmc_write -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o copy -- "
+                  "python3 -m fp4_fully_quantized_amd.profiling copy",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o copy -- "
+                  "python3 -m fp4_fully_quantized_amd.profiling copy",
+}
+
+# Kernel groups of one benchmark step, in step order: (label, name regex, bytes or
+# flops per launch is computed by the benchmark itself).
+GROUPS = [
+    ("NVFP4 GEMM (fwd bf16 out; dgrad, wgrad fp32 out)", r"^k_gemm<0,"),
+    ("MXFP4 GEMM (fwd, bf16 out)", r"^k_gemm<1,"),
+    ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
+    ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
+    ("tensor amax", r"^k_amax<"),
+]
+
+
+def _trace_groups(trace_csv: str):
+    """{group label: [durations in ns]} from a rocprofv3 kernel_trace.csv."""
+    import csv
+    import re
+
+    out = {label: [] for label, _ in GROUPS}
+    for r in csv.DictReader(open(trace_csv)):
+        name = short_name(r["Kernel_Name"])
+        for label, rx in GROUPS:
+            if re.search(rx, name):
+                out[label].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def _gemm_shape(grid: int, index: int):
+    names = ["fwd 32768x11008x4096 (bf16 out)", "dgrad 32768x4096x11008 (fp32 out)",
+             "wgrad 11008x4096x32768 (fp32 out)"]
+    return names[index % 3]
+
+
+def summarize(out_dir: str, profiles_dir: str) -> None:
+    import json
+    import os
+
+    stats_csv = os.path.join(out_dir, "prof_bench", "bench_kernel_stats.csv")
+    trace_csv = os.path.join(out_dir, "prof_bench", "bench_kernel_trace.csv")
+    cmd = lambda k: PROFILE_COMMANDS[k].replace("OUT", "gpurun_out")
+
+    # ---- kernel time of the step
+    groups = _trace_groups(trace_csv)
+    lines = [
+        "# Kernel time of the Llama-7B layer step (bench.py)",
+        "",
+        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first):",
+        "",
+        "```", cmd("stats"), "```",
+        "",
+        "One step = NVFP4 fwd (quantize X, W; GEMM bf16 out), NVFP4 bwd (SR quantize dY, W^T, dY^T, X^T; "
+        "dgrad and wgrad GEMMs fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). 7 steps traced "
+        "(2 warm-up + 5 timed); torch kernels are the one-time input generation.",
+        "",
+        "`k_gemm<0, 256, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *>` = MXFP4 GEMM (scaled FP4 MFMA); "
+        "the last template flag = bf16 output.",
+        "",
+        "## Kernel groups (from the kernel trace)",
+        "",
+        "| group | launches | avg us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for label, _ in GROUPS:
+        d = groups[label]
+        if d:
+            lines.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
+                         f"{max(d) / 1e3:.1f} |")
+    lines += ["", "## Per kernel (`--stats` summary)", "", kernel_stats_table(stats_csv), ""]
+    with open(os.path.join(profiles_dir, "llama7b_step_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines))
+
+    # ---- HBM traffic of the NVFP4 GEMM
+    # Only the copy dispatches (the fill that creates the source is left out).
+    def copy_avg(path, counter):
+        v = [x for _, _, x in counter_per_dispatch(path, counter, "copyBuffer")]
+        return sum(v) / len(v)
+
+    cf = copy_avg(os.path.join(out_dir, "pmc_copy_fetch", "copy_counter_collection.csv"), "FETCH_SIZE")
+    cw = copy_avg(os.path.join(out_dir, "pmc_copy_write", "copy_counter_collection.csv"), "WRITE_SIZE")
+    reps_kib = COPY_BYTES / 1024
+    f_fac = reps_kib / cf
+    w_fac = reps_kib / cw
+    fe = counter_per_dispatch(os.path.join(out_dir, "pmc_fetch", "bench_counter_collection.csv"),
+                              "FETCH_SIZE", r"k_gemm<0,")
+    wr = counter_per_dispatch(os.path.join(out_dir, "pmc_write", "bench_counter_collection.csv"),
+                              "WRITE_SIZE", r"k_gemm<0,")
+    assert len(fe) == len(wr) and len(fe) % 3 == 0, (len(fe), len(wr))
+    rows = []
+    for i, ((_, grid, fk), (_, _, wk)) in enumerate(zip(fe, wr)):
+        rows.append((_gemm_shape(grid, i), grid // 256, fk, wk, (fk * f_fac + wk * w_fac) * 1024))
+    avg = sum(r[4] for r in rows) / len(rows)
+    lines = [
+        "# HBM traffic of the NVFP4 GEMM (Llama-7B layer: fwd, dgrad, wgrad)",
+        "",
+        "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`):",
+        "",
+        "```", cmd("fetch"), cmd("write"), cmd("copy_fetch"), cmd("copy_write"), "```",
+        "",
+        "## Calibration with a plain copy of 1 GiB (`__amd_rocclr_copyBuffer`, average of 3 dispatches)",
+        "",
+        f"FETCH_SIZE reads {cf:.0f} KiB for {reps_kib:.0f} KiB read -> factor {f_fac:.3f}; "
+        f"WRITE_SIZE reads {cw:.0f} KiB for {reps_kib:.0f} KiB written -> factor {w_fac:.3f}.",
+        "",
+        "## Per dispatch (KiB as read, then bytes after calibration)",
+        "",
+        "| GEMM | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) |",
+        "|---|---|---|---|---|",
+    ]
+    for name, wgs, fk, wk, b in rows:
+        lines.append(f"| {name} | {wgs} WGs | {fk:.0f} | {wk:.0f} | {b / 1e6:.1f} MB |")
+    lines += [
+        "",
+        f"Average over the NVFP4 GEMM launches: {avg / 1e6:.1f} MB per launch (this is `roofline.traffic`).",
+        "Algorithmic bytes per launch are 100.7 MB of operands (codes + scales of both operands) plus the "
+        "output (721 MB bf16 fwd, 537 MB fp32 dgrad, 180 MB fp32 wgrad).",
+        "",
+        f"GEMM source digest: `{source_digest()}`.",
+        "",
+    ]
+    with open(os.path.join(profiles_dir, "nvfp4_gemm_llama7b_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines))
+    with open(os.path.join(profiles_dir, "traffic.json"), "w") as f:
+        json.dump({"nv_gemm_bytes_per_launch": round(avg), "source_digest": source_digest(),
+                   "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}, f, indent=1)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "copy":
+        copy()
+    elif len(sys.argv) > 2 and sys.argv[1] == "summarize":
+        import os
+
+        summarize(sys.argv[2], os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                            "profiles"))
+    else:
+        print(__doc__)

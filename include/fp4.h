@@ -155,8 +155,9 @@ fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64
  * shared contraction axis K), M = A->rows, N = B->rows, K = A->cols = B->cols,
  * alpha = (*A->tscale) * (*B->tscale) for NVFP4 and 1 for MXFP4.
  *   MXFP4 runs on the gfx950 block-scaled FP4 MFMA with the E8M0 bytes as its
- *   scale operands. NVFP4 decodes e2m1 * E4M3 exactly into bf16 in registers
- *   (at most 6 significant bits) and runs the bf16 MFMA.
+ *   scale operands. NVFP4 decodes e2m1 * E4M3 exactly into f16 in registers
+ *   (at most 6 significant bits, magnitudes in [2^-10, 2688]) and runs the
+ *   f16 MFMA.
  * C: device, M x N row-major, leading dimension ldc >= N, FP32 or bf16
  * (rounded to nearest even once, after alpha).
  * Requires: same fmt, had_on and had_signs on both operands; K % 128 == 0;
