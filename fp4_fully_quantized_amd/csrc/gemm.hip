@@ -33,7 +33,10 @@
 // substep are read while the current substep's MFMAs run. Workgroups are mapped
 // to tiles so that the ones resident on one XCD (dispatch is round-robin over
 // the 8 XCDs) cover a compact group of tile rows and share operand panels in
-// that XCD's L2.
+// that XCD's L2. The MFMAs take the B fragment first, so each lane's
+// accumulator holds four consecutive columns of one output row; after the K
+// loop each wave stages its outputs through the idle LDS tiles, 32 rows at a
+// time, and every store instruction writes whole rows in 16-byte pieces.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 
@@ -116,10 +119,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
                                                   const float* __restrict__ a_ts, const float* __restrict__ b_ts,
                                                   uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_m,
                                                   uint32_t tiles_n, uint32_t per_xcd, uint32_t group_m,
-                                                  void* __restrict__ cout, int64_t ldc) {
+                                                  void* __restrict__ cout, int64_t ldc, uint32_t vec_ok) {
   using C = Cfg<FMT, BK>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[2][C::LDS_CODES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s[2][C::LDS_SCALES];
+  // One LDS array: the double-buffered code and scale tiles of the K loop,
+  // reused afterwards to stage the output tile for row-contiguous stores.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (C::LDS_CODES + C::LDS_SCALES)];
+  uint8_t (*lds_c)[C::LDS_CODES] = reinterpret_cast<uint8_t (*)[C::LDS_CODES]>(lds);
+  uint8_t (*lds_s)[C::LDS_SCALES] = reinterpret_cast<uint8_t (*)[C::LDS_SCALES]>(lds + 2 * C::LDS_CODES);
 
   // ---- tile of this workgroup
   const uint32_t xcd = blockIdx.x % NXCD;
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const v8i bv = {(int)b[cur][j].x, (int)b[cur][j].y, (int)b[cur][j].z, (int)b[cur][j].w, 0, 0, 0, 0};
-            acc[i][j] = mfma_mx_sel(s, av, bv, acc[i][j], (int)SA[i], (int)SB[j]);
+            acc[i][j] = mfma_mx_sel(s, bv, av, acc[i][j], (int)SB[j], (int)SA[i]);
           }
         }
         // Instruction order for the scheduler: the next substep's LDS reads
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i], op[FM + j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[FM + j], op[i], acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -398,26 +404,75 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   float alpha = 1.0f;
   if constexpr (FMT == NV) alpha = (*a_ts) * (*b_ts);
 
-  // Epilogue. Lane l of a 32x32 fragment holds column l%32 and rows
-  // 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
+  // Epilogue. The MFMAs take the B fragment as their first operand, so the
+  // accumulator of fragments (i, j) is the transposed product: lane l holds
+  // output row i*32 + l%32 (of the wave's 128 rows) and columns j*32 + 8*(r/4)
+  // + 4*(l/32) + r%4, r = 0..15: four consecutive columns of one row per group
+  // of four r. bf16 outputs are rounded to nearest even.
+  constexpr int ES = BF16OUT ? 2 : 4;  // output element bytes
+  const uint32_t row0 = m0 + wm * WM;  // first output row / column of this wave
+  const uint32_t col0 = n0 + wn * WN;
+  auto out_at = [&](uint32_t row, uint32_t col) {
+    return static_cast<uint8_t*>(cout) + ((int64_t)row * ldc + col) * ES;
+  };
+  if (vec_ok && m0 + BM <= M && n0 + BN <= N) {
+    // Interior tile: staged through LDS, 32 rows of the wave at a time, so
+    // that every store instruction writes whole rows in 16-byte pieces
+    // (non-temporal: the output is not read again by this kernel). The row
+    // pitch of 132 outputs (4 of padding) keeps the LDS writes and reads free
+    // of bank conflicts.
+    constexpr int PITCH = 132 * ES;
+    static_assert(4 * 32 * PITCH <= 2 * (C::LDS_CODES + C::LDS_SCALES), "output staging exceeds the LDS tiles");
+    __syncthreads();  // every wave is done with the K loop's LDS tiles
+    uint8_t* stage = lds + wave * 32 * PITCH;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const uint32_t col = n0 + wn * WN + j * 32 + lr;
-      if (col >= N) continue;
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row >= M) continue;
-        float y = acc[i][j][r];
-        if constexpr (FMT == NV) y = y * alpha;
-        if constexpr (BF16OUT) {
-          uint32_t u = __float_as_uint(y);
-          u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-          static_cast<uint16_t*>(cout)[(int64_t)row * ldc + col] = (uint16_t)u;
-        } else {
-          __builtin_nontemporal_store(y, static_cast<float*>(cout) + (int64_t)row * ldc + col);
+        for (int q = 0; q < 4; ++q) {
+          v4f y = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if constexpr (FMT == NV) y = y * alpha;
+          uint8_t* d = stage + lr * PITCH + (j * 32 + 8 * q + 4 * g) * ES;
+          if constexpr (BF16OUT) {
+            const v2bf lo = __builtin_convertvector((v2f){y[0], y[1]}, v2bf);
+            const v2bf hi = __builtin_convertvector((v2f){y[2], y[3]}, v2bf);
+            *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          } else {
+            *reinterpret_cast<v4f*>(d) = y;
+          }
+        }
+      }
+      // Read back 16 bytes per lane: a row of 128 outputs is 128 * ES / 16 lanes.
+      constexpr int LPR = 128 * ES / 16;  // lanes per row
+      constexpr int RPS = 64 / LPR;       // rows per store instruction
+#pragma unroll
+      for (int k = 0; k < 32 / RPS; ++k) {
+        const int rr = k * RPS + lane / LPR;
+        const int cc = (lane % LPR) * (16 / ES);
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH + cc * ES);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t row = row0 + i * 32 + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t col = col0 + j * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (col >= N) continue;
+          float y = acc[i][j][r];
+          if constexpr (FMT == NV) y = y * alpha;
+          if constexpr (BF16OUT) {
+            const v2bf b = __builtin_convertvector((v2f){y, y}, v2bf);
+            *reinterpret_cast<uint16_t*>(out_at(row, col)) = __builtin_bit_cast(uint16_t, b[0]);
+          } else {
+            *reinterpret_cast<float*>(out_at(row, col)) = y;
+          }
         }
       }
     }
@@ -432,14 +487,18 @@ void launch(const GemmArgs& g, hipStream_t s) {
   const uint32_t per_xcd = (tiles + NXCD - 1) / NXCD;
   const uint32_t group_m = 8;
   const dim3 grid(per_xcd * NXCD), block(256);
+  // Interior tiles store 16-byte pieces of output rows: the base address and
+  // every row start must be 16-byte aligned.
+  const int64_t es = g.bf16out ? 2 : 4;
+  const uint32_t vec_ok = (g.ldc * es) % 16 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
   if (g.bf16out)
     hipLaunchKernelGGL((k_gemm<FMT, BK, true>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
                        g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
-                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc);
+                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc, vec_ok);
   else
     hipLaunchKernelGGL((k_gemm<FMT, BK, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
                        g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
-                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc);
+                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc, vec_ok);
 }
 
 }  // namespace
