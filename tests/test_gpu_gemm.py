@@ -80,28 +80,33 @@ def _rows_of(q, rows):
     return d
 
 
-def _sample_rows(M, seed):
+def _sample_rows(M, seed, n=64):
+    """The first and last n rows (first and last row tiles) and n random rows."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
-                                     rng.integers(0, M, 64)]))
+    return np.unique(np.concatenate([np.arange(n), np.arange(M - n, M),
+                                     rng.integers(0, M, n)]))
 
 
-# Full Llama-7B-shaped GEMMs (32768 tokens, 4096 in, 11008 out): the forward
-# on NVFP4 and MXFP4+Hadamard operands, dgrad and wgrad on SR operands.
+# Full-size GEMMs. Llama-7B-shaped layer (32768 tokens, 4096 in, 11008 out):
+# the forward on NVFP4 and MXFP4+Hadamard operands, dgrad and wgrad on SR
+# operands. Large layer (16384 tokens, 8192 in, 28672 out): the NVFP4 step.
 FULL = [
-    ("fwd-nvfp4", "bf16"),
-    ("fwd-mxfp4", "bf16"),
-    ("dgrad", "fp32"),
-    ("wgrad", "fp32"),
+    ("llama7b", "fwd-nvfp4", "bf16"),
+    ("llama7b", "fwd-mxfp4", "bf16"),
+    ("llama7b", "dgrad", "fp32"),
+    ("llama7b", "wgrad", "fp32"),
+    ("large", "fwd-nvfp4", "bf16"),
+    ("large", "dgrad", "fp32"),
+    ("large", "wgrad", "fp32"),
 ]
 
 
-@pytest.mark.parametrize("which,out", FULL)
-def test_full_size_gemm_sampled_rows(fp4, orc, which, out):
+@pytest.mark.parametrize("wl,which,out", FULL)
+def test_full_size_gemm_sampled_rows(fp4, orc, wl, which, out):
     from fp4_fully_quantized_amd import workloads
     import torch
-    say("full-size gemm", which, out)
-    dev = lambda role: to_host(workloads.device_tensor("llama7b", role))
+    say("full-size gemm", wl, which, out)
+    dev = lambda role: to_host(workloads.device_tensor(wl, role))
     signs = 0
     if which.startswith("fwd"):
         fmt = 0 if which == "fwd-nvfp4" else 1
@@ -126,7 +131,7 @@ def test_full_size_gemm_sampled_rows(fp4, orc, which, out):
     A = q_from_oracle(qa, had_signs=signs if had else None)
     B = q_from_oracle(qb, had_signs=signs if had else None)
     y = fp4.gemm(A, B, dtype=torch.bfloat16 if out == "bf16" else torch.float32)
-    rows = _sample_rows(qa["rows"], 17)
+    rows = _sample_rows(qa["rows"], 17, 64 if wl == "llama7b" else 16)
     yh = to_host(y[torch.from_numpy(rows).cuda()])
     if out == "bf16":
         yh = orc.bf16_bits_to_f32(yh)

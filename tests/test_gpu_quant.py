@@ -101,7 +101,7 @@ def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
 
 # ------------------------------------------------------------- full sizes
 FULL = [
-    # (workload, role, axis, fmt, rnd, had)  -- the passes of the Llama-7B layer step
+    # (workload, role, axis, fmt, rnd, had)  -- the passes of the layer steps
     ("llama7b", "X", 0, 0, 0, False),
     ("llama7b", "W", 0, 0, 0, False),
     ("llama7b", "dY", 0, 0, 1, False),
@@ -110,6 +110,13 @@ FULL = [
     ("llama7b", "W", 1, 0, 1, False),
     ("llama7b", "X", 0, 1, 0, True),
     ("llama7b", "W", 0, 1, 0, True),
+    # the large-layer step (hidden 8192, MLP 28672, 16384 tokens)
+    ("large", "X", 0, 0, 0, False),
+    ("large", "W", 0, 0, 0, False),
+    ("large", "dY", 0, 0, 1, False),
+    ("large", "W", 1, 0, 1, False),
+    ("large", "dY", 1, 0, 1, False),
+    ("large", "X", 1, 0, 1, False),
 ]
 
 
