@@ -106,7 +106,7 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
   const int64_t blocked = axis == FP4_AXIS_ROWS ? R : C;
   if (blocked % B != 0) return FP4_ERR_SHAPE;
   if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
-  if (axis == FP4_AXIS_ROWS && (R + 4 * B - 1) / (4 * B) * ((C + 63) / 64) > 0x7FFFFFFF)
+  if (axis == FP4_AXIS_ROWS && (R + 255) / 256 * ((C + 63) / 64) > 0x7FFFFFFF)
     return FP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (nv && !amax_ready) {

@@ -20,9 +20,11 @@
 //                  lane stores one dword of 8 codes (256 contiguous bytes per
 //                  wave).
 //  * k_quant_rows  blocks along rows (the transposed orientation used by dgrad
-//                  and wgrad operands): a 64(or 128) x 64 tile is loaded with
-//                  coalesced 16-byte row loads, staged through LDS as FP32,
-//                  and each thread quantizes one block down a column.
+//                  and wgrad operands): a 256 x 64 tile is loaded with
+//                  coalesced 16-byte row loads into LDS (input format), each
+//                  thread quantizes one block in each of 2 or 4 adjacent
+//                  columns, and the codes leave through an LDS staging area
+//                  in whole 128-byte lines.
 //  * k_dequant     8 elements per lane.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
@@ -184,22 +186,39 @@ __device__ __forceinline__ void fwht32_local(float x[32]) {
   }
 }
 
-// Transposed quantize: blocks along rows. Tile = TR rows x 64 columns of the
-// input; thread (c = tid % 64, p = tid / 64) quantizes the block of B rows
-// p*B .. p*B+B-1 of column c. Output row c_glob (of R elements) receives it.
+// Transposed quantize: blocks along rows (the orientation of the dgrad and
+// wgrad operands). A workgroup takes a tile of TR = 256 rows x TC = 64
+// columns of the input:
+//  1. coalesced 16-byte row loads into LDS, kept in the input format (row
+//     pitch padded so the column reads below are free of bank conflicts);
+//  2. thread (b, q) quantizes block b (rows b*B .. b*B+B-1) of the NCOL
+//     adjacent columns q*NCOL ..: each LDS read brings one row of those NCOL
+//     columns, so a block costs B reads for NCOL blocks (NVFP4: 4 columns of
+//     16 rows, MXFP4: 2 columns of 32 rows);
+//  3. codes and scale bytes are staged in LDS per output row (= input
+//     column) and written out in whole 128-byte lines.
 template <int FMT, int RND, bool BF16, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src, int64_t R, int64_t C,
                                                      int64_t ld, uint32_t tiles_c,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
                                                      const float* __restrict__ amax, float* tscale,
-                                                     uint64_t seed, uint64_t offset, uint32_t signs) {
+                                                     uint64_t seed, uint64_t offset, uint32_t signs,
+                                                     uint32_t scale_words) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
-  constexpr int TR = 4 * B;
-  constexpr int TC = 64;
-  constexpr int PITCH = TC + 1;
-  __shared__ float tile[TR * PITCH];
+  constexpr int TR = 256, TC = 64;
+  constexpr int NB = TR / B;               // blocks per tile column
+  constexpr int NCOL = NB * TC / 256;      // adjacent columns per thread
+  constexpr int TPB = TC / NCOL;           // threads per block row
+  // Row pitch in bytes: the NCOL-column reads are NCOL*ES bytes and aligned to
+  // that; one extra read's width of padding puts the block rows that one read
+  // instruction touches in disjoint bank ranges.
+  constexpr int PITCH = TC * ES + NCOL * ES;
+  constexpr int SP = TR / 2 + 4;           // staged code bytes per output row (+ padding)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TR * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_c[TC * SP];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_s[TC * NB];
 
   float sg = 1.0f;
   if constexpr (FMT == NV) {
@@ -210,64 +229,120 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
   const uint32_t tc = blockIdx.x - tr * tiles_c;
   const int64_t r0 = (int64_t)tr * TR;
   const int64_t c0 = (int64_t)tc * TC;
+  const int tid = threadIdx.x;
 
-  // Coalesced load: each row of the tile is TC elements = 8 (bf16) or 16 (fp32) 16-byte chunks.
-  constexpr int CPR = TC / 8;  // 8-element chunks per tile row
-  for (int idx = threadIdx.x; idx < TR * CPR; idx += 256) {
-    const int rr = idx / CPR;
-    const int cc = (idx - rr * CPR) * 8;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (r0 + rr < R && c0 + cc < C)
-      load8<BF16>(static_cast<const char*>(src) + ((r0 + rr) * ld + c0 + cc) * ES, x);
+  // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load.
+  constexpr int CPR = TC * ES / 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[rr * PITCH + cc + i] = x[i];
+  for (int k = 0; k < TR * CPR / 256; ++k) {
+    const int idx = k * 256 + tid;
+    const int rr = idx / CPR;
+    const int cc = idx % CPR;
+    const int64_t col = c0 + cc * (16 / ES);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + rr < R && col < C)
+      v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
+    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
   __syncthreads();
 
-  const int c = threadIdx.x & 63;
-  const int p = threadIdx.x >> 6;
-  const int64_t cg = c0 + c;
-  const int64_t rg = r0 + (int64_t)p * B;
-  if (cg >= C || rg >= R) return;
-
-  float x[B];
+  // 2. quantize NCOL blocks per thread.
+  const int b = tid / TPB;
+  const int cl0 = (tid % TPB) * NCOL;
+  const int64_t rg = r0 + (int64_t)b * B;
+  float x[NCOL][B];
 #pragma unroll
-  for (int i = 0; i < B; ++i) x[i] = tile[(p * B + i) * PITCH + c];
-  if constexpr (HAD) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if ((signs >> i) & 1u) x[i] = -x[i];
-    fwht32_local(x);
-    const float hc = hadamard_norm();
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = x[i] * hc;
-  }
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
-  float rcp;
-  const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
-  uint32_t w[B / 8];
-#pragma unroll
-  for (int g = 0; g < B / 8; ++g) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
-    if constexpr (RND == 0) {
-      w[g] = e2m1_rtn_pack8(v);
+  for (int i = 0; i < B; ++i) {
+    const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
+    if constexpr (BF16) {
+      if constexpr (NCOL == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+        x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
+      }
     } else {
-      uint32_t h[8];
-      sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
-      w[g] = e2m1_sr_pack8(v, h);
+      if constexpr (NCOL == 4) {
+        const float4 w = *reinterpret_cast<const float4*>(p);
+        x[0][i] = w.x; x[1][i] = w.y; x[2][i] = w.z; x[3][i] = w.w;
+      } else {
+        const float2 w = *reinterpret_cast<const float2*>(p);
+        x[0][i] = w.x; x[1][i] = w.y;
+      }
     }
   }
-  uint8_t* dst = codes + cg * (R / 2) + rg / 2;
-  if constexpr (B == 16) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  } else {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+  for (int k = 0; k < NCOL; ++k) {
+    const int cl = cl0 + k;
+    const int64_t cg = c0 + cl;
+    float* xk = x[k];
+    if constexpr (HAD) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if ((signs >> i) & 1u) xk[i] = -xk[i];
+      fwht32_local(xk);
+      const float hc = hadamard_norm();
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xk[i] = xk[i] * hc;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
+    float rcp;
+    const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+    uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
+#pragma unroll
+    for (int g = 0; g < B / 8; ++g) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
+      if constexpr (RND == 0) {
+        sc[g] = e2m1_rtn_pack8(v);
+      } else {
+        uint32_t h[8];
+        sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+        sc[g] = e2m1_sr_pack8(v, h);
+      }
+    }
+    stage_s[cl * NB + b] = (uint8_t)sbyte;
   }
-  scales[cg * (R / B) + rg / B] = (uint8_t)sbyte;
+  __syncthreads();
+
+  // 3. write out: output row c0 + cl gets the codes of input rows r0 .. (8-byte
+  // pieces, 16 per row) and the scale bytes of its NB blocks.
+  const int64_t rows_here = R - r0 < TR ? R - r0 : TR;  // a multiple of B
+#pragma unroll
+  for (int k = 0; k < TC * 16 / 256; ++k) {
+    const int idx = k * 256 + tid;
+    const int cl = idx / 16;
+    const int seg = idx % 16;
+    if (c0 + cl < C && seg * 16 < rows_here) {
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
+      *reinterpret_cast<uint2*>(codes + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
+    }
+  }
+  if (scale_words) {
+    // (R / B) % 4 == 0: one 4-byte word per thread covers 4 blocks of a row.
+    constexpr int WPR = NB / 4;
+    if (tid < TC * WPR) {
+      const int cl = tid / WPR;
+      const int wd = tid % WPR;
+      if (c0 + cl < C && wd * 4 * B < rows_here)
+        *reinterpret_cast<uint32_t*>(scales + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
+            *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < (TC * NB + 255) / 256; ++k) {
+      const int idx = k * 256 + tid;
+      const int cl = idx / NB;
+      const int bb = idx % NB;
+      if (idx < TC * NB && c0 + cl < C && bb * B < rows_here)
+        scales[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
+    }
+  }
 }
 
 template <int FMT, bool BF16OUT>
@@ -344,10 +419,11 @@ template <int FMT, int RND, bool BF16, bool HAD>
 void launch_rows(const QuantArgs& a, hipStream_t s) {
   constexpr int B = FMT == NV ? 16 : 32;
   const uint32_t tiles_c = (uint32_t)((a.C + 63) / 64);
-  const uint32_t tiles_r = (uint32_t)((a.R + 4 * B - 1) / (4 * B));
+  const uint32_t tiles_r = (uint32_t)((a.R + 255) / 256);
+  const uint32_t scale_words = (a.R / B) % 4 == 0;
   hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD>), dim3(tiles_c * tiles_r), dim3(256), 0, s,
                      a.src, a.R, a.C, a.ld, tiles_c, a.codes, a.scales, a.amax, a.tscale, a.seed,
-                     a.offset, a.signs);
+                     a.offset, a.signs, scale_words);
 }
 
 template <int FMT, int RND, bool BF16, bool HAD>
