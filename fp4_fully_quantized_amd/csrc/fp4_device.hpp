@@ -94,22 +94,6 @@ __device__ __forceinline__ uint32_t e2m1_rtn_pack8(const float v[8]) {
   return w;
 }
 
-// Stochastic rounding of one value v (scaled) with the 16-bit draw h:
-// a = min(|v|, 6) lies between grid neighbours lo <= a < hi of spacing
-// q = 0.5 (a < 2), 1 (a < 4), 2 (otherwise); with s = a / q, lo = floor(s) q
-// and p = s - floor(s) (exact); round up iff h < p * 2^16. The magnitude code
-// of n * q is n + 2k for q = 2^(k-1).
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t h) {
-  float a = fminf(fabsf(v), 6.0f);
-  int k = (a >= 4.0f) ? 2 : ((a >= 2.0f) ? 1 : 0);
-  float s = __builtin_ldexpf(a, 1 - k);
-  float fl = __builtin_floorf(s);
-  float p = s - fl;
-  uint32_t up = ((float)h < p * 65536.0f) ? 1u : 0u;
-  uint32_t code = (uint32_t)fl + up + 2u * (uint32_t)k;
-  return code | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) ----------------------
 __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                               uint32_t k0, uint32_t k1, uint32_t out[4]) {
@@ -129,23 +113,51 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
   out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-// The 8 16-bit draws of elements 8j .. 8j+7 (j = call index = element / 8).
-__device__ __forceinline__ void sr_draws8(uint64_t seed, uint64_t call, uint32_t h[8]) {
-  uint32_t w[4];
+// The draws of elements 8j .. 8j+7 (j = call index = element / 8): word i
+// holds element 2i's 16-bit draw in its low half, element 2i+1's in its high half.
+__device__ __forceinline__ void sr_draws8(uint64_t seed, uint64_t call, uint32_t w[4]) {
   philox4x32_10((uint32_t)call, (uint32_t)(call >> 32), 0u, 0u, (uint32_t)seed,
                 (uint32_t)(seed >> 32), w);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[2 * i] = w[i] & 0xFFFFu;
-    h[2 * i + 1] = w[i] >> 16;
-  }
 }
 
-__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float v[8], const uint32_t h[8]) {
-  uint32_t w = 0;
+// Stochastic rounding of 8 scaled values v with their 16-bit draws: a = |v|
+// lies between grid neighbours lo <= a < hi (or is >= 6: code 7); with
+// p = (a - lo) / (hi - lo) it rounds up iff h < p * 2^16; the sign is kept
+// (also of zero). Done on the hardware convert v_cvt_scalef32_sr_pk_fp4_f32.
+// Measured on gfx950: it rounds the first value
+// of its pair up iff (R >> 10) + floor(p * 2^22) >= 2^22, R its 32-bit random
+// operand (saturating at 6, keeping the sign, also of zero), and divides the
+// value by the power-of-two scale operand first. With R = ~(h << 16), i.e.
+// R >> 10 = 2^22 - 1 - 64 h, that is floor(p * 2^22) > 64 h, the same as
+// p * 2^22 > 64 h (h < p * 2^16) whenever p * 2^22 is an integer. It is once
+// |v| is rounded up to a multiple of 2^-23: the grid points are such
+// multiples, so the neighbours do not change, and because 64 h is an integer
+// the rounded-up p decides as the exact one. That multiple is passed times
+// 2^23 with the scale operand 2^23. The second value of the pair would use
+// R << 1, not an independent draw, so each value gets its own convert (second
+// value 0); the destination keeps its other bytes, and four byte-selects fill
+// one word for the even elements and one for the odd. w[i] holds the draws of
+// elements 2i (low half) and 2i+1 (high half).
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float v[8], const uint32_t w[4]) {
+  const float k23 = 8388608.0f;  // 2^23
+  uint32_t ev = 0, od = 0;
+#define FP4_SR_CVT(DST, X, R, SEL)                                                               \
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" SEL : "+v"(DST) : "v"(X), "v"(R), "s"(k23))
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_sr(v[i], h[i]) << (4 * i);
-  return w;
+  for (int i = 0; i < 4; ++i) {
+    const v2f xe = {__builtin_copysignf(__builtin_ceilf(fabsf(v[2 * i]) * k23), v[2 * i]), 0.0f};
+    const v2f xo = {__builtin_copysignf(__builtin_ceilf(fabsf(v[2 * i + 1]) * k23), v[2 * i + 1]), 0.0f};
+    const uint32_t nw = ~w[i];
+    const uint32_t re = (nw << 16) | 0xFFFFu;  // ~(h_even << 16)
+    const uint32_t ro = nw | 0xFFFFu;          // ~(h_odd << 16)
+    if (i == 0) { FP4_SR_CVT(ev, xe, re, ""); FP4_SR_CVT(od, xo, ro, ""); }
+    if (i == 1) { FP4_SR_CVT(ev, xe, re, " op_sel:[0,0,1,0]"); FP4_SR_CVT(od, xo, ro, " op_sel:[0,0,1,0]"); }
+    if (i == 2) { FP4_SR_CVT(ev, xe, re, " op_sel:[0,0,0,1]"); FP4_SR_CVT(od, xo, ro, " op_sel:[0,0,0,1]"); }
+    if (i == 3) { FP4_SR_CVT(ev, xe, re, " op_sel:[0,0,1,1]"); FP4_SR_CVT(od, xo, ro, " op_sel:[0,0,1,1]"); }
+  }
+#undef FP4_SR_CVT
+  // Even codes sit in the low nibble of each byte of ev, odd ones in od.
+  return ev | (od << 4);
 }
 
 // ---- Hadamard --------------------------------------------------------------

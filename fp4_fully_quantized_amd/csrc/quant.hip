@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
     if constexpr (RND == 0) {
       w = e2m1_rtn_pack8(v);
     } else {
-      uint32_t h[8];
+      uint32_t h[4];
       sr_draws8(seed, (offset + (uint64_t)r * (uint64_t)C + (uint64_t)col) >> 3, h);
       w = e2m1_sr_pack8(v, h);
     }
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
       if constexpr (RND == 0) {
         sc[g] = e2m1_rtn_pack8(v);
       } else {
-        uint32_t h[8];
+        uint32_t h[4];
         sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
         sc[g] = e2m1_sr_pack8(v, h);
       }

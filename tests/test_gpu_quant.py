@@ -99,6 +99,56 @@ def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
         assert np.array_equal(to_host(y), want)
 
 
+# ------------------------------------------------------- SR decision boundaries
+def _sr_boundary_input(orc, R, C, axis, seed, offset):
+    """fp32 [R, C] whose MXFP4 block exponents are all 0 (element 0 of every
+    block along the blocked axis is 5.5), so the scaled values equal the
+    inputs, and whose other values sit on or next to the stochastic-rounding
+    boundary of their own draw h: p * 2^22 = 64 h - 1, 64 h, 64 h + 1/2,
+    64 h + 1, in each binade of the E2M1 grid, plus values far below the
+    first grid step. The draw is the one of the element's index in the
+    quantized orientation."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((R, C), dtype=np.float32)
+    kinds = ["a1", "a2", "a4", "half", "tiny", "tinier"]
+    for r in range(R):
+        for c in range(C):
+            pos = c % 32 if axis == 0 else r % 32
+            if pos == 0:
+                x[r, c] = 5.5
+                continue
+            idx = offset + (r * C + c if axis == 0 else c * R + r)
+            h = orc.sr_draw16(seed, idx)
+            kind = kinds[(r * 7 + c * 3) % len(kinds)]
+            d = [-1.0, 0.0, 0.5, 1.0][(r + c) % 4]
+            g = 64 * h + d                     # target p * 2^22
+            if kind in ("a1", "a2", "a4"):     # [1,2), [2,4), [4,6): p * 2^22 = rem (22 bits)
+                lo = {"a1": 1.0, "a2": 2.0, "a4": 4.0}[kind]
+                q = {"a1": 0.5, "a2": 1.0, "a4": 2.0}[kind]
+                g = np.floor(g) if g >= 0 else 0.0   # these binades hold integer p * 2^22 only
+                a = lo + q * g / 4194304.0
+            elif kind == "half":               # [0.5, 1): p * 2^22 = m / 2
+                a = 0.5 + 0.5 * max(g, 0.0) / 4194304.0
+            elif kind == "tiny":               # below 0.5: p * 2^22 = a * 2^23
+                a = max(g, 0.25) / 8388608.0
+            else:
+                a = float(rng.choice([2.0 ** -30, 3.0 * 2 ** -40, 2.0 ** -24]))
+            x[r, c] = np.float32(a) * (1.0 if rng.random() < 0.5 else -1.0)
+    return x
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_sr_decision_boundaries(fp4, orc, axis):
+    say("SR boundary cases, axis", axis)
+    R, C = (8, 512) if axis == 0 else (512, 8)
+    seed, offset = 29, 1024
+    xh = _sr_boundary_input(orc, R, C, axis, seed, offset)
+    want = orc.quantize(xh, axis=axis, fmt=1, rnd=1, seed=seed, index_offset=offset)
+    assert (want["scales"] == 127).all()       # every block exponent is 0
+    q = fp4.quantize(to_device(xh), axis=axis, fmt=1, rnd=1, seed=seed, index_offset=offset)
+    assert_same_quant(q_to_host(q), want, "SR boundaries")
+
+
 # ------------------------------------------------------------- full sizes
 FULL = [
     # (workload, role, axis, fmt, rnd, had)  -- the passes of the layer steps
