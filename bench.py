@@ -12,6 +12,11 @@ measurements use this shape), inputs resident in HBM:
   MXFP4 forward   X, W with the 32-wide random-sign Hadamard (RTN),
                   Y = X W^T on the block-scaled FP4 MFMA (bf16 out)
 
+Each NVFP4 tensor's two quantizations (X and W: RTN along K for the forward,
+SR along the other axis for the backward; dY: SR along both) come from one
+read of the tensor (fp4_quantize_dual); `--separate-passes` runs them as
+separate fp4_quantize calls instead (same outputs).
+
 Printed: one JSON line. `value` = GEMM FLOPs of the step / step time (TFLOP/s).
 `roofline` is for the dominant kernel (the NVFP4 GEMM), timed with HIP events
 on the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded
@@ -36,16 +41,17 @@ PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic_bytes(n_elem: int, src_bytes: int, block: int, amax_pass: bool) -> float:
+def algorithmic_bytes(n_elem: int, src_bytes: int, block: int, amax_pass: bool, outputs: int = 1) -> float:
     """Read the input once per pass, write 0.5 B of codes and 1/B B of scale
-    per element; an NVFP4 pass without a ready amax reads the input once more."""
-    b = n_elem * (src_bytes + 0.5 + 1.0 / block)
+    per element for each output orientation; an NVFP4 pass without a ready
+    amax reads the input once more."""
+    b = n_elem * (src_bytes + outputs * (0.5 + 1.0 / block))
     if amax_pass:
         b += n_elem * src_bytes
     return b
 
 
-def make_step(fp4, X, W, dY, signs):
+def make_step(fp4, X, W, dY, signs, separate=False):
     import torch
 
     outs = {
@@ -69,6 +75,31 @@ def make_step(fp4, X, W, dY, signs):
     COLS, ROWS, RTN, SR = fp4.FP4_AXIS_COLS, fp4.FP4_AXIS_ROWS, fp4.FP4_RTN, fp4.FP4_SR
     seed = lambda role: (2 << 8) | role
 
+    mx_ops = [
+        ("quant X mx had", "q", lambda: fp4.fp4_quantize(X, COLS, RTN, 0, 0, False, q["mX"]),
+         algorithmic_bytes(TOKENS * D_IN, 2, 32, False)),
+        ("quant W mx had", "q", lambda: fp4.fp4_quantize(W, COLS, RTN, 0, 0, False, q["mW"]),
+         algorithmic_bytes(D_OUT * D_IN, 2, 32, False)),
+        ("gemm fwd mx", "g_mx", lambda: fp4.fp4_gemm(q["mX"], q["mW"], outs["Ymx"]), GEMM_FLOP),
+    ]
+    if not separate:
+        dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
+        ops = [
+            ("quant X nv dual (rtn K, sr tokens)", "q",
+             lambda: dual(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
+             algorithmic_bytes(TOKENS * D_IN, 2, 16, True, 2)),
+            ("quant W nv dual (rtn K, sr out)", "q",
+             lambda: dual(W, RTN, 0, SR, seed(4), q["W"], q["Wt"]),
+             algorithmic_bytes(D_OUT * D_IN, 2, 16, True, 2)),
+            ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"]), GEMM_FLOP),
+            ("quant dY nv dual (sr both)", "q",
+             lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
+             algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
+            ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"]), GEMM_FLOP),
+            ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), GEMM_FLOP),
+        ] + mx_ops
+        return ops, outs, q
+
     # (name, kind, callable, algorithmic units)
     ops = [
         ("quant X nv rtn", "q", lambda: fp4.fp4_quantize(X, COLS, RTN, 0, 0, False, q["X"]),
@@ -86,12 +117,7 @@ def make_step(fp4, X, W, dY, signs):
         ("quant X^T nv sr", "q", lambda: fp4.fp4_quantize(X, ROWS, SR, seed(3), 0, True, q["Xt"]),
          algorithmic_bytes(TOKENS * D_IN, 2, 16, False)),
         ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), GEMM_FLOP),
-        ("quant X mx had", "q", lambda: fp4.fp4_quantize(X, COLS, RTN, 0, 0, False, q["mX"]),
-         algorithmic_bytes(TOKENS * D_IN, 2, 32, False)),
-        ("quant W mx had", "q", lambda: fp4.fp4_quantize(W, COLS, RTN, 0, 0, False, q["mW"]),
-         algorithmic_bytes(D_OUT * D_IN, 2, 32, False)),
-        ("gemm fwd mx", "g_mx", lambda: fp4.fp4_gemm(q["mX"], q["mW"], outs["Ymx"]), GEMM_FLOP),
-    ]
+    ] + mx_ops
     return ops, outs, q
 
 
@@ -166,6 +192,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-passes", action="store_true",
+                    help="quantize each orientation with its own pass instead of one read per tensor")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the FP4 quantize + GEMM path is built and timed on a "
@@ -185,7 +213,7 @@ def main():
     W = workloads.device_tensor("llama7b", "W")
     dY = workloads.device_tensor("llama7b", "dY")
     signs = fp4.fp4_hadamard_signs(3)
-    ops, outs, q = make_step(fp4, X, W, dY, signs)
+    ops, outs, q = make_step(fp4, X, W, dY, signs, separate=args.separate_passes)
     torch.cuda.synchronize()
 
     def step(events=None):
@@ -263,7 +291,8 @@ def main():
             "workload": ("Llama-7B-shaped linear layer step: NVFP4 fwd + bwd (RTN fwd, SR bwd, "
                          "transposed quantization) and MXFP4+Hadamard fwd"),
             "tokens": TOKENS, "in_features": D_IN, "out_features": D_OUT,
-            "gemms_per_step": 4, "quant_passes_per_step": 8,
+            "gemms_per_step": 4, "quantizations_per_step": 8,
+            "quantize_launches": "separate" if args.separate_passes else "one read per NVFP4 tensor",
         },
         "quantize_GBps_aggregate": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "per_op": per_op,

@@ -22,7 +22,7 @@ FP4_AXIS_COLS, FP4_AXIS_ROWS = 0, 1
 BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
-           "fp4_tensor_amax", "fp4_quantize", "fp4_dequantize", "fp4_gemm"]
+           "fp4_tensor_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_gemm"]
 
 
 class Fp4Error(RuntimeError):
@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.fp4_quantize.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64, c.c_int,
                                    c.c_int, c.c_uint64, c.c_uint64, c.c_int,
                                    c.POINTER(fp4_tensor), c.c_void_p]
+        L.fp4_quantize_dual.restype = c.c_int
+        L.fp4_quantize_dual.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
+                                        c.c_int, c.c_uint64, c.c_uint64, c.c_int, c.c_uint64, c.c_uint64,
+                                        c.c_int, c.POINTER(fp4_tensor), c.POINTER(fp4_tensor), c.c_void_p]
         L.fp4_dequantize.restype = c.c_int
         L.fp4_dequantize.argtypes = [c.POINTER(fp4_tensor), c.c_int, c.c_void_p, c.c_int64,
                                      c.c_void_p]
@@ -164,6 +168,21 @@ def fp4_quantize(src, axis: int, rnd: int, seed: int, index_offset: int, amax_re
     out.rows, out.cols = d.rows, d.cols
 
 
+def fp4_quantize_dual(src, rnd_cols: int, seed_cols: int, index_offset_cols: int, rnd_rows: int,
+                      seed_rows: int, index_offset_rows: int, amax_ready: bool, out_cols: QTensor,
+                      out_rows: QTensor, stream=None) -> None:
+    R, C = src.shape
+    if src.stride(1) != 1:
+        raise ValueError("src must be row-major with unit column stride")
+    dc, dr = out_cols.desc(), out_rows.desc()
+    _check(lib().fp4_quantize_dual(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), rnd_cols,
+                                   seed_cols, index_offset_cols, rnd_rows, seed_rows, index_offset_rows,
+                                   int(bool(amax_ready)), ctypes.byref(dc), ctypes.byref(dr),
+                                   _stream(stream)), "fp4_quantize_dual")
+    out_cols.rows, out_cols.cols = dc.rows, dc.cols
+    out_rows.rows, out_rows.cols = dr.rows, dr.cols
+
+
 def fp4_dequantize(q: QTensor, dst, stream=None) -> None:
     d = q.desc()
     _check(lib().fp4_dequantize(ctypes.byref(d), _dtype_code(dst), dst.data_ptr(), dst.stride(0),
@@ -191,6 +210,27 @@ def quantize(src, axis: int = FP4_AXIS_COLS, fmt: int = FP4_NVFP4, rnd: int = FP
         ready = True
     fp4_quantize(src, axis, rnd, seed, index_offset, ready, q, stream)
     return q
+
+
+def quantize_dual(src, fmt: int = FP4_NVFP4, rnd_cols: int = FP4_RTN, seed_cols: int = 0,
+                  index_offset_cols: int = 0, rnd_rows: int = FP4_SR, seed_rows: int = 0,
+                  index_offset_rows: int = 0, had_signs_cols: int | None = None,
+                  had_signs_rows: int | None = None, amax_from: QTensor | None = None, stream=None):
+    """Allocate both QTensors and quantize src along C and along R in one
+    read. Returns (q_cols [R, C], q_rows [C, R]); they share the tensor amax
+    (NVFP4)."""
+    R, C = src.shape
+    qc = QTensor(R, C, fmt, device=src.device, had_signs=had_signs_cols)
+    qr = QTensor(C, R, fmt, device=src.device, had_signs=had_signs_rows)
+    ready = False
+    if amax_from is not None and fmt == FP4_NVFP4:
+        qc.amax = amax_from.amax
+        ready = True
+    if fmt == FP4_NVFP4:
+        qr.amax = qc.amax
+    fp4_quantize_dual(src, rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
+                      index_offset_rows, ready, qc, qr, stream)
+    return qc, qr
 
 
 def dequantize(q: QTensor, dtype=None, stream=None):

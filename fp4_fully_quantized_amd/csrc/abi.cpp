@@ -137,6 +137,69 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
   return hip_status();
 }
 
+fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                             fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
+                             fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
+                             int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
+                             fp4_stream_t stream) {
+  if (!out_cols || !out_rows) return FP4_ERR_NULL;
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if ((rnd_cols != FP4_RTN && rnd_cols != FP4_SR) || (rnd_rows != FP4_RTN && rnd_rows != FP4_SR))
+    return FP4_ERR_ARG;
+  if (!valid_fmt(out_cols->fmt) || !valid_fmt(out_rows->fmt)) return FP4_ERR_ARG;
+  if (out_cols->fmt != out_rows->fmt) return FP4_ERR_UNSUPPORTED;
+  if ((out_cols->had_on != 0) != (out_rows->had_on != 0)) return FP4_ERR_UNSUPPORTED;
+  for (const fp4_tensor* o : {out_cols, out_rows}) {
+    if (!o->codes || !o->scales) return FP4_ERR_NULL;
+    if (!aligned16(o->codes) || !aligned16(o->scales)) return FP4_ERR_ALIGN;
+  }
+  const bool nv = out_cols->fmt == FP4_NVFP4;
+  if (nv && (!out_cols->amax || !out_cols->tscale || !out_rows->tscale)) return FP4_ERR_NULL;
+  if (out_cols->had_on && nv) return FP4_ERR_UNSUPPORTED;
+  const int B = block_of(out_cols->fmt);
+  if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
+  if ((rnd_cols == FP4_SR && index_offset_cols % 8 != 0) || (rnd_rows == FP4_SR && index_offset_rows % 8 != 0))
+    return FP4_ERR_ALIGN;
+  if ((R + 127) / 128 * ((C + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nv && !amax_ready) {
+    fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out_cols->amax, s);
+    st = hip_status();
+    if (st != FP4_OK) return st;
+  }
+  DualArgs a;
+  a.src = src;
+  a.bf16 = src_t == FP4_DTYPE_BF16;
+  a.R = R;
+  a.C = C;
+  a.ld = ld;
+  a.fmt = out_cols->fmt;
+  a.had_on = out_cols->had_on != 0;
+  a.sr_c = rnd_cols == FP4_SR;
+  a.sr_r = rnd_rows == FP4_SR;
+  a.seed_c = seed_cols;
+  a.offset_c = index_offset_cols;
+  a.seed_r = seed_rows;
+  a.offset_r = index_offset_rows;
+  a.signs_c = out_cols->had_signs;
+  a.signs_r = out_rows->had_signs;
+  a.codes_c = out_cols->codes;
+  a.scales_c = out_cols->scales;
+  a.codes_r = out_rows->codes;
+  a.scales_r = out_rows->scales;
+  a.amax = out_cols->amax;
+  a.tscale_c = out_cols->tscale;
+  a.tscale_r = out_rows->tscale;
+  a.amax_r = (nv && out_rows->amax && out_rows->amax != out_cols->amax) ? out_rows->amax : nullptr;
+  fp4i_launch_quant_dual(a, s);
+  out_cols->rows = R;
+  out_cols->cols = C;
+  out_rows->rows = C;
+  out_rows->cols = R;
+  return hip_status();
+}
+
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
                           fp4_stream_t stream) {
   if (!q || !dst) return FP4_ERR_NULL;

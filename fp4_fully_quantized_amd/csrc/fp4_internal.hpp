@@ -20,6 +20,23 @@ struct QuantArgs {
   float* tscale;         // NVFP4: receives s_g
 };
 
+// Both orientations of one source (fp4_quantize_dual): *_c blocks along C,
+// *_r blocks along R (transposed output).
+struct DualArgs {
+  const void* src;
+  bool bf16;
+  int64_t R, C, ld;
+  int fmt;
+  bool had_on;
+  bool sr_c, sr_r;
+  uint64_t seed_c, offset_c, seed_r, offset_r;
+  uint32_t signs_c, signs_r;
+  uint8_t *codes_c, *scales_c, *codes_r, *scales_r;
+  const float* amax;               // NVFP4: the tensor amax (already computed)
+  float *tscale_c, *tscale_r;      // NVFP4: receive s_g
+  float* amax_r;                   // NVFP4: receives a copy of the amax, or null
+};
+
 struct GemmArgs {
   const uint8_t* a_codes;
   const uint8_t* a_scales;
@@ -37,6 +54,7 @@ struct GemmArgs {
 void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
                       hipStream_t s);
 void fp4i_launch_quant(const QuantArgs& a, hipStream_t s);
+void fp4i_launch_quant_dual(const DualArgs& a, hipStream_t s);
 void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);

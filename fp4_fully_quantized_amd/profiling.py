@@ -97,6 +97,7 @@ PROFILE_COMMANDS = {
 GROUPS = [
     ("NVFP4 GEMM (fwd bf16 out; dgrad, wgrad fp32 out)", r"^k_gemm<0,"),
     ("MXFP4 GEMM (fwd, bf16 out)", r"^k_gemm<1,"),
+    ("quantize, both orientations from one read", r"^k_quant_dual<"),
     ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
     ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
     ("tensor amax", r"^k_amax<"),
@@ -140,8 +141,9 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
         "",
         "```", cmd("stats"), "```",
         "",
-        "One step = NVFP4 fwd (quantize X, W; GEMM bf16 out), NVFP4 bwd (SR quantize dY, W^T, dY^T, X^T; "
-        "dgrad and wgrad GEMMs fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). 7 steps traced "
+        "One step = NVFP4 quantization of X, W and dY, each tensor read once for both of its orientations "
+        "(X, W: RTN along K + SR along the other axis; dY: SR along both), the fwd GEMM (bf16 out), dgrad and "
+        "wgrad GEMMs (fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). 7 steps traced "
         "(2 warm-up + 5 timed); torch kernels are the one-time input generation.",
         "",
         "`k_gemm<0, 256, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *>` = MXFP4 GEMM (scaled FP4 MFMA); "

@@ -141,6 +141,28 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream);
 
+/* Both orientations of one R x C source from a single read of it (the
+ * "read once, emit both" fusion of the two quantizations that a linear layer's
+ * backward pass needs for dY and X; FP4 All the Way, Key points: every GEMM
+ * operand blocked along its contraction dimension). Equivalent, bit for bit,
+ * to
+ *   fp4_quantize(src, ..., FP4_AXIS_COLS, rnd_cols, seed_cols, index_offset_cols, ..., out_cols)
+ *   fp4_quantize(src, ..., FP4_AXIS_ROWS, rnd_rows, seed_rows, index_offset_rows, ..., out_rows)
+ * with both calls using the same tensor amax.
+ *   out_cols     blocks along C: out_cols is R x C.
+ *   out_rows     blocks along R: out_rows is C x R (the transpose).
+ *   amax_ready   NVFP4: 1 if *out_cols->amax already holds this tensor's amax;
+ *                0 to compute it first. *out_rows->amax, when it is another
+ *                scalar, receives a copy; both tscale scalars receive s_g.
+ * The two descriptors must have the same fmt and had_on (MXFP4: each keeps
+ * its own had_signs). Requires: R, C >= 1, both multiples of B; C % 8 == 0;
+ * ld >= C and ld % 8 == 0; src 16-byte aligned. Errors as fp4_quantize. */
+fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                             fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
+                             fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
+                             int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
+                             fp4_stream_t stream);
+
 /* Dequantize q to dst (device, q->rows x q->cols row-major, leading dimension
  * ld >= cols, FP32 or bf16):
  *   NVFP4: (e2m1 * sdec) * s_g, the last product rounded once to FP32;

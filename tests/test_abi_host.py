@@ -110,6 +110,38 @@ def test_quantize_rejects_null_descriptor(fp4):
     assert fp4.lib().fp4_quantize(0x1000, 1, 64, 128, 128, 0, 0, 0, 0, 1, None, None) == 1
 
 
+DUAL_BAD = [
+    # (src, dtype, R, C, ld, rnd_c, off_c, rnd_r, off_r, cols overrides, rows overrides, expected)
+    (0, 1, 64, 128, 128, 0, 0, 1, 0, {}, {}, 1),
+    (0x1000, 1, 40, 128, 128, 0, 0, 1, 0, {}, {}, 2),          # R not a multiple of 16
+    (0x1000, 1, 64, 120, 128, 0, 0, 1, 0, {}, {}, 2),          # C not a multiple of 16
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"fmt": 1}, {}, 4),  # formats differ
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"fmt": 1, "had_on": 1}, {"fmt": 1}, 4),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"had_on": 1}, 4),  # Hadamard with NVFP4
+    (0x1000, 1, 64, 128, 128, 1, 4, 1, 0, {}, {}, 3),          # SR offset % 8 (cols)
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 12, {}, {}, 3),         # SR offset % 8 (rows)
+    (0x1000, 1, 64, 128, 128, 2, 0, 1, 0, {}, {}, 5),          # bad rounding
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {}, {"codes": 0}, 1),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {}, {"tscale": 0}, 1),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"scales": 0x20004}, {}, 3),
+]
+
+
+@pytest.mark.parametrize("case", DUAL_BAD)
+def test_quantize_dual_rejects_bad_arguments(fp4, case):
+    src, dt, R, C, ld, rc, oc, rr, orr, over_c, over_r, want = case
+    dc, dr = _t(fp4, **over_c), _t(fp4, **over_r)
+    st = fp4.lib().fp4_quantize_dual(src, dt, R, C, ld, rc, 0, oc, rr, 0, orr, 1, ctypes.byref(dc),
+                                     ctypes.byref(dr), None)
+    assert st == want
+
+
+def test_quantize_dual_rejects_null_descriptors(fp4):
+    d = _t(fp4)
+    assert fp4.lib().fp4_quantize_dual(0x1000, 1, 64, 128, 128, 0, 0, 0, 1, 0, 0, 1, None,
+                                       ctypes.byref(d), None) == 1
+
+
 GEMM_BAD = [
     ({}, {"fmt": 1}, 1, 128, 4),                      # mixed formats
     ({"fmt": 1, "had_on": 1, "had_signs": 5}, {"fmt": 1, "had_on": 1, "had_signs": 6}, 1, 128, 4),

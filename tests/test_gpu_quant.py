@@ -99,6 +99,49 @@ def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
         assert np.array_equal(to_host(y), want)
 
 
+# ------------------------------------------------ both orientations in one read
+DUAL = []
+for fmt in (0, 1):
+    for rc, rr in ((0, 1), (1, 1), (0, 0), (1, 0)):
+        for had in ((False, True) if fmt == 1 else (False,)):
+            DUAL.append((fmt, rc, rr, had))
+
+
+@pytest.mark.parametrize("fmt,rc,rr,had", DUAL)
+@pytest.mark.parametrize("shape,bf16", [((96, 1056), True), ((256, 256), True), ((160, 96), False),
+                                        ((32, 64), True), ((384, 4128), True)])
+def test_quantize_dual_matches_two_oracle_passes(fp4, orc, fmt, rc, rr, had, shape, bf16):
+    B = 16 if fmt == 0 else 32
+    if shape[0] % B or shape[1] % B:
+        pytest.skip("the dual pass needs both dimensions blocked")
+    say("quantize_dual", shape, "fmt", fmt, "rnd", rc, rr, "had", had, "bf16", bf16)
+    xh = _mixed(shape, 31 + shape[1], bf16)
+    sc = orc.hadamard_signs(5) if had else 0
+    sr = orc.hadamard_signs(6) if had else 0
+    want_c = orc.quantize(xh, axis=0, fmt=fmt, rnd=rc, seed=21, index_offset=8, had_on=had, had_signs=sc)
+    want_r = orc.quantize(xh, axis=1, fmt=fmt, rnd=rr, seed=22, index_offset=16, had_on=had, had_signs=sr)
+    qc, qr = fp4.quantize_dual(to_device(xh), fmt=fmt, rnd_cols=rc, seed_cols=21, index_offset_cols=8,
+                               rnd_rows=rr, seed_rows=22, index_offset_rows=16,
+                               had_signs_cols=sc if had else None, had_signs_rows=sr if had else None)
+    assert_same_quant(q_to_host(qc), want_c, "dual, blocks along C")
+    assert_same_quant(q_to_host(qr), want_r, "dual, blocks along R")
+
+
+def test_quantize_dual_full_size_gradient(fp4, orc):
+    """The Llama-7B layer's dY (32768 x 11008 bf16), SR in both orientations."""
+    import torch
+    from fp4_fully_quantized_amd import workloads
+    say("quantize_dual full size dY")
+    x = workloads.device_tensor("llama7b", "dY")
+    qc, qr = fp4.quantize_dual(x, rnd_cols=1, seed_cols=(2 << 8) | 1, rnd_rows=1, seed_rows=(2 << 8) | 2)
+    torch.cuda.synchronize()
+    got_c, got_r = q_to_host(qc), q_to_host(qr)
+    xh = to_host(x)
+    del qc, qr, x
+    assert_same_quant(got_c, orc.quantize(xh, axis=0, rnd=1, seed=(2 << 8) | 1), "dY, blocks along C")
+    assert_same_quant(got_r, orc.quantize(xh, axis=1, rnd=1, seed=(2 << 8) | 2), "dY, blocks along R")
+
+
 # ------------------------------------------------------- SR decision boundaries
 def _sr_boundary_input(orc, R, C, axis, seed, offset):
     """fp32 [R, C] whose MXFP4 block exponents are all 0 (element 0 of every
