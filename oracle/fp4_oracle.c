@@ -237,6 +237,28 @@ void o_fwht32(float x[32], uint32_t signs)
     for (int j = 0; j < 32; ++j) x[j] = x[j] * c;
 }
 
+/* The random Hadamard transform for NVFP4 (Robots Atlas "FP4", How it       */
+/* works: random Hadamard transforms are one of the stabilizers of FP4       */
+/* training, not tied to one format). Reading: like the MXFP4 rotation, it   */
+/* spans exactly one scale block, so here 16 elements:                       */
+/* y = (1/4) * H16 * (D x), D from bits 0..15 of the mask, butterfly stages  */
+/* h = 1, 2, 4, 8 in FP32. The normalisation 16^-1/2 = 1/4 is exact.         */
+void o_fwht16(float x[16], uint32_t signs)
+{
+    for (int j = 0; j < 16; ++j)
+        if ((signs >> j) & 1u) x[j] = -x[j];
+    for (int h = 1; h < 16; h <<= 1) {
+        for (int i = 0; i < 16; ++i) {
+            if ((i & h) == 0) {
+                float a = x[i], b = x[i + h];
+                x[i] = a + b;
+                x[i + h] = a - b;
+            }
+        }
+    }
+    for (int j = 0; j < 16; ++j) x[j] = x[j] * 0.25f;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tensors.                                                                  */
 /* ------------------------------------------------------------------------ */
@@ -274,7 +296,6 @@ int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
 {
     if (!src || !codes || !scales || R <= 0 || C <= 0 || ld < C) return -1;
     if (fmt != O_FMT_NVFP4 && fmt != O_FMT_MXFP4) return -1;
-    if (had_on && fmt != O_FMT_MXFP4) return -1;
     const int B = (fmt == O_FMT_NVFP4) ? 16 : 32;
     const int64_t rows_q = (axis == O_AXIS_ROWS) ? C : R;
     const int64_t cols_q = (axis == O_AXIS_ROWS) ? R : C;
@@ -300,6 +321,22 @@ int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
         return -2;
     }
 
+    /* The rotation (when on) acts on every block along the blocked axis before
+     * anything else: the tensor amax of NVFP4 is that of the rotated tensor,
+     * the values the scales have to cover. */
+    const int64_t nblk = cols_q / B;
+    if (had_on) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows_q; ++r)
+            for (int64_t b = 0; b < nblk; ++b) {
+                float* blk = t + r * cols_q + b * B;
+                if (B == 16)
+                    o_fwht16(blk, had_signs);
+                else
+                    o_fwht32(blk, had_signs);
+            }
+    }
+
     float sg = 1.0f;
     if (fmt == O_FMT_NVFP4) {
         float amax = amax_given ? amax_in : o_tensor_amax(t, 0, rows_q, cols_q, cols_q);
@@ -308,13 +345,11 @@ int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
         if (sg_out) *sg_out = sg;
     }
 
-    const int64_t nblk = cols_q / B;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows_q; ++r) {
         for (int64_t b = 0; b < nblk; ++b) {
             float x[32];
             for (int j = 0; j < B; ++j) x[j] = t[r * cols_q + b * B + j];
-            if (had_on) o_fwht32(x, had_signs);
 
             float amax_b = 0.0f;
             for (int j = 0; j < B; ++j)

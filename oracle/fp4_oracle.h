@@ -53,12 +53,16 @@ uint32_t o_hadamard_signs(uint64_t seed);
 
 /* ---- rotation ---- */
 void     o_fwht32(float x[32], uint32_t signs);        /* signs, Sylvester FWHT, times 2^-2.5 */
+void     o_fwht16(float x[16], uint32_t signs);        /* bits 0..15, Sylvester FWHT, times 1/4 */
 
 /* ---- tensors ---- */
 /* max |x| over an R x C matrix with leading dimension ld (elements). */
 float    o_tensor_amax(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld);
 
 /* Quantize an R x C matrix (row-major, leading dimension ld, fp32 or bf16 bits).
+ * had_on: every block along the blocked axis is rotated first (MXFP4: 32-wide,
+ * o_fwht32; NVFP4: 16-wide, o_fwht16); the NVFP4 tensor amax is then that of
+ * the rotated tensor.
  * In the quantized orientation (rows_q x cols_q; [R][C] for COLS, [C][R] for ROWS):
  *   codes  : rows_q * cols_q / 2 bytes, element 2t in the low nibble of byte t
  *   scales : rows_q * cols_q / B bytes (B = 16 NVFP4, 32 MXFP4)

@@ -68,6 +68,8 @@ def lib():
         L.o_hadamard_signs.argtypes = [c.c_uint64]
         L.o_fwht32.restype = None
         L.o_fwht32.argtypes = [c.POINTER(c.c_float), c.c_uint32]
+        L.o_fwht16.restype = None
+        L.o_fwht16.argtypes = [c.POINTER(c.c_float), c.c_uint32]
         L.o_tensor_amax.restype = c.c_float
         L.o_tensor_amax.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64]
         L.o_quantize.restype = c.c_int
@@ -140,6 +142,13 @@ def fwht32(x, signs: int) -> np.ndarray:
     buf = np.ascontiguousarray(np.asarray(x, dtype=np.float32).copy())
     assert buf.shape == (32,)
     lib().o_fwht32(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), signs)
+    return buf
+
+
+def fwht16(x, signs: int) -> np.ndarray:
+    buf = np.ascontiguousarray(np.asarray(x, dtype=np.float32).copy())
+    assert buf.shape == (16,)
+    lib().o_fwht16(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), signs)
     return buf
 
 

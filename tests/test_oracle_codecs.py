@@ -286,6 +286,38 @@ def test_fwht_orthonormal_and_invertible(orc):
         assert np.max(np.abs(back - x)) <= 1e-5 * np.linalg.norm(x)
 
 
+def test_fwht16_is_sylvester_hadamard(orc):
+    from scipy.linalg import hadamard
+    H = hadamard(16)
+    assert np.array_equal(H @ H.T, 16 * np.eye(16, dtype=H.dtype))
+    rng = np.random.default_rng(4)
+    for trial in range(200):
+        signs = int(rng.integers(0, 2 ** 32))
+        x = rng.integers(-(2 ** 19), 2 ** 19, 16).astype(np.int64)
+        D = np.array([-1 if (signs >> j) & 1 else 1 for j in range(16)], dtype=np.int64)
+        exact = H @ (D * x)                        # integer, |.| < 2^23: exact in fp32
+        expect = exact.astype(np.float32) * np.float32(0.25)   # exact
+        got = orc.fwht16(x.astype(np.float32), signs)
+        assert np.array_equal(got, expect), trial
+        # only bits 0..15 of the mask act
+        assert np.array_equal(orc.fwht16(x.astype(np.float32), signs & 0xFFFF), got)
+
+
+def test_fwht16_inverse_is_exact(orc):
+    # (1/4) H16 is its own inverse; with integer x every step is exact, so
+    # undoing the rotation (H16 / 4, then the signs) gives x back bit for bit.
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        signs = int(rng.integers(0, 2 ** 16))
+        x = rng.integers(-(2 ** 12), 2 ** 12, 16).astype(np.float32)
+        y = orc.fwht16(x, signs)
+        back = orc.fwht16(y, 0)
+        D = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(16)], dtype=np.float32)
+        assert np.array_equal(back * D, x)
+        assert np.isclose(np.linalg.norm(y.astype(np.float64)), np.linalg.norm(x.astype(np.float64)),
+                          rtol=1e-12)
+
+
 def test_hadamard_mask_is_a_separate_philox_counter(orc):
     # word 0 of counter (0,0,0,1), which the element stream (c2 = c3 = 0) never uses
     for seed in (0, 1, 3, 2 ** 40 + 5):

@@ -54,6 +54,49 @@ def test_mxfp4_hadamard_worked_example(orc):
     assert list(unpack(q["codes"])[0]) == list(c)
 
 
+def test_nvfp4_hadamard_worked_example(orc):
+    f, x, c = load_worked("nvfp4_hadamard_worked.txt", 2, 16)
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4, had_on=True, had_signs=int(f["mask"][0], 16))
+    assert q["amax"] == float(f["amax"][0])
+    assert q["sg"] == float(np.float32(2.0) / np.float32(2688.0))
+    assert list(q["scales"][0]) == [int(v, 16) for v in f["scales"]]
+    assert list(unpack(q["codes"])[0]) == list(c)
+
+
+def _rotate_blocks(x, B, signs):
+    """(H_B D) applied to every B-block of each row, exactly, in integers."""
+    from scipy.linalg import hadamard
+    H = hadamard(B).astype(np.int64)
+    D = np.array([-1 if (signs >> j) & 1 else 1 for j in range(B)], dtype=np.int64)
+    R, C = x.shape
+    blocks = x.astype(np.int64).reshape(R, C // B, B) * D
+    return (blocks @ H.T).reshape(R, C)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_nvfp4_hadamard_is_quantization_of_the_rotated_tensor(orc, axis, rnd):
+    # Integer inputs with |H x| < 2^24: the rotation is exact in FP32, so the
+    # rotated tensor is known without the oracle's butterfly; quantizing it
+    # without rotation must give the same codes, scales and tensor scale.
+    rng = np.random.default_rng(21)
+    x = rng.integers(-1000, 1001, (48, 96)).astype(np.int64)
+    x[5, 7] = 40000                                 # an outlier the rotation spreads
+    signs = 0xA5C3F00F
+    if axis == orc.AXIS_COLS:
+        y = _rotate_blocks(x, 16, signs)
+    else:
+        y = _rotate_blocks(x.T, 16, signs).T
+    yf = (y.astype(np.float64) * 0.25).astype(np.float32)
+    assert np.array_equal(yf.astype(np.float64), y * 0.25)
+    a = orc.quantize(x.astype(np.float32), axis=axis, fmt=orc.FMT_NVFP4, rnd=rnd, seed=3,
+                     had_on=True, had_signs=signs)
+    b = orc.quantize(np.ascontiguousarray(yf), axis=axis, fmt=orc.FMT_NVFP4, rnd=rnd, seed=3)
+    assert a["amax"] == float(np.abs(yf).max()) != float(np.abs(x).max())
+    assert a["sg"] == b["sg"]
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
 def _randn(shape, seed, outliers=False):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal(shape).astype(np.float32)
@@ -120,7 +163,7 @@ def test_power_of_two_scale_invariance(orc, fmt, k):
         assert np.array_equal(q0["scales"].astype(int) + k, q1["scales"].astype(int))
 
 
-@pytest.mark.parametrize("fmt,rnd,had", [(0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 1)])
+@pytest.mark.parametrize("fmt,rnd,had", [(0, 0, 0), (0, 1, 0), (0, 0, 1), (0, 1, 1), (1, 0, 0), (1, 1, 1)])
 def test_rows_axis_equals_cols_axis_of_the_transpose(orc, fmt, rnd, had):
     x = _randn((96, 64), 4)
     a = orc.quantize(x, axis=orc.AXIS_ROWS, fmt=fmt, rnd=rnd, seed=9, had_on=had,
