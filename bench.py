@@ -121,6 +121,71 @@ def make_step(fp4, X, W, dY, signs, separate=False):
     return ops, outs, q
 
 
+def make_extras(fp4, X, dY, signs16):
+    """Adjacent passes timed beside the step (not part of it): the NVFP4
+    quantizations of the wgrad operands with the 16-wide random-sign Hadamard
+    along the tokens. With a rotation on one orientation the two orientations
+    have their own tensor amax (the plain one and the rotated one), both taken
+    in one read of the tensor before the dual pass."""
+    Q = fp4.QTensor
+    NV = fp4.FP4_NVFP4
+    COLS, ROWS, RTN, SR = fp4.FP4_AXIS_COLS, fp4.FP4_AXIS_ROWS, fp4.FP4_RTN, fp4.FP4_SR
+    seed = lambda role: (2 << 8) | role
+    q = {
+        "X": Q(TOKENS, D_IN, NV), "Xt": Q(D_IN, TOKENS, NV, had_signs=signs16),
+        "dY": Q(TOKENS, D_OUT, NV), "dYt": Q(D_OUT, TOKENS, NV, had_signs=signs16),
+    }
+    dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
+    ops = [
+        ("amax dY had16 tokens", "q", lambda: fp4.fp4_tensor_amax_hadamard16(dY, ROWS, signs16, q["dYt"].amax),
+         TOKENS * D_OUT * 2.0),
+        ("quant X nv dual (rtn K, sr+had16 tokens)", "q",
+         lambda: dual(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
+         algorithmic_bytes(TOKENS * D_IN, 2, 16, True, 2)),
+        ("quant dY nv dual (sr K, sr+had16 tokens)", "q",
+         lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
+         algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
+    ]
+    return ops, q
+
+
+def time_ops(ops, steps, warmup):
+    """Per-op records (HIP events around each call on the current stream)."""
+    import torch
+
+    for _ in range(warmup):
+        for _, _, fn, _ in ops:
+            fn()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for i, (_, _, fn, _) in enumerate(ops):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    return [op_record(name, kind, units, [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)])
+            for i, (name, kind, _, units) in enumerate(ops)]
+
+
+def op_record(name, kind, units, times_ms):
+    ms = sorted(times_ms)
+    avg = sum(ms) / len(ms)
+    rec = {"op": name, "avg_ms": round(avg, 4), "median_ms": round(ms[len(ms) // 2], 4)}
+    if kind == "q":
+        rec["GBps"] = round(units / (avg * 1e-3) / 1e9, 1)
+        rec["frac_hbm"] = round(rec["GBps"] / PEAK_HBM_GBS, 3)
+    else:
+        tf = units / (avg * 1e-3) / 1e12
+        rec["TFLOPs"] = round(tf, 1)
+        rec["frac_f16_peak" if kind == "g_nv" else "frac_fp4_peak"] = round(
+            tf / (PEAK_F16_TFLOPS if kind == "g_nv" else PEAK_FP4_TFLOPS), 3)
+        if kind == "g_nv":
+            rec["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 3)
+    return rec
+
+
 def cpu_baseline():
     """The oracle on a bounded sample of the step: every quantization pass on a
     row slab of its tensor and every GEMM reference on a few output rows, each
@@ -238,22 +303,13 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    per_op = []
-    for i, (name, kind, _, units) in enumerate(ops):
-        ms = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
-        avg = sum(ms) / len(ms)
-        rec = {"op": name, "avg_ms": round(avg, 4), "median_ms": round(ms[len(ms) // 2], 4)}
-        if kind == "q":
-            rec["GBps"] = round(units / (avg * 1e-3) / 1e9, 1)
-            rec["frac_hbm"] = round(rec["GBps"] / PEAK_HBM_GBS, 3)
-        else:
-            tf = units / (avg * 1e-3) / 1e12
-            rec["TFLOPs"] = round(tf, 1)
-            rec["frac_f16_peak" if kind == "g_nv" else "frac_fp4_peak"] = round(
-                tf / (PEAK_F16_TFLOPS if kind == "g_nv" else PEAK_FP4_TFLOPS), 3)
-            if kind == "g_nv":
-                rec["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 3)
-        per_op.append(rec)
+    per_op = [op_record(name, kind, units, [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
+              for i, (name, kind, _, units) in enumerate(ops)]
+
+    # Adjacent passes, timed after the step's timed region.
+    extra_ops, extra_q = make_extras(fp4, X, dY, fp4.fp4_hadamard_signs(4))
+    extras = time_ops(extra_ops, args.steps, 2)
+    del extra_ops, extra_q
 
     nv = [r for r, o in zip(per_op, ops) if o[1] == "g_nv"]
     nv_avg_ms = sum(r["avg_ms"] for r in nv) / len(nv)
@@ -296,6 +352,7 @@ def main():
         },
         "quantize_GBps_aggregate": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "per_op": per_op,
+        "extras": extras,
         "roofline": {
             "kernel": "NVFP4 GEMM (e2m1*E4M3 decoded exactly to f16, f16 MFMA)",
             "bound": "mfma",

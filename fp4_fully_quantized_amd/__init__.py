@@ -22,7 +22,8 @@ FP4_AXIS_COLS, FP4_AXIS_ROWS = 0, 1
 BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
-           "fp4_tensor_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_gemm"]
+           "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
+           "fp4_dequantize", "fp4_gemm"]
 
 
 class Fp4Error(RuntimeError):
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.fp4_tensor_amax.restype = c.c_int
         L.fp4_tensor_amax.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
                                       c.c_void_p, c.c_void_p]
+        L.fp4_tensor_amax_hadamard16.restype = c.c_int
+        L.fp4_tensor_amax_hadamard16.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
+                                                 c.c_int, c.c_uint32, c.c_void_p, c.c_void_p]
         L.fp4_quantize.restype = c.c_int
         L.fp4_quantize.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64, c.c_int,
                                    c.c_int, c.c_uint64, c.c_uint64, c.c_int,
@@ -156,6 +160,13 @@ def fp4_tensor_amax(src, amax, stream=None) -> None:
                                  amax.data_ptr(), _stream(stream)), "fp4_tensor_amax")
 
 
+def fp4_tensor_amax_hadamard16(src, axis: int, had_signs: int, amax, stream=None) -> None:
+    R, C = src.shape
+    _check(lib().fp4_tensor_amax_hadamard16(src.data_ptr(), _dtype_code(src), R, C, src.stride(0),
+                                            axis, had_signs, amax.data_ptr(), _stream(stream)),
+           "fp4_tensor_amax_hadamard16")
+
+
 def fp4_quantize(src, axis: int, rnd: int, seed: int, index_offset: int, amax_ready: bool,
                  out: QTensor, stream=None) -> None:
     R, C = src.shape
@@ -217,16 +228,22 @@ def quantize_dual(src, fmt: int = FP4_NVFP4, rnd_cols: int = FP4_RTN, seed_cols:
                   index_offset_rows: int = 0, had_signs_cols: int | None = None,
                   had_signs_rows: int | None = None, amax_from: QTensor | None = None, stream=None):
     """Allocate both QTensors and quantize src along C and along R in one
-    read. Returns (q_cols [R, C], q_rows [C, R]); they share the tensor amax
-    (NVFP4)."""
+    read. Returns (q_cols [R, C], q_rows [C, R]). NVFP4 without rotation: they
+    share the tensor amax (`amax_from`: a QTensor whose amax to reuse). NVFP4
+    with a rotation on either side: each keeps its own amax (`amax_from`: a
+    pair of QTensors, for the cols and the rows orientation)."""
     R, C = src.shape
     qc = QTensor(R, C, fmt, device=src.device, had_signs=had_signs_cols)
     qr = QTensor(C, R, fmt, device=src.device, had_signs=had_signs_rows)
     ready = False
+    two = fmt == FP4_NVFP4 and (qc.had_on or qr.had_on)
     if amax_from is not None and fmt == FP4_NVFP4:
-        qc.amax = amax_from.amax
+        if two:
+            qc.amax, qr.amax = amax_from[0].amax, amax_from[1].amax
+        else:
+            qc.amax = amax_from.amax
         ready = True
-    if fmt == FP4_NVFP4:
+    if fmt == FP4_NVFP4 and not two:
         qr.amax = qc.amax
     fp4_quantize_dual(src, rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
                       index_offset_rows, ready, qc, qr, stream)

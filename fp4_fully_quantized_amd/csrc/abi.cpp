@@ -88,6 +88,19 @@ fp4_status fp4_tensor_amax(const void* src, fp4_dtype src_t, int64_t R, int64_t 
   return hip_status();
 }
 
+fp4_status fp4_tensor_amax_hadamard16(const void* src, fp4_dtype src_t, int64_t R, int64_t C,
+                                      int64_t ld, fp4_axis axis, uint32_t had_signs, float* amax,
+                                      fp4_stream_t stream) {
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if (!amax) return FP4_ERR_NULL;
+  if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
+  if ((axis == FP4_AXIS_ROWS ? R : C) % 16 != 0) return FP4_ERR_SHAPE;
+  fp4i_launch_amax_rot16(src, src_t == FP4_DTYPE_BF16, R, C, ld, axis == FP4_AXIS_ROWS, had_signs,
+                         amax, reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
 fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream) {
@@ -101,7 +114,6 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
   if (!aligned16(out->codes) || !aligned16(out->scales)) return FP4_ERR_ALIGN;
   const bool nv = out->fmt == FP4_NVFP4;
   if (nv && (!out->amax || !out->tscale)) return FP4_ERR_NULL;
-  if (out->had_on && nv) return FP4_ERR_UNSUPPORTED;
   const int B = block_of(out->fmt);
   const int64_t blocked = axis == FP4_AXIS_ROWS ? R : C;
   if (blocked % B != 0) return FP4_ERR_SHAPE;
@@ -110,7 +122,11 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
     return FP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (nv && !amax_ready) {
-    fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
+    if (out->had_on)
+      fp4i_launch_amax_rot16(src, src_t == FP4_DTYPE_BF16, R, C, ld, axis == FP4_AXIS_ROWS,
+                             out->had_signs, out->amax, s);
+    else
+      fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
     st = hip_status();
     if (st != FP4_OK) return st;
   }
@@ -149,14 +165,18 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
     return FP4_ERR_ARG;
   if (!valid_fmt(out_cols->fmt) || !valid_fmt(out_rows->fmt)) return FP4_ERR_ARG;
   if (out_cols->fmt != out_rows->fmt) return FP4_ERR_UNSUPPORTED;
-  if ((out_cols->had_on != 0) != (out_rows->had_on != 0)) return FP4_ERR_UNSUPPORTED;
   for (const fp4_tensor* o : {out_cols, out_rows}) {
     if (!o->codes || !o->scales) return FP4_ERR_NULL;
     if (!aligned16(o->codes) || !aligned16(o->scales)) return FP4_ERR_ALIGN;
   }
   const bool nv = out_cols->fmt == FP4_NVFP4;
+  const bool had_c = out_cols->had_on != 0, had_r = out_rows->had_on != 0;
+  // NVFP4 with a rotation: the two orientations' values have different amaxes,
+  // each kept in its own descriptor.
+  const bool two_amax = nv && (had_c || had_r);
   if (nv && (!out_cols->amax || !out_cols->tscale || !out_rows->tscale)) return FP4_ERR_NULL;
-  if (out_cols->had_on && nv) return FP4_ERR_UNSUPPORTED;
+  if (two_amax && !out_rows->amax) return FP4_ERR_NULL;
+  if (two_amax && out_rows->amax == out_cols->amax) return FP4_ERR_UNSUPPORTED;
   const int B = block_of(out_cols->fmt);
   if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
   if ((rnd_cols == FP4_SR && index_offset_cols % 8 != 0) || (rnd_rows == FP4_SR && index_offset_rows % 8 != 0))
@@ -164,7 +184,12 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
   if ((R + 127) / 128 * ((C + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (nv && !amax_ready) {
-    fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out_cols->amax, s);
+    const bool bf = src_t == FP4_DTYPE_BF16;
+    if (two_amax)
+      fp4i_launch_amax_pair(src, bf, R, C, ld, had_c, out_cols->had_signs, had_r, out_rows->had_signs,
+                            out_cols->amax, out_rows->amax, s);
+    else
+      fp4i_launch_amax(src, bf, R, C, ld, out_cols->amax, s);
     st = hip_status();
     if (st != FP4_OK) return st;
   }
@@ -175,7 +200,8 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
   a.C = C;
   a.ld = ld;
   a.fmt = out_cols->fmt;
-  a.had_on = out_cols->had_on != 0;
+  a.had_c = had_c;
+  a.had_r = had_r;
   a.sr_c = rnd_cols == FP4_SR;
   a.sr_r = rnd_rows == FP4_SR;
   a.seed_c = seed_cols;
@@ -188,10 +214,12 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
   a.scales_c = out_cols->scales;
   a.codes_r = out_rows->codes;
   a.scales_r = out_rows->scales;
-  a.amax = out_cols->amax;
+  a.amax_c = out_cols->amax;
+  a.amax_r = two_amax ? out_rows->amax : out_cols->amax;
   a.tscale_c = out_cols->tscale;
   a.tscale_r = out_rows->tscale;
-  a.amax_r = (nv && out_rows->amax && out_rows->amax != out_cols->amax) ? out_rows->amax : nullptr;
+  a.amax_copy = (nv && !two_amax && out_rows->amax && out_rows->amax != out_cols->amax)
+                    ? out_rows->amax : nullptr;
   fp4i_launch_quant_dual(a, s);
   out_cols->rows = R;
   out_cols->cols = C;

@@ -27,14 +27,15 @@ struct DualArgs {
   bool bf16;
   int64_t R, C, ld;
   int fmt;
-  bool had_on;
+  bool had_c, had_r;               // rotation of each orientation
   bool sr_c, sr_r;
   uint64_t seed_c, offset_c, seed_r, offset_r;
   uint32_t signs_c, signs_r;
   uint8_t *codes_c, *scales_c, *codes_r, *scales_r;
-  const float* amax;               // NVFP4: the tensor amax (already computed)
-  float *tscale_c, *tscale_r;      // NVFP4: receive s_g
-  float* amax_r;                   // NVFP4: receives a copy of the amax, or null
+  const float* amax_c;             // NVFP4: tensor amax of each orientation's values
+  const float* amax_r;             //   (already computed; the same pointer when equal)
+  float *tscale_c, *tscale_r;      // NVFP4: receive s_g of each orientation
+  float* amax_copy;                // NVFP4: receives a copy of *amax_c, or null
 };
 
 struct GemmArgs {
@@ -53,6 +54,17 @@ struct GemmArgs {
 
 void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
                       hipStream_t s);
+// amax of the values rotated 16-wide (NVFP4 Hadamard) along rows (blocks along
+// C) or down columns (rows_axis: blocks along R).
+void fp4i_launch_amax_rot16(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld,
+                            bool rows_axis, uint32_t signs, float* amax, hipStream_t s);
+// Both orientations' amaxes of a dual quantization with a rotation on at least
+// one side, from one read (R % 16 == 0, C % 16 == 0): amax_c of the values
+// blocked along C (rotated along C when had_c), amax_r of those blocked along R
+// (rotated along R when had_r).
+void fp4i_launch_amax_pair(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, bool had_c,
+                           uint32_t signs_c, bool had_r, uint32_t signs_r, float* amax_c,
+                           float* amax_r, hipStream_t s);
 void fp4i_launch_quant(const QuantArgs& a, hipStream_t s);
 void fp4i_launch_quant_dual(const DualArgs& a, hipStream_t s);
 void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,

@@ -5,14 +5,20 @@
 // the Way, Key points; Quartet, Approach):
 //   NVFP4  s_g = amax/2688; per 16-block byte = E4M3_rne((amax_b/6)/s_g),
 //          r = 1/(sdec*s_g); codes = E2M1(x*r)
-//   MXFP4  optional 32-wide random-sign Hadamard; per 32-block e = the
-//          smallest e with 6*2^e >= amax_b; codes = E2M1(x*2^-e)
+//   MXFP4  per 32-block e = the smallest e with 6*2^e >= amax_b;
+//          codes = E2M1(x*2^-e)
+//   optional random-sign Hadamard rotation of each block first (32-wide for
+//   MXFP4, 16-wide for NVFP4, whose tensor amax is then the rotated values')
 //   RTN or SR (16-bit Philox4x32-10 draws keyed by seed and element index).
 //
 // Memory-bound passes: every element is read once from HBM with 16-byte loads
 // and written once as a nibble; block scales are one byte per block.
 //  * k_amax        wave-strided 16-byte loads, per-lane max, wave and workgroup
-//                  reduction, one atomicMax per workgroup on the float bits.
+//                  reduction, one atomicMax per workgroup on the float bits;
+//                  optionally of the 16-wide rotated values along rows (pairs
+//                  of lanes hold a block: one DPP butterfly stage).
+//  * k_amax_rot_rows  the same for the rotation down columns: each lane reads
+//                  16 rows x 8 columns and rotates each column in registers.
 //  * k_quant_cols  blocks along the contiguous axis: each lane owns 8
 //                  consecutive elements (one 16-byte bf16 load), a block spans
 //                  2 (NVFP4) or 4 (MXFP4) lanes; the block amax and the
@@ -25,28 +31,57 @@
 //                  thread quantizes one block in each of 2 or 4 adjacent
 //                  columns, and the codes leave through an LDS staging area
 //                  in whole 128-byte lines.
-//  * k_quant_dual  both orientations from one read: a 128 x 128 tile in LDS,
-//                  quantized down its columns (staged, as k_quant_rows) and
-//                  along its rows (written directly).
 //  * k_dequant     8 elements per lane.
-#include "fp4_device.hpp"
+// Both orientations from one read are in quant_dual.hip.
 #include "fp4_internal.hpp"
+#include "quant_common.hpp"
 
-using namespace fp4dev;
+using namespace fp4q;
 
 namespace {
 
-constexpr int NV = 0;
-constexpr int MX = 1;
-
 __global__ void k_zero1(float* p) { *p = 0.0f; }
+
+// The 16-wide rotation of 8 elements per lane, lanes 2j and 2j+1 holding one
+// block (elements 0..7 and 8..15): signs, stages 1, 2, 4 in registers, stage
+// 8 across the lane pair, times 1/4. Every lane of the wave must take part.
+__device__ __forceinline__ void hadamard16_lane_pair(float x[8], uint32_t signs, int upper) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((signs >> (8 * upper + i)) & 1u) x[i] = -x[i];
+  fwht8_local(x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = dpp_xor1(x[i]);
+    x[i] = upper ? p - x[i] : x[i] + p;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * 0.25f;
+}
+
+// Wave and workgroup max of m >= 0, one atomicMax per workgroup on the float
+// bits (monotone for non-negative floats).
+__device__ __forceinline__ void amax_reduce(float m, float* amax) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float part[4];
+  if (lane == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(b));
+  }
+}
 
 // A wave task is a 2048-element segment of one row: each lane issues four
 // independent 16-byte (bf16) loads before reducing, to keep enough bytes in
-// flight per CU.
-template <bool BF16>
+// flight per CU. ROT: the amax of the values rotated 16-wide along the row
+// (C % 16 == 0, so both lanes of a block are in or out of range together).
+template <bool BF16, bool ROT>
 __global__ __launch_bounds__(256) void k_amax(const void* __restrict__ src, int64_t C, int64_t ld,
-                                               uint32_t spr, uint32_t ntasks, float* amax) {
+                                               uint32_t spr, uint32_t ntasks, uint32_t signs,
+                                               float* amax) {
   constexpr int ES = BF16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
@@ -66,43 +101,55 @@ __global__ __launch_bounds__(256) void k_amax(const void* __restrict__ src, int6
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[k][i] = 0.0f;
     }
+    if constexpr (ROT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hadamard16_lane_pair(x[k], signs, lane & 1);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[k][i]));
   }
+  amax_reduce(m, amax);
+}
+
+// The amax of the values rotated 16-wide down the columns (R % 16 == 0). A
+// wave task is a band of 16 rows by 512 columns: each lane loads 16 rows of
+// its 8 columns (coalesced 16-byte loads, 1 KiB per row per wave for bf16)
+// and rotates each column in registers.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_amax_rot_rows(const void* __restrict__ src, int64_t C,
+                                                        int64_t ld, uint32_t spr, uint32_t ntasks,
+                                                        uint32_t signs, float* amax) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t nwaves = gridDim.x * 4u;
+  float m = 0.0f;
+  for (uint32_t t = wave; t < ntasks; t += nwaves) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t band = tu / spr;
+    const uint32_t seg = tu - band * spr;
+    const int64_t col = (int64_t)seg * 512 + lane * 8;
+    if (col < C) {
+      const char* base = static_cast<const char*>(src) + ((int64_t)band * 16 * ld + col) * ES;
+      float x[16][8];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  __shared__ float part[4];
-  if (lane == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(b));
+      for (int i = 0; i < 16; ++i) load8<BF16>(base + (int64_t)i * ld * ES, x[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = x[i][j];
+        hadamard_block<16>(v, signs);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+      }
+    }
   }
+  amax_reduce(m, amax);
 }
 
-__device__ __forceinline__ float nv_tensor_scale(float amax) {
-  return amax == 0.0f ? 1.0f : amax / 2688.0f;
-}
-
-// Block scale of one block with amax m. Returns the scale byte, sets the
-// element multiplier r.
-template <int FMT>
-__device__ __forceinline__ uint32_t block_scale(float m, float sg, float& r) {
-  if constexpr (FMT == NV) {
-    float q = m / 6.0f;
-    q = q / sg;
-    uint32_t byte = e4m3_encode(q);
-    float d = e4m3_decode(byte) * sg;
-    r = (d == 0.0f) ? 0.0f : 1.0f / d;
-    return byte;
-  } else {
-    int e = e8m0_exponent(m);
-    r = pow2_neg(e);
-    return (uint32_t)(e + 127);
-  }
-}
 
 template <int FMT, int RND, bool BF16, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t C, int64_t ld,
@@ -121,7 +168,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
     sg = nv_tensor_scale(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
   }
-  const int sub = lane & 3;  // position of this lane's 8 elements inside a 32-block
+  const int sub = lane & (B / 8 - 1);  // position of this lane's 8 elements inside its block
   for (uint32_t t = wave; t < ntasks; t += nwaves) {
     const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
     const uint32_t r = tu / spr;
@@ -130,7 +177,10 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
     const bool active = col < C;
     float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (active) load8<BF16>(static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES, x);
-    if constexpr (HAD) {
+    if constexpr (HAD && FMT == NV) {
+      hadamard16_lane_pair(x, signs, sub);
+    } else if constexpr (HAD) {
+      // 32-wide: stages 1, 2, 4 in registers, 8 and 16 across the lane quad.
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if ((signs >> (8 * sub + i)) & 1u) x[i] = -x[i];
@@ -174,20 +224,6 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
   }
 }
 
-// Full 32-point butterfly (stages 1, 2, 4, 8, 16) on a 32-block held by one thread.
-__device__ __forceinline__ void fwht32_local(float x[32]) {
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if ((i & h) == 0) {
-        float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
-      }
-    }
-  }
-}
 
 // Transposed quantize: blocks along rows (the orientation of the dgrad and
 // wgrad operands). A workgroup takes a tile of TR = 256 rows x TC = 64
@@ -281,15 +317,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
     const int cl = cl0 + k;
     const int64_t cg = c0 + cl;
     float* xk = x[k];
-    if constexpr (HAD) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if ((signs >> i) & 1u) xk[i] = -xk[i];
-      fwht32_local(xk);
-      const float hc = hadamard_norm();
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xk[i] = xk[i] * hc;
-    }
+    if constexpr (HAD) hadamard_block<B>(xk, signs);
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
@@ -348,238 +376,66 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
   }
 }
 
-// Both orientations from one read of the source. A workgroup takes a
-// 128 x 128 tile into LDS once (input format), then
-//  (a) quantizes it with blocks down its columns (the transposed, ROWS
-//      orientation), as k_quant_rows does: thread (b, q) handles block b of
-//      NCOL adjacent columns; codes and scales are staged in LDS per output
-//      row and written out after (b);
-//  (b) quantizes it with blocks along its rows (the COLS orientation): thread
-//      (row, half) takes 64 consecutive elements of one row (4 NVFP4 or 2
-//      MXFP4 blocks) and writes their codes (32 bytes) and scales directly.
-// Each orientation has its own rounding mode, SR stream and Hadamard mask;
-// the results equal the two separate passes bit for bit.
-template <int FMT, int RC, int RR, bool BF16, bool HAD>
-__global__ __launch_bounds__(256) void k_quant_dual(
-    const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c,
-    uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
-    uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
-    const float* __restrict__ amax, float* tscale_c, float* tscale_r, float* amax_r,
-    uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
-    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r) {
+// Both orientations' tensor amaxes from one read, for a dual quantization with
+// a rotation on at least one side (R % 16 == 0, C % 16 == 0): the values
+// blocked along C (rotated 16-wide along the row when HC) and the values
+// blocked along R (rotated 16-wide down the column when HR). A wave task is a
+// band of 16 rows by 512 columns, each lane holding 16 rows of 8 columns: a
+// row's 16-block sits in a lane pair, a column's in one lane.
+template <bool BF16, bool HC, bool HR>
+__global__ __launch_bounds__(256) void k_amax_pair(const void* __restrict__ src, int64_t C, int64_t ld,
+                                                    uint32_t spr, uint32_t ntasks, uint32_t signs_c,
+                                                    uint32_t signs_r, float* amax_c, float* amax_r) {
   constexpr int ES = BF16 ? 2 : 4;
-  constexpr int B = FMT == NV ? 16 : 32;
-  constexpr int T = 128;                  // tile rows = tile columns
-  constexpr int NB = T / B;               // blocks per tile column (and per tile row)
-  constexpr int NCOL = NB * T / 256;      // (a): adjacent columns per thread
-  constexpr int TPB = T / NCOL;           // (a): threads per block row
-  constexpr int PITCH = T * ES + 8;       // row pitch in bytes (8-byte reads stay aligned)
-  constexpr int SP = T / 2 + 4;           // staged code bytes per output row of (a)
-  __shared__ __attribute__((aligned(16))) uint8_t tile[T * PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_c[T * SP];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_s[T * NB];
-
-  float sg = 1.0f;
-  if constexpr (FMT == NV) {
-    const float a = *amax;
-    sg = nv_tensor_scale(a);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      *tscale_c = sg;
-      *tscale_r = sg;
-      if (amax_r) *amax_r = a;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t nwaves = gridDim.x * 4u;
+  float mc = 0.0f, mr = 0.0f;
+  for (uint32_t t = wave; t < ntasks; t += nwaves) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t band = tu / spr;
+    const uint32_t seg = tu - band * spr;
+    const int64_t col = (int64_t)seg * 512 + lane * 8;
+    const char* base = static_cast<const char*>(src) + ((int64_t)band * 16 * ld + col) * ES;
+    float x[16][8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (col < C) load8<BF16>(base + (int64_t)i * ld * ES, x[i]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
+    }
+    // blocks along C (all lanes take part in the lane-pair exchange)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = x[i][j];
+      if constexpr (HC) hadamard16_lane_pair(w, signs_c, lane & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mc = fmaxf(mc, fabsf(w[j]));
+    }
+    // blocks along R
+    if constexpr (HR) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = x[i][j];
+        hadamard_block<16>(v, signs_r);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mr = fmaxf(mr, fabsf(v[i]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mr = fmaxf(mr, fabsf(x[i][j]));
     }
   }
-  const uint32_t tr = blockIdx.x / tiles_c;
-  const uint32_t tc = blockIdx.x - tr * tiles_c;
-  const int64_t r0 = (int64_t)tr * T;
-  const int64_t c0 = (int64_t)tc * T;
-  const int tid = threadIdx.x;
-
-  // 1. tile load, 16 bytes per load.
-  constexpr int CPR = T * ES / 16;
-#pragma unroll
-  for (int k = 0; k < T * CPR / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int rr = idx / CPR;
-    const int cc = idx % CPR;
-    const int64_t col = c0 + cc * (16 / ES);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < R && col < C)
-      v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-    uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
-    d[0] = make_uint2(v.x, v.y);
-    d[1] = make_uint2(v.z, v.w);
-  }
+  amax_reduce(mc, amax_c);
   __syncthreads();
-
-  const int64_t rows_here = R - r0 < T ? R - r0 : T;  // multiples of B
-  const int64_t cols_here = C - c0 < T ? C - c0 : T;
-
-  // (a) blocks down the columns: output row c0 + cl, elements r0 ..
-  {
-    const int b = tid / TPB;
-    const int cl0 = (tid % TPB) * NCOL;
-    const int64_t rg = r0 + (int64_t)b * B;
-    float x[NCOL][B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
-      if constexpr (BF16) {
-        if constexpr (NCOL == 4) {
-          const uint2 w = *reinterpret_cast<const uint2*>(p);
-          x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
-        } else {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-          x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < NCOL; k += 2) {
-          const float2 w = *reinterpret_cast<const float2*>(p + 4 * k);
-          x[k][i] = w.x; x[k + 1][i] = w.y;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NCOL; ++k) {
-      const int cl = cl0 + k;
-      const int64_t cg = c0 + cl;
-      float* xk = x[k];
-      if constexpr (HAD) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if ((signs_r >> i) & 1u) xk[i] = -xk[i];
-        fwht32_local(xk);
-        const float hc = hadamard_norm();
-#pragma unroll
-        for (int i = 0; i < 32; ++i) xk[i] = xk[i] * hc;
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
-      float rcp;
-      const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
-      uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
-#pragma unroll
-      for (int g = 0; g < B / 8; ++g) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
-        if constexpr (RR == 0) {
-          sc[g] = e2m1_rtn_pack8(v);
-        } else {
-          uint32_t h[4];
-          sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
-          sc[g] = e2m1_sr_pack8(v, h);
-        }
-      }
-      stage_s[cl * NB + b] = (uint8_t)sbyte;
-    }
-  }
-
-  // (b) blocks along the rows: row r0 + row, elements c0 + 64 * half ..
-  {
-    const int row = tid >> 1;
-    const int half = tid & 1;
-    const int64_t rgl = r0 + row;
-    constexpr int NBT = 64 / B;  // blocks per thread
-    uint32_t w[8];
-    uint32_t sb[NBT];
-#pragma unroll
-    for (int bb = 0; bb < NBT; ++bb) {
-      float x[B];
-      const uint8_t* p = &tile[row * PITCH + (half * 64 + bb * B) * ES];
-#pragma unroll
-      for (int i = 0; i < B; i += 4) {
-        if constexpr (BF16) {
-          const uint2 u = *reinterpret_cast<const uint2*>(p + 2 * i);
-          x[i] = bf16_lo(u.x); x[i + 1] = bf16_hi(u.x); x[i + 2] = bf16_lo(u.y); x[i + 3] = bf16_hi(u.y);
-        } else {
-          const float2 a = *reinterpret_cast<const float2*>(p + 4 * i);
-          const float2 c = *reinterpret_cast<const float2*>(p + 4 * i + 8);
-          x[i] = a.x; x[i + 1] = a.y; x[i + 2] = c.x; x[i + 3] = c.y;
-        }
-      }
-      if constexpr (HAD) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if ((signs_c >> i) & 1u) x[i] = -x[i];
-        fwht32_local(x);
-        const float hc = hadamard_norm();
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = x[i] * hc;
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
-      float rcp;
-      sb[bb] = block_scale<FMT>(m, sg, rcp);
-      const int64_t col0 = c0 + half * 64 + bb * B;
-#pragma unroll
-      for (int g = 0; g < B / 8; ++g) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
-        if constexpr (RC == 0) {
-          w[bb * (B / 8) + g] = e2m1_rtn_pack8(v);
-        } else {
-          uint32_t h[4];
-          sr_draws8(seed_c, (off_c + (uint64_t)rgl * (uint64_t)C + (uint64_t)col0) / 8 + g, h);
-          w[bb * (B / 8) + g] = e2m1_sr_pack8(v, h);
-        }
-      }
-    }
-    if (row < rows_here && half * 64 < cols_here) {
-      uint8_t* dst = codes_c + rgl * (C / 2) + (c0 + half * 64) / 2;
-      const bool full = half * 64 + 64 <= cols_here;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (full || (half * 64 + 16 * k) < cols_here)
-          *reinterpret_cast<uint2*>(dst + 8 * k) = make_uint2(w[2 * k], w[2 * k + 1]);
-      uint8_t* sdst = scales_c + rgl * (C / B) + (c0 + half * 64) / B;
-      if (scale_words_c && full) {
-        if constexpr (NBT == 4) *reinterpret_cast<uint32_t*>(sdst) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-        else *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)(sb[0] | (sb[1] << 8));
-      } else {
-#pragma unroll
-        for (int bb = 0; bb < NBT; ++bb)
-          if (half * 64 + bb * B < cols_here) sdst[bb] = (uint8_t)sb[bb];
-      }
-    }
-  }
-  __syncthreads();
-
-  // write out (a): output row c0 + cl gets T/2 code bytes (8-byte pieces) and NB scale bytes.
-#pragma unroll
-  for (int k = 0; k < T * (T / 16) / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int cl = idx / (T / 16);
-    const int seg = idx % (T / 16);
-    if (cl < cols_here && seg * 16 < rows_here) {
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
-      *reinterpret_cast<uint2*>(codes_r + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
-    }
-  }
-  if (scale_words_r) {
-    // (R / B) % 4 == 0: 4-byte words, NB / 4 per output row.
-    constexpr int WPR = NB / 4;
-    if (tid < T * WPR) {
-      const int cl = tid / WPR;
-      const int wd = tid % WPR;
-      if (cl < cols_here && wd * 4 * B < rows_here)
-        *reinterpret_cast<uint32_t*>(scales_r + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
-            *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < (T * NB + 255) / 256; ++k) {
-      const int idx = k * 256 + tid;
-      const int cl = idx / NB;
-      const int bb = idx % NB;
-      if (idx < T * NB && cl < cols_here && bb * B < rows_here)
-        scales_r[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
-    }
-  }
+  amax_reduce(mr, amax_r);
 }
 
 template <int FMT, bool BF16OUT>
@@ -673,68 +529,73 @@ void launch_axis(const QuantArgs& a, hipStream_t s) {
 
 template <int FMT, int RND>
 void launch_src(const QuantArgs& a, hipStream_t s) {
-  if constexpr (FMT == MX) {
-    if (a.had_on) {
-      if (a.bf16) launch_axis<FMT, RND, true, true>(a, s);
-      else launch_axis<FMT, RND, false, true>(a, s);
-      return;
-    }
-  }
-  if (a.bf16) launch_axis<FMT, RND, true, false>(a, s);
-  else launch_axis<FMT, RND, false, false>(a, s);
-}
-
-template <int FMT, int RC, int RR, bool BF16, bool HAD>
-void launch_dual(const DualArgs& a, hipStream_t s) {
-  constexpr int B = FMT == NV ? 16 : 32;
-  const uint32_t tiles_c = (uint32_t)((a.C + 127) / 128);
-  const uint32_t tiles_r = (uint32_t)((a.R + 127) / 128);
-  // Scale bytes of a tile go out as words when every row start keeps them aligned.
-  const uint32_t words_c = FMT == NV ? (a.C / B) % 4 == 0 : (a.C / B) % 2 == 0;
-  const uint32_t words_r = (a.R / B) % 4 == 0;
-  hipLaunchKernelGGL((k_quant_dual<FMT, RC, RR, BF16, HAD>), dim3(tiles_c * tiles_r), dim3(256), 0, s,
-                     a.src, a.R, a.C, a.ld, tiles_c, a.codes_c, a.scales_c, a.codes_r, a.scales_r,
-                     a.amax, a.tscale_c, a.tscale_r, a.amax_r, a.seed_c, a.offset_c, a.signs_c,
-                     a.seed_r, a.offset_r, a.signs_r, words_c, words_r);
-}
-
-template <int FMT, bool BF16, bool HAD>
-void launch_dual_rnd(const DualArgs& a, hipStream_t s) {
-  if (a.sr_c) {
-    if (a.sr_r) launch_dual<FMT, 1, 1, BF16, HAD>(a, s);
-    else launch_dual<FMT, 1, 0, BF16, HAD>(a, s);
+  if (a.had_on) {
+    if (a.bf16) launch_axis<FMT, RND, true, true>(a, s);
+    else launch_axis<FMT, RND, false, true>(a, s);
   } else {
-    if (a.sr_r) launch_dual<FMT, 0, 1, BF16, HAD>(a, s);
-    else launch_dual<FMT, 0, 0, BF16, HAD>(a, s);
+    if (a.bf16) launch_axis<FMT, RND, true, false>(a, s);
+    else launch_axis<FMT, RND, false, false>(a, s);
   }
 }
 
 }  // namespace
 
-void fp4i_launch_quant_dual(const DualArgs& a, hipStream_t s) {
-  if (a.fmt == NV) {
-    if (a.bf16) launch_dual_rnd<NV, true, false>(a, s);
-    else launch_dual_rnd<NV, false, false>(a, s);
-  } else if (a.had_on) {
-    if (a.bf16) launch_dual_rnd<MX, true, true>(a, s);
-    else launch_dual_rnd<MX, false, true>(a, s);
-  } else {
-    if (a.bf16) launch_dual_rnd<MX, true, false>(a, s);
-    else launch_dual_rnd<MX, false, false>(a, s);
-  }
-}
 
 void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
                       hipStream_t s) {
   hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax);
   const uint32_t spr = (uint32_t)((C + 2047) / 2048);
   const uint32_t ntasks = (uint32_t)(R * spr);
+  const dim3 g(strided_grid(ntasks)), b(256);
   if (bf16)
-    hipLaunchKernelGGL(k_amax<true>, dim3(strided_grid(ntasks)), dim3(256), 0, s, src, C, ld, spr,
-                       ntasks, amax);
+    hipLaunchKernelGGL((k_amax<true, false>), g, b, 0, s, src, C, ld, spr, ntasks, 0u, amax);
   else
-    hipLaunchKernelGGL(k_amax<false>, dim3(strided_grid(ntasks)), dim3(256), 0, s, src, C, ld, spr,
-                       ntasks, amax);
+    hipLaunchKernelGGL((k_amax<false, false>), g, b, 0, s, src, C, ld, spr, ntasks, 0u, amax);
+}
+
+void fp4i_launch_amax_rot16(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld,
+                            bool rows_axis, uint32_t signs, float* amax, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax);
+  if (rows_axis) {
+    const uint32_t spr = (uint32_t)((C + 511) / 512);
+    const uint32_t ntasks = (uint32_t)(R / 16 * spr);
+    const dim3 g(strided_grid(ntasks)), b(256);
+    if (bf16)
+      hipLaunchKernelGGL((k_amax_rot_rows<true>), g, b, 0, s, src, C, ld, spr, ntasks, signs, amax);
+    else
+      hipLaunchKernelGGL((k_amax_rot_rows<false>), g, b, 0, s, src, C, ld, spr, ntasks, signs, amax);
+  } else {
+    const uint32_t spr = (uint32_t)((C + 2047) / 2048);
+    const uint32_t ntasks = (uint32_t)(R * spr);
+    const dim3 g(strided_grid(ntasks)), b(256);
+    if (bf16)
+      hipLaunchKernelGGL((k_amax<true, true>), g, b, 0, s, src, C, ld, spr, ntasks, signs, amax);
+    else
+      hipLaunchKernelGGL((k_amax<false, true>), g, b, 0, s, src, C, ld, spr, ntasks, signs, amax);
+  }
+}
+
+void fp4i_launch_amax_pair(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, bool had_c,
+                           uint32_t signs_c, bool had_r, uint32_t signs_r, float* amax_c,
+                           float* amax_r, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax_c);
+  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, s, amax_r);
+  const uint32_t spr = (uint32_t)((C + 511) / 512);
+  const uint32_t ntasks = (uint32_t)(R / 16 * spr);
+  const dim3 g(strided_grid(ntasks)), b(256);
+#define FP4_AMAX_PAIR(BF, HC, HR)                                                                 \
+  hipLaunchKernelGGL((k_amax_pair<BF, HC, HR>), g, b, 0, s, src, C, ld, spr, ntasks, signs_c, signs_r, \
+                     amax_c, amax_r)
+  if (bf16) {
+    if (had_c && had_r) FP4_AMAX_PAIR(true, true, true);
+    else if (had_c) FP4_AMAX_PAIR(true, true, false);
+    else FP4_AMAX_PAIR(true, false, true);
+  } else {
+    if (had_c && had_r) FP4_AMAX_PAIR(false, true, true);
+    else if (had_c) FP4_AMAX_PAIR(false, true, false);
+    else FP4_AMAX_PAIR(false, false, true);
+  }
+#undef FP4_AMAX_PAIR
 }
 
 void fp4i_launch_quant(const QuantArgs& a, hipStream_t s) {

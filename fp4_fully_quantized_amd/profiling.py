@@ -101,6 +101,8 @@ GROUPS = [
     ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
     ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
     ("tensor amax", r"^k_amax<"),
+    ("tensor amax of the values rotated down the columns", r"^k_amax_rot_rows<"),
+    ("both orientations' amaxes, one rotated (one read)", r"^k_amax_pair<"),
 ]
 
 

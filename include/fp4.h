@@ -12,9 +12,10 @@
  *     backward and update passes ("FP4 All the Way: Fully Quantized Training of
  *     LLMs", Key points), the random stream being Philox4x32-10 keyed by
  *     (seed, element index);
- *   - the block-wise random-sign Hadamard rotation of MXFP4 operands
- *     ("Quartet: Native FP4 Training Can Be Optimal for Large Language Models",
- *     Approach);
+ *   - the block-wise random-sign Hadamard rotation of operands, 32-wide for
+ *     MXFP4 ("Quartet: Native FP4 Training Can Be Optimal for Large Language
+ *     Models", Approach) and 16-wide for NVFP4 (Robots Atlas, "FP4", How it
+ *     works: random Hadamard transforms among the stabilizers of FP4 training);
  *   - the three linear-layer GEMMs in FP4 with FP32 accumulation (Quartet,
  *     summary; Robots Atlas "FP4", How it works / Execution paradigm):
  *       forward  Y  = X  W^T : A = X  (blocks along K = in-features),
@@ -37,10 +38,14 @@
  *              the element: Philox4x32-10, key = seed, counter = (i / 8, 0, 0)
  *              as (lo32, hi32, 0, 0), word (i / 2) % 4, low half for even i;
  *              i = row-major index in the quantized orientation + index_offset.
- *   Hadamard   per 32-block along the blocked axis: negate x_j where bit j of
- *              had_signs is set, Sylvester FWHT (stages 1, 2, 4, 8, 16, FP32),
- *              multiply by fp32(2^-2.5). The same mask must be used for both
- *              GEMM operands so the rotation cancels.
+ *   Hadamard   per B-block along the blocked axis (one rotation per scale
+ *              block): negate x_j where bit j of had_signs is set (j < B),
+ *              Sylvester FWHT (stages 1, 2, .., B/2, FP32), multiply by
+ *              fp32(2^-2.5) (MXFP4, B = 32) or 1/4 (NVFP4, B = 16, exact).
+ *              The rotation comes first: the NVFP4 tensor amax is that of the
+ *              rotated values (so it depends on the rotation axis). The same
+ *              mask must be used for both GEMM operands so the rotation
+ *              cancels.
  *
  * Memory and ownership: every pointer argument named "device" is a device
  * pointer the caller allocated (and keeps ownership of); the library never
@@ -97,7 +102,7 @@ typedef struct fp4_tensor {
     int64_t rows;
     int64_t cols;
     int32_t fmt;        /* fp4_format */
-    int32_t had_on;     /* 1: values are in the Hadamard-rotated domain (MXFP4 only) */
+    int32_t had_on;     /* 1: values are in the Hadamard-rotated domain */
     uint32_t had_signs; /* the rotation's sign mask when had_on */
     uint32_t reserved;
 } fp4_tensor;
@@ -122,21 +127,33 @@ const char* fp4_status_str(fp4_status s);
 fp4_status fp4_tensor_amax(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                            float* amax, fp4_stream_t stream);
 
+/* The tensor amax of the NVFP4-rotated values: *amax = max |y| where y is src
+ * with the 16-wide random-sign Hadamard rotation (mask had_signs, see
+ * Conventions) applied to every 16-block along the given axis (COLS: along C;
+ * ROWS: down the columns, along R). This is the amax an NVFP4 quantization with
+ * had_on uses (Robots Atlas "FP4", How it works: per-tensor scale, random
+ * Hadamard transforms); a data-parallel caller reduces it across ranks before
+ * quantizing with amax_ready = 1. Same requirements as fp4_tensor_amax, and
+ * the rotated dimension a multiple of 16. */
+fp4_status fp4_tensor_amax_hadamard16(const void* src, fp4_dtype src_t, int64_t R, int64_t C,
+                                      int64_t ld, fp4_axis axis, uint32_t had_signs, float* amax,
+                                      fp4_stream_t stream);
+
 /* Quantize the R x C matrix src (row-major, leading dimension ld, FP32 or bf16;
  * device) into *out.
  *   axis         FP4_AXIS_COLS: blocks along C, out is R x C;
  *                FP4_AXIS_ROWS: blocks along R, out is C x R (the transpose).
  *   rnd          FP4_RTN or FP4_SR.
  *   seed, index_offset  the SR stream (ignored for RTN).
- *   amax_ready   NVFP4: 1 if *out->amax already holds this tensor's amax (from
- *                fp4_tensor_amax or an earlier quantize of the same tensor in
- *                the other orientation); 0 to compute it first. Ignored for MXFP4.
+ *   amax_ready   NVFP4: 1 if *out->amax already holds the amax of the values
+ *                quantized (from fp4_tensor_amax, or fp4_tensor_amax_hadamard16
+ *                with this axis and mask when had_on, or an earlier quantize
+ *                of the same values); 0 to compute it first. Ignored for MXFP4.
  *   out          caller-filled descriptor: codes, scales, fmt, had_on,
  *                had_signs and, for NVFP4, amax and tscale. The call writes
  *                out->rows and out->cols; *out->tscale receives s_g.
  * Requires: R, C >= 1; the blocked dimension a multiple of B (C for COLS, R
- * for ROWS); C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned;
- * had_on only with MXFP4. */
+ * for ROWS); C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned. */
 fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream);
@@ -148,14 +165,20 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
  * to
  *   fp4_quantize(src, ..., FP4_AXIS_COLS, rnd_cols, seed_cols, index_offset_cols, ..., out_cols)
  *   fp4_quantize(src, ..., FP4_AXIS_ROWS, rnd_rows, seed_rows, index_offset_rows, ..., out_rows)
- * with both calls using the same tensor amax.
+ * with each call's amax_ready set as below.
  *   out_cols     blocks along C: out_cols is R x C.
  *   out_rows     blocks along R: out_rows is C x R (the transpose).
- *   amax_ready   NVFP4: 1 if *out_cols->amax already holds this tensor's amax;
- *                0 to compute it first. *out_rows->amax, when it is another
- *                scalar, receives a copy; both tscale scalars receive s_g.
- * The two descriptors must have the same fmt and had_on (MXFP4: each keeps
- * its own had_signs). Requires: R, C >= 1, both multiples of B; C % 8 == 0;
+ *   amax_ready   NVFP4 without rotation: 1 if *out_cols->amax already holds the
+ *                tensor amax, 0 to compute it first; *out_rows->amax, when it
+ *                is another scalar, receives a copy; both tscale scalars
+ *                receive s_g.
+ *                NVFP4 with had_on in either descriptor: the two orientations'
+ *                values have different amaxes, so out_rows->amax must be its
+ *                own scalar (FP4_ERR_NULL if NULL, FP4_ERR_UNSUPPORTED if it is
+ *                out_cols->amax); 1 if each already holds its orientation's
+ *                amax, 0 to compute both first; each tscale receives its own s_g.
+ * The two descriptors must have the same fmt; had_on and had_signs are each
+ * descriptor's own. Requires: R, C >= 1, both multiples of B; C % 8 == 0;
  * ld >= C and ld % 8 == 0; src 16-byte aligned. Errors as fp4_quantize. */
 fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                              fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,

@@ -86,7 +86,7 @@ QUANT_BAD = [
     (0x1000, 1, 64, 128, 132, 0, 0, 0, {}, 3),          # ld % 8
     (0x1000, 1, 40, 128, 128, 1, 0, 0, {}, 2),          # R not a multiple of 16 (ROWS)
     (0x1000, 1, 64, 80, 128, 0, 0, 0, {"fmt": 1}, 2),   # C not a multiple of 32 (MXFP4)
-    (0x1000, 1, 64, 128, 128, 0, 0, 0, {"had_on": 1}, 4),  # Hadamard with NVFP4
+    (0x1000, 1, 40, 128, 128, 1, 0, 0, {"had_on": 1}, 2),  # NVFP4 rotation, R not a multiple of 16
     (0x1000, 1, 64, 128, 128, 0, 1, 4, {}, 3),          # SR offset % 8
     (0x1000, 2, 64, 128, 128, 0, 0, 0, {}, 5),          # bad dtype
     (0x1000, 1, 64, 128, 128, 2, 0, 0, {}, 5),          # bad axis
@@ -116,8 +116,10 @@ DUAL_BAD = [
     (0x1000, 1, 40, 128, 128, 0, 0, 1, 0, {}, {}, 2),          # R not a multiple of 16
     (0x1000, 1, 64, 120, 128, 0, 0, 1, 0, {}, {}, 2),          # C not a multiple of 16
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"fmt": 1}, {}, 4),  # formats differ
-    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"fmt": 1, "had_on": 1}, {"fmt": 1}, 4),
-    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"had_on": 1}, 4),  # Hadamard with NVFP4
+    # NVFP4 with a rotation: the orientations need their own amax scalars
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"had_on": 1}, 4),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {}, {"had_on": 1}, 4),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"amax": 0}, 1),
     (0x1000, 1, 64, 128, 128, 1, 4, 1, 0, {}, {}, 3),          # SR offset % 8 (cols)
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 12, {}, {}, 3),         # SR offset % 8 (rows)
     (0x1000, 1, 64, 128, 128, 2, 0, 1, 0, {}, {}, 5),          # bad rounding
@@ -140,6 +142,24 @@ def test_quantize_dual_rejects_null_descriptors(fp4):
     d = _t(fp4)
     assert fp4.lib().fp4_quantize_dual(0x1000, 1, 64, 128, 128, 0, 0, 0, 1, 0, 0, 1, None,
                                        ctypes.byref(d), None) == 1
+
+
+AMAX_H16_BAD = [
+    # (src, dtype, R, C, ld, axis, amax, expected)
+    (0, 1, 64, 128, 128, 0, 0x30000, 1),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1),
+    (0x1000, 1, 64, 136, 136, 0, 0x30000, 2),   # C not a multiple of 16 (COLS)
+    (0x1000, 1, 40, 128, 128, 1, 0x30000, 2),   # R not a multiple of 16 (ROWS)
+    (0x1000, 1, 64, 128, 128, 2, 0x30000, 5),   # bad axis
+    (0x1000, 3, 64, 128, 128, 0, 0x30000, 5),   # bad dtype
+    (0x1004, 1, 64, 128, 128, 0, 0x30000, 3),   # misaligned
+]
+
+
+@pytest.mark.parametrize("case", AMAX_H16_BAD)
+def test_amax_hadamard16_rejects_bad_arguments(fp4, case):
+    src, dt, R, C, ld, axis, amax, want = case
+    assert fp4.lib().fp4_tensor_amax_hadamard16(src, dt, R, C, ld, axis, 5, amax, None) == want
 
 
 GEMM_BAD = [

@@ -43,7 +43,7 @@ def _run(fp4, orc, qa, qb, out, signs=None):
 SHAPES = [(200, 136, 256), (77, 300, 384), (256, 256, 128), (1, 1, 128), (513, 129, 1024)]
 
 
-@pytest.mark.parametrize("fmt,had", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("fmt,had", [(0, False), (0, True), (1, False), (1, True)])
 @pytest.mark.parametrize("out", ["fp32", "bf16"])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_matches_oracle(fp4, orc, fmt, had, out, M, N, K):
@@ -72,6 +72,35 @@ def test_gpu_quantizer_into_gemm_end_to_end(fp4, orc):
     ref, S = orc.gemm_ref(orc.quantize(xh), orc.quantize(wh))
     ok, worst = orc.gemm_check(to_host(y), ref, S, "fp32")
     assert ok, worst
+
+
+def test_nvfp4_rotated_wgrad_end_to_end(fp4, orc):
+    """wgrad dW = dY^T X with both operands quantized by the GPU along the
+    tokens with the same 16-wide rotation (SR, one dual pass each): equal to
+    the oracle's GEMM of the oracle's quantizations, and the rotation cancels
+    (close to the unrotated product)."""
+    import torch
+    T, N, K = 512, 192, 256
+    dyh, xh = _data((T, N), 6), _data((T, K), 7, outliers=True)
+    signs = orc.hadamard_signs(21)
+    _, a = fp4.quantize_dual(to_device(dyh), rnd_cols=1, seed_cols=1, rnd_rows=1, seed_rows=2,
+                             had_signs_rows=signs)
+    _, b = fp4.quantize_dual(to_device(xh), rnd_cols=0, rnd_rows=1, seed_rows=3, had_signs_rows=signs)
+    y = to_host(fp4.gemm(a, b, dtype=torch.float32))
+    qa = orc.quantize(dyh, axis=1, rnd=1, seed=2, had_on=True, had_signs=signs)
+    qb = orc.quantize(xh, axis=1, rnd=1, seed=3, had_on=True, had_signs=signs)
+    ref, S = orc.gemm_ref(qa, qb)
+    ok, worst = orc.gemm_check(y, ref, S, "fp32")
+    assert ok, worst
+    # The rotation cancels: the error against the exact product is that of an
+    # unrotated FP4 quantization of the same operands (a mask mismatch would
+    # leave an error of the order of the product itself).
+    exact = orc.bf16_bits_to_f32(dyh).astype(np.float64).T @ orc.bf16_bits_to_f32(xh).astype(np.float64)
+    plain, _ = orc.gemm_ref(orc.quantize(dyh, axis=1, rnd=1, seed=2), orc.quantize(xh, axis=1, rnd=1, seed=3))
+    rel = np.linalg.norm(y - exact) / np.linalg.norm(exact)
+    rel_plain = np.linalg.norm(plain - exact) / np.linalg.norm(exact)
+    say("relative error rotated", rel, "unrotated", rel_plain)
+    assert rel < 1.5 * rel_plain, (rel, rel_plain)
 
 
 def _rows_of(q, rows):

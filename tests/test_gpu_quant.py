@@ -42,7 +42,7 @@ CASES = []
 for fmt in (0, 1):
     for rnd in (0, 1):
         for axis in (0, 1):
-            for had in ((False, True) if fmt == 1 else (False,)):
+            for had in (False, True):
                 for bf16 in (True, False):
                     CASES.append((fmt, rnd, axis, had, bf16))
 
@@ -74,6 +74,39 @@ def test_amax_ready_reuses_the_given_amax(fp4, orc):
     assert float(amax.cpu()[0]) == orc.tensor_amax(xh)
 
 
+AMAX_H16 = [((96, 1056), True), ((256, 256), False), ((32, 2064), True), ((4112, 48), True)]
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("shape,bf16", AMAX_H16)
+def test_amax_hadamard16_matches_oracle(fp4, orc, axis, shape, bf16):
+    """The amax of the 16-wide rotated values, along either axis, on shapes
+    with ragged wave segments (C not a multiple of 512 or 2048)."""
+    import torch
+    say("amax hadamard16", shape, "axis", axis, "bf16", bf16)
+    xh = _mixed(shape, 41 + shape[0], bf16)
+    signs = orc.hadamard_signs(12)
+    want = orc.quantize(xh, axis=axis, fmt=0, had_on=True, had_signs=signs)["amax"]
+    amax = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    fp4.fp4_tensor_amax_hadamard16(to_device(xh), axis, signs, amax)
+    assert float(amax.cpu()[0]) == want
+    assert want != orc.tensor_amax(xh)           # the rotation changes the amax here
+
+
+def test_nvfp4_hadamard_with_a_given_amax(fp4, orc):
+    """amax_ready: a rotated quantization takes the amax of the rotated values
+    from the dedicated call (as a data-parallel caller would after reducing it)."""
+    import torch
+    xh = _mixed((256, 512), 43)
+    x = to_device(xh)
+    signs = orc.hadamard_signs(13)
+    q = fp4.QTensor(512, 256, 0, had_signs=signs)
+    fp4.fp4_tensor_amax_hadamard16(x, 1, signs, q.amax)
+    fp4.fp4_quantize(x, 1, 1, 4, 0, True, q)
+    want = orc.quantize(xh, axis=1, rnd=1, seed=4, had_on=True, had_signs=signs)
+    assert_same_quant(q_to_host(q), want, "rows, rotated, given amax")
+
+
 def test_strided_source(fp4, orc):
     import torch
     xh = _mixed((64, 1024), 4)
@@ -103,7 +136,9 @@ def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
 DUAL = []
 for fmt in (0, 1):
     for rc, rr in ((0, 1), (1, 1), (0, 0), (1, 0)):
-        for had in ((False, True) if fmt == 1 else (False,)):
+        DUAL.append((fmt, rc, rr, (False, False)))
+    for had in ((True, True), (False, True), (True, False)):
+        for rc, rr in ((0, 1), (1, 1)):
             DUAL.append((fmt, rc, rr, had))
 
 
@@ -116,13 +151,14 @@ def test_quantize_dual_matches_two_oracle_passes(fp4, orc, fmt, rc, rr, had, sha
         pytest.skip("the dual pass needs both dimensions blocked")
     say("quantize_dual", shape, "fmt", fmt, "rnd", rc, rr, "had", had, "bf16", bf16)
     xh = _mixed(shape, 31 + shape[1], bf16)
-    sc = orc.hadamard_signs(5) if had else 0
-    sr = orc.hadamard_signs(6) if had else 0
-    want_c = orc.quantize(xh, axis=0, fmt=fmt, rnd=rc, seed=21, index_offset=8, had_on=had, had_signs=sc)
-    want_r = orc.quantize(xh, axis=1, fmt=fmt, rnd=rr, seed=22, index_offset=16, had_on=had, had_signs=sr)
+    hc, hr = had
+    sc = orc.hadamard_signs(5) if hc else 0
+    sr = orc.hadamard_signs(6) if hr else 0
+    want_c = orc.quantize(xh, axis=0, fmt=fmt, rnd=rc, seed=21, index_offset=8, had_on=hc, had_signs=sc)
+    want_r = orc.quantize(xh, axis=1, fmt=fmt, rnd=rr, seed=22, index_offset=16, had_on=hr, had_signs=sr)
     qc, qr = fp4.quantize_dual(to_device(xh), fmt=fmt, rnd_cols=rc, seed_cols=21, index_offset_cols=8,
                                rnd_rows=rr, seed_rows=22, index_offset_rows=16,
-                               had_signs_cols=sc if had else None, had_signs_rows=sr if had else None)
+                               had_signs_cols=sc if hc else None, had_signs_rows=sr if hr else None)
     assert_same_quant(q_to_host(qc), want_c, "dual, blocks along C")
     assert_same_quant(q_to_host(qr), want_r, "dual, blocks along R")
 
@@ -203,6 +239,9 @@ FULL = [
     ("llama7b", "W", 1, 0, 1, False),
     ("llama7b", "X", 0, 1, 0, True),
     ("llama7b", "W", 0, 1, 0, True),
+    # NVFP4 wgrad operands rotated 16-wide along the tokens
+    ("llama7b", "dY", 1, 0, 1, True),
+    ("llama7b", "X", 1, 0, 1, True),
     # the large-layer step (hidden 8192, MLP 28672, 16384 tokens)
     ("large", "X", 0, 0, 0, False),
     ("large", "W", 0, 0, 0, False),
