@@ -289,10 +289,50 @@ static float nv_tensor_scale(float amax)
     return amax / 2688.0f;
 }
 
-int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
-               int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
-               int had_on, uint32_t had_signs, int amax_given, float amax_in,
-               uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out)
+static double scale_value(const uint8_t* scales, int64_t i, int fmt);
+
+/* Quantization noise of a quantized tensor (FP4 All the Way, Summary: the
+ * gradient norm set against the quantization noise). x holds the values that
+ * were quantized (after the rotation, when it is on), rows x cols in the
+ * quantized orientation. out[0] = sum x^2, out[1] = sum (xhat - x)^2 with xhat
+ * the exact value the code and scales stand for (e2m1 * sdec * s_g, or
+ * e2m1 * 2^e): every product is exact in FP64 (at most 31 significant bits),
+ * the difference and the sums are FP64 roundings. Rows are summed in order. */
+static void quant_noise(const float* x, const uint8_t* codes, const uint8_t* scales,
+                        int64_t rows, int64_t cols, int fmt, float sg, double out[2])
+{
+    const int B = (fmt == O_FMT_NVFP4) ? 16 : 32;
+    double* part = (double*)calloc((size_t)(2 * rows), sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double g = 0.0, e = 0.0;
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t pos = r * cols + c;
+            unsigned code = (codes[pos >> 1] >> ((pos & 1) * 4)) & 15u;
+            double xhat = o_e2m1_value(code) * scale_value(scales, r * (cols / B) + c / B, fmt);
+            if (fmt == O_FMT_NVFP4) xhat *= (double)sg;
+            double xv = (double)x[pos];
+            double d = xhat - xv;
+            g += xv * xv;
+            e += d * d;
+        }
+        part[2 * r] = g;
+        part[2 * r + 1] = e;
+    }
+    out[0] = 0.0;
+    out[1] = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+        out[0] += part[2 * r];
+        out[1] += part[2 * r + 1];
+    }
+    free(part);
+}
+
+static int quantize_impl(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
+                         int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
+                         int had_on, uint32_t had_signs, int amax_given, float amax_in,
+                         uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out,
+                         double* noise)
 {
     if (!src || !codes || !scales || R <= 0 || C <= 0 || ld < C) return -1;
     if (fmt != O_FMT_NVFP4 && fmt != O_FMT_MXFP4) return -1;
@@ -396,8 +436,29 @@ int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
             }
         }
     }
+    if (noise) quant_noise(t, codes, scales, rows_q, cols_q, fmt, sg, noise);
     free(t);
     return 0;
+}
+
+int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
+               int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
+               int had_on, uint32_t had_signs, int amax_given, float amax_in,
+               uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out)
+{
+    return quantize_impl(src, src_bf16, R, C, ld, axis, fmt, rnd, seed, index_offset, had_on,
+                         had_signs, amax_given, amax_in, codes, scales, amax_out, sg_out, NULL);
+}
+
+int o_quantize_noise(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
+                     int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
+                     int had_on, uint32_t had_signs, int amax_given, float amax_in,
+                     uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out,
+                     double noise[2])
+{
+    if (!noise) return -1;
+    return quantize_impl(src, src_bf16, R, C, ld, axis, fmt, rnd, seed, index_offset, had_on,
+                         had_signs, amax_given, amax_in, codes, scales, amax_out, sg_out, noise);
 }
 
 static double scale_value(const uint8_t* scales, int64_t i, int fmt)

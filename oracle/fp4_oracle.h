@@ -78,6 +78,14 @@ int o_quantize(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
 /* Dequantize to FP32 exactly as the library contract defines it:
  *   NVFP4: (e2m1 * scale) * tensor_scale, the last product rounded once to FP32;
  *   MXFP4: e2m1 * 2^e (exact). */
+/* o_quantize, plus the quantization noise of the result: noise[0] = sum x^2
+ * and noise[1] = sum (xhat - x)^2 over the quantized values x (rotated when
+ * had_on) and the exact values xhat their codes and scales stand for. */
+int o_quantize_noise(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
+                     int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
+                     int had_on, uint32_t had_signs, int amax_given, float amax_in,
+                     uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out,
+                     double noise[2]);
 int o_dequantize_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int fmt, float sg, float* out);
 /* Exact dequantized values in FP64 (e2m1 * scale * tensor_scale is exact in FP64). */

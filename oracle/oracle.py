@@ -78,6 +78,8 @@ def lib():
                                  c.c_int, c.c_uint32, c.c_int, c.c_float,
                                  c.c_void_p, c.c_void_p, c.POINTER(c.c_float),
                                  c.POINTER(c.c_float)]
+        L.o_quantize_noise.restype = c.c_int
+        L.o_quantize_noise.argtypes = L.o_quantize.argtypes + [c.c_void_p]
         L.o_dequantize_f32.restype = c.c_int
         L.o_dequantize_f32.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                        c.c_float, c.c_void_p]
@@ -174,9 +176,11 @@ def tensor_amax(x: np.ndarray) -> float:
 
 def quantize(x: np.ndarray, axis: int = AXIS_COLS, fmt: int = FMT_NVFP4, rnd: int = RTN,
              seed: int = 0, index_offset: int = 0, had_on: bool = False, had_signs: int = 0,
-             amax: float | None = None) -> dict:
+             amax: float | None = None, noise: bool = False) -> dict:
     """Quantize a 2-D float32 (or bf16-bits uint16) matrix. Returns codes, scales
-    (uint8, quantized orientation), and for NVFP4 the tensor amax and scale."""
+    (uint8, quantized orientation), and for NVFP4 the tensor amax and scale.
+    noise: also return "noise" = [sum x^2, sum (xhat - x)^2] (FP64) over the
+    quantized values x and the exact values xhat of their codes."""
     a, bf = _src(x)
     R, C = a.shape
     B = BLOCK[fmt]
@@ -185,10 +189,15 @@ def quantize(x: np.ndarray, axis: int = AXIS_COLS, fmt: int = FMT_NVFP4, rnd: in
     scales = np.zeros((rows_q, cols_q // B), dtype=np.uint8)
     am = ctypes.c_float(0.0)
     sg = ctypes.c_float(1.0)
-    rc = lib().o_quantize(a.ctypes.data, bf, R, C, C, axis, fmt, rnd, seed, index_offset,
-                          int(bool(had_on)), had_signs, int(amax is not None),
-                          float(amax or 0.0), codes.ctypes.data, scales.ctypes.data,
-                          ctypes.byref(am), ctypes.byref(sg))
+    args = (a.ctypes.data, bf, R, C, C, axis, fmt, rnd, seed, index_offset,
+            int(bool(had_on)), had_signs, int(amax is not None),
+            float(amax or 0.0), codes.ctypes.data, scales.ctypes.data,
+            ctypes.byref(am), ctypes.byref(sg))
+    nz = np.zeros(2, dtype=np.float64)
+    if noise:
+        rc = lib().o_quantize_noise(*args, nz.ctypes.data)
+    else:
+        rc = lib().o_quantize(*args)
     if rc != 0:
         raise ValueError(f"oracle quantize rejected its input (rc={rc})")
     out = {"codes": codes, "scales": scales, "fmt": fmt, "rows": rows_q, "cols": cols_q}
@@ -198,6 +207,8 @@ def quantize(x: np.ndarray, axis: int = AXIS_COLS, fmt: int = FMT_NVFP4, rnd: in
     else:
         out["amax"] = None
         out["sg"] = 1.0
+    if noise:
+        out["noise"] = nz
     return out
 
 

@@ -259,3 +259,75 @@ def test_sr_index_offset_shifts_the_stream(orc):
     full = orc.quantize(np.vstack([x, x]), fmt=1, rnd=orc.SR, seed=4)
     second = orc.quantize(x, fmt=1, rnd=orc.SR, seed=4, index_offset=4 * 64)
     assert np.array_equal(full["codes"][4:], second["codes"])
+
+
+# ------------------------------------------------------------ quantization noise
+def test_noise_worked_examples(orc):
+    f = fields("quant_noise_worked.txt")
+    for fmt, key, B in ((1, "mx", 32), (0, "nv", 16)):
+        x = np.zeros((1, B), dtype=np.float32)
+        vals = [float(v) for v in f[f"{key}_x"]]
+        x[0, :len(vals)] = vals
+        q = orc.quantize(x, fmt=fmt, noise=True)
+        assert q["noise"][0] == float(f[f"{key}_g2"][0])
+        assert q["noise"][1] == float(f[f"{key}_e2"][0])
+
+
+def test_noise_zero_tensor_and_grid_values(orc):
+    q = orc.quantize(np.zeros((16, 64), dtype=np.float32), fmt=0, noise=True)
+    assert list(q["noise"]) == [0.0, 0.0]
+    # MXFP4 blocks whose values sit on the grid (amax 6 * 2^k): no noise
+    rng = np.random.default_rng(8)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    x = rng.choice(grid, size=(8, 64)) * rng.choice([-1.0, 1.0], size=(8, 64)).astype(np.float32)
+    x[:, ::32] = 6.0
+    x *= np.float32(2.0 ** -3)
+    q = orc.quantize(x, fmt=1, rnd=1, seed=3, noise=True)
+    assert q["noise"][1] == 0.0
+    assert q["noise"][0] == float(np.sum(x.astype(np.float64) ** 2))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_noise_matches_the_dequantizer(orc, fmt):
+    # The noise sum equals sum (dequantize_f64 - x)^2 taken with numpy from the
+    # separately pinned dequantizer; the signal sum equals numpy's sum of squares.
+    x = _randn((64, 256), 12, outliers=True)
+    for rnd in (0, 1):
+        q = orc.quantize(x, fmt=fmt, rnd=rnd, seed=5, noise=True)
+        x64 = x.astype(np.float64)
+        e2 = float(np.sum((orc.dequantize_f64(q) - x64) ** 2))
+        assert np.isclose(q["noise"][1], e2, rtol=1e-12, atol=0)
+        assert np.isclose(q["noise"][0], float(np.sum(x64 ** 2)), rtol=1e-12, atol=0)
+        assert 0 < q["noise"][1] < q["noise"][0]
+
+
+def test_noise_of_rotated_values_keeps_the_signal_norm(orc):
+    # the rotation is orthonormal: sum y^2 = sum x^2 up to FP32 rounding
+    x = _randn((32, 256), 13, outliers=True)
+    for fmt, signs in ((0, 0xBEEF), (1, 0x12345678)):
+        q = orc.quantize(x, fmt=fmt, had_on=True, had_signs=signs, noise=True)
+        g = float(np.sum(x.astype(np.float64) ** 2))
+        assert abs(q["noise"][0] - g) <= 1e-6 * g
+
+
+def test_sr_noise_has_the_bernoulli_expectation(orc):
+    # MXFP4 with SR: an element a (scaled) between grid neighbours lo < a < hi
+    # rounds up with probability p = (a - lo)/(hi - lo), so its squared error
+    # has mean (hi - a)(a - lo) * s^2 and variance p(1-p)((hi-a)^2-(a-lo)^2)^2 s^4.
+    # Averaged over seeds the oracle's noise sum must match the closed form.
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    x = _randn((4, 64), 14)
+    q0 = orc.quantize(x, fmt=1)
+    s = 2.0 ** (q0["scales"].astype(np.float64) - 127)          # per block
+    sc = np.repeat(s, 32, axis=1)
+    a = np.abs(x.astype(np.float64)) / sc
+    hi_i = np.searchsorted(grid, a, side="left")
+    on = grid[np.minimum(hi_i, 7)] == a
+    lo = grid[np.maximum(hi_i - 1, 0)]
+    hi = grid[np.minimum(hi_i, 7)]
+    mean = np.where(on, 0.0, (hi - a) * (a - lo)) * sc ** 2
+    p = np.where(on, 0.0, (a - lo) / np.where(hi > lo, hi - lo, 1.0))
+    var = p * (1 - p) * (((hi - a) ** 2 - (a - lo) ** 2) * sc ** 2) ** 2
+    n = 400
+    e2 = np.array([orc.quantize(x, fmt=1, rnd=1, seed=1000 + k, noise=True)["noise"][1] for k in range(n)])
+    assert abs(e2.mean() - mean.sum()) <= 4.5 * np.sqrt(var.sum() / n) + 1e-12
