@@ -124,17 +124,23 @@ def make_step(fp4, X, W, dY, signs, separate=False):
 def make_extras(fp4, X, dY, signs16):
     """Adjacent passes timed beside the step (not part of it): the NVFP4
     quantizations of the wgrad operands with the 16-wide random-sign Hadamard
-    along the tokens. With a rotation on one orientation the two orientations
-    have their own tensor amax (the plain one and the rotated one), both taken
-    in one read of the tensor before the dual pass."""
+    along the tokens (with a rotation on one orientation the two orientations
+    have their own tensor amax, the plain one and the rotated one, both taken
+    in one read of the tensor before the dual pass), and dY's dual SR pass with
+    the gradient-noise monitor on both orientations."""
     Q = fp4.QTensor
     NV = fp4.FP4_NVFP4
     COLS, ROWS, RTN, SR = fp4.FP4_AXIS_COLS, fp4.FP4_AXIS_ROWS, fp4.FP4_RTN, fp4.FP4_SR
     seed = lambda role: (2 << 8) | role
+    import torch
+
     q = {
         "X": Q(TOKENS, D_IN, NV), "Xt": Q(D_IN, TOKENS, NV, had_signs=signs16),
         "dY": Q(TOKENS, D_OUT, NV), "dYt": Q(D_OUT, TOKENS, NV, had_signs=signs16),
+        "dYm": Q(TOKENS, D_OUT, NV), "dYmt": Q(D_OUT, TOKENS, NV),
     }
+    q["dYmt"].amax = q["dYm"].amax
+    noise = torch.zeros(4, dtype=torch.float64, device="cuda")
     dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
     ops = [
         ("amax dY had16 tokens", "q", lambda: fp4.fp4_tensor_amax_hadamard16(dY, ROWS, signs16, q["dYt"].amax),
@@ -144,6 +150,10 @@ def make_extras(fp4, X, dY, signs16):
          algorithmic_bytes(TOKENS * D_IN, 2, 16, True, 2)),
         ("quant dY nv dual (sr K, sr+had16 tokens)", "q",
          lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
+         algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
+        ("quant dY nv dual (sr both) + noise monitor on both", "q",
+         lambda: fp4.fp4_quantize_dual_noise(dY, SR, seed(1), 0, SR, seed(2), 0, False, q["dYm"], q["dYmt"],
+                                             noise[0:2], noise[2:4]),
          algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
     ]
     return ops, q

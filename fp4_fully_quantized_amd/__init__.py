@@ -23,7 +23,7 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
-           "fp4_dequantize", "fp4_gemm"]
+           "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_dequantize", "fp4_gemm"]
 
 
 class Fp4Error(RuntimeError):
@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.fp4_quantize_dual.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
                                         c.c_int, c.c_uint64, c.c_uint64, c.c_int, c.c_uint64, c.c_uint64,
                                         c.c_int, c.POINTER(fp4_tensor), c.POINTER(fp4_tensor), c.c_void_p]
+        L.fp4_quantize_noise.restype = c.c_int
+        L.fp4_quantize_noise.argtypes = L.fp4_quantize.argtypes[:-1] + [c.c_void_p, c.c_void_p]
+        L.fp4_quantize_dual_noise.restype = c.c_int
+        L.fp4_quantize_dual_noise.argtypes = L.fp4_quantize_dual.argtypes[:-1] + [c.c_void_p, c.c_void_p,
+                                                                                  c.c_void_p]
         L.fp4_dequantize.restype = c.c_int
         L.fp4_dequantize.argtypes = [c.POINTER(fp4_tensor), c.c_int, c.c_void_p, c.c_int64,
                                      c.c_void_p]
@@ -194,6 +199,46 @@ def fp4_quantize_dual(src, rnd_cols: int, seed_cols: int, index_offset_cols: int
     out_rows.rows, out_rows.cols = dr.rows, dr.cols
 
 
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def fp4_quantize_noise(src, axis: int, rnd: int, seed: int, index_offset: int, amax_ready: bool,
+                       out: QTensor, noise, stream=None) -> None:
+    """fp4_quantize plus noise[0] += sum x^2, noise[1] += sum (xhat - x)^2
+    (noise: a float64 device tensor of 2 elements)."""
+    R, C = src.shape
+    if src.stride(1) != 1:
+        raise ValueError("src must be row-major with unit column stride")
+    d = out.desc()
+    _check(lib().fp4_quantize_noise(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), axis, rnd,
+                                    seed, index_offset, int(bool(amax_ready)), ctypes.byref(d),
+                                    _ptr(noise), _stream(stream)), "fp4_quantize_noise")
+    out.rows, out.cols = d.rows, d.cols
+
+
+def fp4_quantize_dual_noise(src, rnd_cols: int, seed_cols: int, index_offset_cols: int, rnd_rows: int,
+                            seed_rows: int, index_offset_rows: int, amax_ready: bool, out_cols: QTensor,
+                            out_rows: QTensor, noise_cols=None, noise_rows=None, stream=None) -> None:
+    R, C = src.shape
+    if src.stride(1) != 1:
+        raise ValueError("src must be row-major with unit column stride")
+    dc, dr = out_cols.desc(), out_rows.desc()
+    _check(lib().fp4_quantize_dual_noise(src.data_ptr(), _dtype_code(src), R, C, src.stride(0),
+                                         rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
+                                         index_offset_rows, int(bool(amax_ready)), ctypes.byref(dc),
+                                         ctypes.byref(dr), _ptr(noise_cols), _ptr(noise_rows),
+                                         _stream(stream)), "fp4_quantize_dual_noise")
+    out_cols.rows, out_cols.cols = dc.rows, dc.cols
+    out_rows.rows, out_rows.cols = dr.rows, dr.cols
+
+
+def noise_ratio(noise) -> float:
+    """||g|| / ||Q(g) - g|| from a monitor's two sums (host read-out)."""
+    g, e = (float(v) for v in noise.cpu())
+    return float("inf") if e == 0.0 else (g / e) ** 0.5
+
+
 def fp4_dequantize(q: QTensor, dst, stream=None) -> None:
     d = q.desc()
     _check(lib().fp4_dequantize(ctypes.byref(d), _dtype_code(dst), dst.data_ptr(), dst.stride(0),
@@ -209,9 +254,10 @@ def fp4_gemm(A: QTensor, B: QTensor, C, stream=None) -> None:
 # ---------------------------------------------------------------- conveniences
 def quantize(src, axis: int = FP4_AXIS_COLS, fmt: int = FP4_NVFP4, rnd: int = FP4_RTN,
              seed: int = 0, index_offset: int = 0, had_signs: int | None = None,
-             amax_from: QTensor | None = None, stream=None) -> QTensor:
+             amax_from: QTensor | None = None, noise=None, stream=None) -> QTensor:
     """Allocate a QTensor and quantize src into it. `amax_from`: reuse the
-    tensor amax already computed for the same tensor (NVFP4)."""
+    tensor amax already computed for the same tensor (NVFP4). `noise`: a float64
+    device tensor of 2 elements that the quantization noise sums are added to."""
     R, C = src.shape
     rows, cols = (C, R) if axis == FP4_AXIS_ROWS else (R, C)
     q = QTensor(rows, cols, fmt, device=src.device, had_signs=had_signs)
@@ -219,14 +265,18 @@ def quantize(src, axis: int = FP4_AXIS_COLS, fmt: int = FP4_NVFP4, rnd: int = FP
     if amax_from is not None and fmt == FP4_NVFP4:
         q.amax = amax_from.amax
         ready = True
-    fp4_quantize(src, axis, rnd, seed, index_offset, ready, q, stream)
+    if noise is None:
+        fp4_quantize(src, axis, rnd, seed, index_offset, ready, q, stream)
+    else:
+        fp4_quantize_noise(src, axis, rnd, seed, index_offset, ready, q, noise, stream)
     return q
 
 
 def quantize_dual(src, fmt: int = FP4_NVFP4, rnd_cols: int = FP4_RTN, seed_cols: int = 0,
                   index_offset_cols: int = 0, rnd_rows: int = FP4_SR, seed_rows: int = 0,
                   index_offset_rows: int = 0, had_signs_cols: int | None = None,
-                  had_signs_rows: int | None = None, amax_from: QTensor | None = None, stream=None):
+                  had_signs_rows: int | None = None, amax_from: QTensor | None = None,
+                  noise_cols=None, noise_rows=None, stream=None):
     """Allocate both QTensors and quantize src along C and along R in one
     read. Returns (q_cols [R, C], q_rows [C, R]). NVFP4 without rotation: they
     share the tensor amax (`amax_from`: a QTensor whose amax to reuse). NVFP4
@@ -245,8 +295,12 @@ def quantize_dual(src, fmt: int = FP4_NVFP4, rnd_cols: int = FP4_RTN, seed_cols:
         ready = True
     if fmt == FP4_NVFP4 and not two:
         qr.amax = qc.amax
-    fp4_quantize_dual(src, rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
-                      index_offset_rows, ready, qc, qr, stream)
+    if noise_cols is None and noise_rows is None:
+        fp4_quantize_dual(src, rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
+                          index_offset_rows, ready, qc, qr, stream)
+    else:
+        fp4_quantize_dual_noise(src, rnd_cols, seed_cols, index_offset_cols, rnd_rows, seed_rows,
+                                index_offset_rows, ready, qc, qr, noise_cols, noise_rows, stream)
     return qc, qr
 
 

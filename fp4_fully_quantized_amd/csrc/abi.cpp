@@ -33,6 +33,138 @@ fp4_status check_matrix(const void* src, int dt, int64_t R, int64_t C, int64_t l
   return FP4_OK;
 }
 
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                         int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream) {
+  if (!out) return FP4_ERR_NULL;
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
+  if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ARG;
+  if (!valid_fmt(out->fmt)) return FP4_ERR_ARG;
+  if (!out->codes || !out->scales) return FP4_ERR_NULL;
+  if (!aligned16(out->codes) || !aligned16(out->scales)) return FP4_ERR_ALIGN;
+  const bool nv = out->fmt == FP4_NVFP4;
+  if (nv && (!out->amax || !out->tscale)) return FP4_ERR_NULL;
+  const int B = block_of(out->fmt);
+  const int64_t blocked = axis == FP4_AXIS_ROWS ? R : C;
+  if (blocked % B != 0) return FP4_ERR_SHAPE;
+  if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
+  if (axis == FP4_AXIS_ROWS && (R + 255) / 256 * ((C + 63) / 64) > 0x7FFFFFFF)
+    return FP4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nv && !amax_ready) {
+    if (out->had_on)
+      fp4i_launch_amax_rot16(src, src_t == FP4_DTYPE_BF16, R, C, ld, axis == FP4_AXIS_ROWS,
+                             out->had_signs, out->amax, s);
+    else
+      fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
+    st = hip_status();
+    if (st != FP4_OK) return st;
+  }
+  QuantArgs a;
+  a.src = src;
+  a.bf16 = src_t == FP4_DTYPE_BF16;
+  a.R = R;
+  a.C = C;
+  a.ld = ld;
+  a.rows_axis = axis == FP4_AXIS_ROWS;
+  a.fmt = out->fmt;
+  a.sr = rnd == FP4_SR;
+  a.seed = seed;
+  a.offset = index_offset;
+  a.had_on = out->had_on != 0;
+  a.signs = out->had_signs;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.amax = out->amax;
+  a.tscale = out->tscale;
+  a.noise = noise;
+  fp4i_launch_quant(a, s);
+  out->rows = a.rows_axis ? C : R;
+  out->cols = a.rows_axis ? R : C;
+  return hip_status();
+}
+
+fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                              fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
+                              fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
+                              int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
+                              double* noise_cols, double* noise_rows, fp4_stream_t stream) {
+  if (!out_cols || !out_rows) return FP4_ERR_NULL;
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if ((rnd_cols != FP4_RTN && rnd_cols != FP4_SR) || (rnd_rows != FP4_RTN && rnd_rows != FP4_SR))
+    return FP4_ERR_ARG;
+  if (!valid_fmt(out_cols->fmt) || !valid_fmt(out_rows->fmt)) return FP4_ERR_ARG;
+  if (out_cols->fmt != out_rows->fmt) return FP4_ERR_UNSUPPORTED;
+  for (const fp4_tensor* o : {out_cols, out_rows}) {
+    if (!o->codes || !o->scales) return FP4_ERR_NULL;
+    if (!aligned16(o->codes) || !aligned16(o->scales)) return FP4_ERR_ALIGN;
+  }
+  const bool nv = out_cols->fmt == FP4_NVFP4;
+  const bool had_c = out_cols->had_on != 0, had_r = out_rows->had_on != 0;
+  // NVFP4 with a rotation: the two orientations' values have different amaxes,
+  // each kept in its own descriptor.
+  const bool two_amax = nv && (had_c || had_r);
+  if (nv && (!out_cols->amax || !out_cols->tscale || !out_rows->tscale)) return FP4_ERR_NULL;
+  if (two_amax && !out_rows->amax) return FP4_ERR_NULL;
+  if (two_amax && out_rows->amax == out_cols->amax) return FP4_ERR_UNSUPPORTED;
+  const int B = block_of(out_cols->fmt);
+  if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
+  if ((rnd_cols == FP4_SR && index_offset_cols % 8 != 0) || (rnd_rows == FP4_SR && index_offset_rows % 8 != 0))
+    return FP4_ERR_ALIGN;
+  if ((R + 127) / 128 * ((C + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nv && !amax_ready) {
+    const bool bf = src_t == FP4_DTYPE_BF16;
+    if (two_amax)
+      fp4i_launch_amax_pair(src, bf, R, C, ld, had_c, out_cols->had_signs, had_r, out_rows->had_signs,
+                            out_cols->amax, out_rows->amax, s);
+    else
+      fp4i_launch_amax(src, bf, R, C, ld, out_cols->amax, s);
+    st = hip_status();
+    if (st != FP4_OK) return st;
+  }
+  DualArgs a;
+  a.src = src;
+  a.bf16 = src_t == FP4_DTYPE_BF16;
+  a.R = R;
+  a.C = C;
+  a.ld = ld;
+  a.fmt = out_cols->fmt;
+  a.had_c = had_c;
+  a.had_r = had_r;
+  a.sr_c = rnd_cols == FP4_SR;
+  a.sr_r = rnd_rows == FP4_SR;
+  a.seed_c = seed_cols;
+  a.offset_c = index_offset_cols;
+  a.seed_r = seed_rows;
+  a.offset_r = index_offset_rows;
+  a.signs_c = out_cols->had_signs;
+  a.signs_r = out_rows->had_signs;
+  a.codes_c = out_cols->codes;
+  a.scales_c = out_cols->scales;
+  a.codes_r = out_rows->codes;
+  a.scales_r = out_rows->scales;
+  a.amax_c = out_cols->amax;
+  a.amax_r = two_amax ? out_rows->amax : out_cols->amax;
+  a.tscale_c = out_cols->tscale;
+  a.tscale_r = out_rows->tscale;
+  a.amax_copy = (nv && !two_amax && out_rows->amax && out_rows->amax != out_cols->amax)
+                    ? out_rows->amax : nullptr;
+  a.noise_c = noise_cols;
+  a.noise_r = noise_rows;
+  fp4i_launch_quant_dual(a, s);
+  out_cols->rows = R;
+  out_cols->cols = C;
+  out_rows->rows = C;
+  out_rows->cols = R;
+  return hip_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,53 +236,17 @@ fp4_status fp4_tensor_amax_hadamard16(const void* src, fp4_dtype src_t, int64_t 
 fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream) {
-  if (!out) return FP4_ERR_NULL;
-  fp4_status st = check_matrix(src, src_t, R, C, ld);
-  if (st != FP4_OK) return st;
-  if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
-  if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ARG;
-  if (!valid_fmt(out->fmt)) return FP4_ERR_ARG;
-  if (!out->codes || !out->scales) return FP4_ERR_NULL;
-  if (!aligned16(out->codes) || !aligned16(out->scales)) return FP4_ERR_ALIGN;
-  const bool nv = out->fmt == FP4_NVFP4;
-  if (nv && (!out->amax || !out->tscale)) return FP4_ERR_NULL;
-  const int B = block_of(out->fmt);
-  const int64_t blocked = axis == FP4_AXIS_ROWS ? R : C;
-  if (blocked % B != 0) return FP4_ERR_SHAPE;
-  if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
-  if (axis == FP4_AXIS_ROWS && (R + 255) / 256 * ((C + 63) / 64) > 0x7FFFFFFF)
-    return FP4_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (nv && !amax_ready) {
-    if (out->had_on)
-      fp4i_launch_amax_rot16(src, src_t == FP4_DTYPE_BF16, R, C, ld, axis == FP4_AXIS_ROWS,
-                             out->had_signs, out->amax, s);
-    else
-      fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
-    st = hip_status();
-    if (st != FP4_OK) return st;
-  }
-  QuantArgs a;
-  a.src = src;
-  a.bf16 = src_t == FP4_DTYPE_BF16;
-  a.R = R;
-  a.C = C;
-  a.ld = ld;
-  a.rows_axis = axis == FP4_AXIS_ROWS;
-  a.fmt = out->fmt;
-  a.sr = rnd == FP4_SR;
-  a.seed = seed;
-  a.offset = index_offset;
-  a.had_on = out->had_on != 0;
-  a.signs = out->had_signs;
-  a.codes = out->codes;
-  a.scales = out->scales;
-  a.amax = out->amax;
-  a.tscale = out->tscale;
-  fp4i_launch_quant(a, s);
-  out->rows = a.rows_axis ? C : R;
-  out->cols = a.rows_axis ? R : C;
-  return hip_status();
+  return quantize_impl(src, src_t, R, C, ld, axis, rnd, seed, index_offset, amax_ready, out, nullptr,
+                       stream);
+}
+
+fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                              fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                              int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream) {
+  if (!noise) return FP4_ERR_NULL;
+  if (!aligned8(noise)) return FP4_ERR_ALIGN;
+  return quantize_impl(src, src_t, R, C, ld, axis, rnd, seed, index_offset, amax_ready, out, noise,
+                       stream);
 }
 
 fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
@@ -158,74 +254,21 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
                              fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
                              int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
                              fp4_stream_t stream) {
-  if (!out_cols || !out_rows) return FP4_ERR_NULL;
-  fp4_status st = check_matrix(src, src_t, R, C, ld);
-  if (st != FP4_OK) return st;
-  if ((rnd_cols != FP4_RTN && rnd_cols != FP4_SR) || (rnd_rows != FP4_RTN && rnd_rows != FP4_SR))
-    return FP4_ERR_ARG;
-  if (!valid_fmt(out_cols->fmt) || !valid_fmt(out_rows->fmt)) return FP4_ERR_ARG;
-  if (out_cols->fmt != out_rows->fmt) return FP4_ERR_UNSUPPORTED;
-  for (const fp4_tensor* o : {out_cols, out_rows}) {
-    if (!o->codes || !o->scales) return FP4_ERR_NULL;
-    if (!aligned16(o->codes) || !aligned16(o->scales)) return FP4_ERR_ALIGN;
-  }
-  const bool nv = out_cols->fmt == FP4_NVFP4;
-  const bool had_c = out_cols->had_on != 0, had_r = out_rows->had_on != 0;
-  // NVFP4 with a rotation: the two orientations' values have different amaxes,
-  // each kept in its own descriptor.
-  const bool two_amax = nv && (had_c || had_r);
-  if (nv && (!out_cols->amax || !out_cols->tscale || !out_rows->tscale)) return FP4_ERR_NULL;
-  if (two_amax && !out_rows->amax) return FP4_ERR_NULL;
-  if (two_amax && out_rows->amax == out_cols->amax) return FP4_ERR_UNSUPPORTED;
-  const int B = block_of(out_cols->fmt);
-  if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
-  if ((rnd_cols == FP4_SR && index_offset_cols % 8 != 0) || (rnd_rows == FP4_SR && index_offset_rows % 8 != 0))
-    return FP4_ERR_ALIGN;
-  if ((R + 127) / 128 * ((C + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (nv && !amax_ready) {
-    const bool bf = src_t == FP4_DTYPE_BF16;
-    if (two_amax)
-      fp4i_launch_amax_pair(src, bf, R, C, ld, had_c, out_cols->had_signs, had_r, out_rows->had_signs,
-                            out_cols->amax, out_rows->amax, s);
-    else
-      fp4i_launch_amax(src, bf, R, C, ld, out_cols->amax, s);
-    st = hip_status();
-    if (st != FP4_OK) return st;
-  }
-  DualArgs a;
-  a.src = src;
-  a.bf16 = src_t == FP4_DTYPE_BF16;
-  a.R = R;
-  a.C = C;
-  a.ld = ld;
-  a.fmt = out_cols->fmt;
-  a.had_c = had_c;
-  a.had_r = had_r;
-  a.sr_c = rnd_cols == FP4_SR;
-  a.sr_r = rnd_rows == FP4_SR;
-  a.seed_c = seed_cols;
-  a.offset_c = index_offset_cols;
-  a.seed_r = seed_rows;
-  a.offset_r = index_offset_rows;
-  a.signs_c = out_cols->had_signs;
-  a.signs_r = out_rows->had_signs;
-  a.codes_c = out_cols->codes;
-  a.scales_c = out_cols->scales;
-  a.codes_r = out_rows->codes;
-  a.scales_r = out_rows->scales;
-  a.amax_c = out_cols->amax;
-  a.amax_r = two_amax ? out_rows->amax : out_cols->amax;
-  a.tscale_c = out_cols->tscale;
-  a.tscale_r = out_rows->tscale;
-  a.amax_copy = (nv && !two_amax && out_rows->amax && out_rows->amax != out_cols->amax)
-                    ? out_rows->amax : nullptr;
-  fp4i_launch_quant_dual(a, s);
-  out_cols->rows = R;
-  out_cols->cols = C;
-  out_rows->rows = C;
-  out_rows->cols = R;
-  return hip_status();
+  return quantize_dual_impl(src, src_t, R, C, ld, rnd_cols, seed_cols, index_offset_cols, rnd_rows,
+                            seed_rows, index_offset_rows, amax_ready, out_cols, out_rows, nullptr,
+                            nullptr, stream);
+}
+
+fp4_status fp4_quantize_dual_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                                   fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
+                                   fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
+                                   int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
+                                   double* noise_cols, double* noise_rows, fp4_stream_t stream) {
+  if (!noise_cols && !noise_rows) return FP4_ERR_NULL;
+  if (!aligned8(noise_cols) || !aligned8(noise_rows)) return FP4_ERR_ALIGN;
+  return quantize_dual_impl(src, src_t, R, C, ld, rnd_cols, seed_cols, index_offset_cols, rnd_rows,
+                            seed_rows, index_offset_rows, amax_ready, out_cols, out_rows, noise_cols,
+                            noise_rows, stream);
 }
 
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,

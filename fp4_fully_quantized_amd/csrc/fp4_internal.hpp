@@ -18,6 +18,7 @@ struct QuantArgs {
   uint8_t* scales;
   const float* amax;     // NVFP4: device tensor amax (already computed)
   float* tscale;         // NVFP4: receives s_g
+  double* noise;         // null, or receives += (sum x^2, sum (xhat - x)^2)
 };
 
 // Both orientations of one source (fp4_quantize_dual): *_c blocks along C,
@@ -36,6 +37,7 @@ struct DualArgs {
   const float* amax_r;             //   (already computed; the same pointer when equal)
   float *tscale_c, *tscale_r;      // NVFP4: receive s_g of each orientation
   float* amax_copy;                // NVFP4: receives a copy of *amax_c, or null
+  double *noise_c, *noise_r;       // null, or receive += (sum x^2, sum (xhat - x)^2)
 };
 
 struct GemmArgs {

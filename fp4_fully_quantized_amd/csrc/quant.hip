@@ -151,16 +151,18 @@ __global__ __launch_bounds__(256) void k_amax_rot_rows(const void* __restrict__ 
 }
 
 
-template <int FMT, int RND, bool BF16, bool HAD>
+template <int FMT, int RND, bool BF16, bool HAD, bool MON>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t C, int64_t ld,
                                                      uint32_t spr, uint32_t ntasks,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
                                                      const float* __restrict__ amax, float* tscale,
-                                                     uint64_t seed, uint64_t offset, uint32_t signs) {
+                                                     uint64_t seed, uint64_t offset, uint32_t signs,
+                                                     double* noise) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
   const int lane = threadIdx.x & 63;
+  double ng = 0.0, ne = 0.0;
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
   const uint32_t nwaves = gridDim.x * 4u;
   float sg = 1.0f;
@@ -221,7 +223,14 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
       *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (C / 2) + col / 2) = w;
       if ((lane & (B / 8 - 1)) == 0) scales[(int64_t)r * (C / B) + col / B] = (uint8_t)sbyte;
     }
+    if constexpr (MON) {
+      float g = 0.0f, e = 0.0f;
+      noise8<FMT>(x, w, scale_value<FMT>(sbyte), sg, g, e);
+      ng += (double)g;
+      ne += (double)e;
+    }
   }
+  if constexpr (MON) noise_reduce(ng, ne, noise);
 }
 
 
@@ -236,14 +245,14 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
 //     16 rows, MXFP4: 2 columns of 32 rows);
 //  3. codes and scale bytes are staged in LDS per output row (= input
 //     column) and written out in whole 128-byte lines.
-template <int FMT, int RND, bool BF16, bool HAD>
+template <int FMT, int RND, bool BF16, bool HAD, bool MON>
 __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src, int64_t R, int64_t C,
-                                                     int64_t ld, uint32_t tiles_c,
+                                                     int64_t ld, uint32_t tiles_c, uint32_t ntiles,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
                                                      const float* __restrict__ amax, float* tscale,
                                                      uint64_t seed, uint64_t offset, uint32_t signs,
-                                                     uint32_t scale_words) {
+                                                     uint32_t scale_words, double* noise) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
   constexpr int TR = 256, TC = 64;
@@ -264,116 +273,132 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
     sg = nv_tensor_scale(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
   }
-  const uint32_t tr = blockIdx.x / tiles_c;
-  const uint32_t tc = blockIdx.x - tr * tiles_c;
-  const int64_t r0 = (int64_t)tr * TR;
-  const int64_t c0 = (int64_t)tc * TC;
-  const int tid = threadIdx.x;
+  double ng = 0.0, ne = 0.0;  // quantization noise, when asked for
+  // One tile per workgroup; with the noise monitor (MON) a capped grid loops
+  // over the tiles.
+  const uint32_t n_it = MON ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 1u;
+  for (uint32_t it = 0; it < n_it; ++it) {
+    const uint32_t ti = blockIdx.x + it * gridDim.x;
+    const uint32_t tr = ti / tiles_c;
+    const uint32_t tc = ti - tr * tiles_c;
+    const int64_t r0 = (int64_t)tr * TR;
+    const int64_t c0 = (int64_t)tc * TC;
+    const int tid = threadIdx.x;
 
-  // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load.
-  constexpr int CPR = TC * ES / 16;
+    // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load.
+    constexpr int CPR = TC * ES / 16;
 #pragma unroll
-  for (int k = 0; k < TR * CPR / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int rr = idx / CPR;
-    const int cc = idx % CPR;
-    const int64_t col = c0 + cc * (16 / ES);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < R && col < C)
-      v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-  __syncthreads();
+    for (int k = 0; k < TR * CPR / 256; ++k) {
+      const int idx = k * 256 + tid;
+      const int rr = idx / CPR;
+      const int cc = idx % CPR;
+      const int64_t col = c0 + cc * (16 / ES);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r0 + rr < R && col < C)
+        v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
+      uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
 
-  // 2. quantize NCOL blocks per thread.
-  const int b = tid / TPB;
-  const int cl0 = (tid % TPB) * NCOL;
-  const int64_t rg = r0 + (int64_t)b * B;
-  float x[NCOL][B];
+    // 2. quantize NCOL blocks per thread.
+    const int b = tid / TPB;
+    const int cl0 = (tid % TPB) * NCOL;
+    const int64_t rg = r0 + (int64_t)b * B;
+    float x[NCOL][B];
 #pragma unroll
-  for (int i = 0; i < B; ++i) {
-    const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
-    if constexpr (BF16) {
-      if constexpr (NCOL == 4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(p);
-        x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
+    for (int i = 0; i < B; ++i) {
+      const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
+      if constexpr (BF16) {
+        if constexpr (NCOL == 4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(p);
+          x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+          x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
+        }
       } else {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-        x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
+        if constexpr (NCOL == 4) {
+          const float4 w = *reinterpret_cast<const float4*>(p);
+          x[0][i] = w.x; x[1][i] = w.y; x[2][i] = w.z; x[3][i] = w.w;
+        } else {
+          const float2 w = *reinterpret_cast<const float2*>(p);
+          x[0][i] = w.x; x[1][i] = w.y;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NCOL; ++k) {
+      const int cl = cl0 + k;
+      const int64_t cg = c0 + cl;
+      float* xk = x[k];
+      if constexpr (HAD) hadamard_block<B>(xk, signs);
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
+      float rcp;
+      const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+      uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
+      float bg = 0.0f, be = 0.0f;
+      const float bs = MON ? scale_value<FMT>(sbyte) : 0.0f;
+#pragma unroll
+      for (int g = 0; g < B / 8; ++g) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
+        uint32_t cw;
+        if constexpr (RND == 0) {
+          cw = e2m1_rtn_pack8(v);
+        } else {
+          uint32_t h[4];
+          sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+          cw = e2m1_sr_pack8(v, h);
+        }
+        sc[g] = cw;
+        if constexpr (MON) noise8<FMT>(xk + 8 * g, cw, bs, sg, bg, be);
+      }
+      stage_s[cl * NB + b] = (uint8_t)sbyte;
+      ng += (double)bg;
+      ne += (double)be;
+    }
+    __syncthreads();
+
+    // 3. write out: output row c0 + cl gets the codes of input rows r0 .. (8-byte
+    // pieces, 16 per row) and the scale bytes of its NB blocks.
+    const int64_t rows_here = R - r0 < TR ? R - r0 : TR;  // a multiple of B
+#pragma unroll
+    for (int k = 0; k < TC * 16 / 256; ++k) {
+      const int idx = k * 256 + tid;
+      const int cl = idx / 16;
+      const int seg = idx % 16;
+      if (c0 + cl < C && seg * 16 < rows_here) {
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
+        *reinterpret_cast<uint2*>(codes + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
+      }
+    }
+    if (scale_words) {
+      // (R / B) % 4 == 0: one 4-byte word per thread covers 4 blocks of a row.
+      constexpr int WPR = NB / 4;
+      if (tid < TC * WPR) {
+        const int cl = tid / WPR;
+        const int wd = tid % WPR;
+        if (c0 + cl < C && wd * 4 * B < rows_here)
+          *reinterpret_cast<uint32_t*>(scales + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
+              *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
       }
     } else {
-      if constexpr (NCOL == 4) {
-        const float4 w = *reinterpret_cast<const float4*>(p);
-        x[0][i] = w.x; x[1][i] = w.y; x[2][i] = w.z; x[3][i] = w.w;
-      } else {
-        const float2 w = *reinterpret_cast<const float2*>(p);
-        x[0][i] = w.x; x[1][i] = w.y;
+#pragma unroll
+      for (int k = 0; k < (TC * NB + 255) / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int cl = idx / NB;
+        const int bb = idx % NB;
+        if (idx < TC * NB && c0 + cl < C && bb * B < rows_here)
+          scales[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
       }
     }
+    if constexpr (MON) __syncthreads();  // the next tile reuses the LDS buffers
   }
-#pragma unroll
-  for (int k = 0; k < NCOL; ++k) {
-    const int cl = cl0 + k;
-    const int64_t cg = c0 + cl;
-    float* xk = x[k];
-    if constexpr (HAD) hadamard_block<B>(xk, signs);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
-    float rcp;
-    const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
-    uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
-#pragma unroll
-    for (int g = 0; g < B / 8; ++g) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
-      if constexpr (RND == 0) {
-        sc[g] = e2m1_rtn_pack8(v);
-      } else {
-        uint32_t h[4];
-        sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
-        sc[g] = e2m1_sr_pack8(v, h);
-      }
-    }
-    stage_s[cl * NB + b] = (uint8_t)sbyte;
-  }
-  __syncthreads();
-
-  // 3. write out: output row c0 + cl gets the codes of input rows r0 .. (8-byte
-  // pieces, 16 per row) and the scale bytes of its NB blocks.
-  const int64_t rows_here = R - r0 < TR ? R - r0 : TR;  // a multiple of B
-#pragma unroll
-  for (int k = 0; k < TC * 16 / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int cl = idx / 16;
-    const int seg = idx % 16;
-    if (c0 + cl < C && seg * 16 < rows_here) {
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
-      *reinterpret_cast<uint2*>(codes + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
-    }
-  }
-  if (scale_words) {
-    // (R / B) % 4 == 0: one 4-byte word per thread covers 4 blocks of a row.
-    constexpr int WPR = NB / 4;
-    if (tid < TC * WPR) {
-      const int cl = tid / WPR;
-      const int wd = tid % WPR;
-      if (c0 + cl < C && wd * 4 * B < rows_here)
-        *reinterpret_cast<uint32_t*>(scales + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
-            *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < (TC * NB + 255) / 256; ++k) {
-      const int idx = k * 256 + tid;
-      const int cl = idx / NB;
-      const int bb = idx % NB;
-      if (idx < TC * NB && c0 + cl < C && bb * B < rows_here)
-        scales[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
-    }
-  }
+  if constexpr (MON) noise_reduce(ng, ne, noise);
 }
 
 // Both orientations' tensor amaxes from one read, for a dual quantization with
@@ -503,20 +528,35 @@ template <int FMT, int RND, bool BF16, bool HAD>
 void launch_cols(const QuantArgs& a, hipStream_t s) {
   const uint32_t spr = (uint32_t)((a.C + 511) / 512);
   const uint32_t ntasks = (uint32_t)(a.R * spr);
-  hipLaunchKernelGGL((k_quant_cols<FMT, RND, BF16, HAD>), dim3(strided_grid(ntasks)), dim3(256), 0, s,
-                     a.src, a.C, a.ld, spr, ntasks, a.codes, a.scales, a.amax, a.tscale, a.seed,
-                     a.offset, a.signs);
+  uint32_t grid = strided_grid(ntasks);
+  if (a.noise && grid > kNoiseGrid) grid = kNoiseGrid;
+  if (a.noise)
+    hipLaunchKernelGGL((k_quant_cols<FMT, RND, BF16, HAD, true>), dim3(grid), dim3(256), 0, s,
+                       a.src, a.C, a.ld, spr, ntasks, a.codes, a.scales, a.amax, a.tscale, a.seed,
+                       a.offset, a.signs, a.noise);
+  else
+    hipLaunchKernelGGL((k_quant_cols<FMT, RND, BF16, HAD, false>), dim3(grid), dim3(256), 0, s,
+                       a.src, a.C, a.ld, spr, ntasks, a.codes, a.scales, a.amax, a.tscale, a.seed,
+                       a.offset, a.signs, nullptr);
 }
 
-template <int FMT, int RND, bool BF16, bool HAD>
-void launch_rows(const QuantArgs& a, hipStream_t s) {
+template <int FMT, int RND, bool BF16, bool HAD, bool MON>
+void launch_rows_mon(const QuantArgs& a, hipStream_t s) {
   constexpr int B = FMT == NV ? 16 : 32;
   const uint32_t tiles_c = (uint32_t)((a.C + 63) / 64);
   const uint32_t tiles_r = (uint32_t)((a.R + 255) / 256);
   const uint32_t scale_words = (a.R / B) % 4 == 0;
-  hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD>), dim3(tiles_c * tiles_r), dim3(256), 0, s,
-                     a.src, a.R, a.C, a.ld, tiles_c, a.codes, a.scales, a.amax, a.tscale, a.seed,
-                     a.offset, a.signs, scale_words);
+  const uint32_t ntiles = tiles_c * tiles_r;
+  const uint32_t grid = MON && ntiles > kNoiseGrid ? kNoiseGrid : ntiles;
+  hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD, MON>), dim3(grid), dim3(256), 0, s, a.src, a.R,
+                     a.C, a.ld, tiles_c, ntiles, a.codes, a.scales, a.amax, a.tscale, a.seed, a.offset,
+                     a.signs, scale_words, a.noise);
+}
+
+template <int FMT, int RND, bool BF16, bool HAD>
+void launch_rows(const QuantArgs& a, hipStream_t s) {
+  if (a.noise) launch_rows_mon<FMT, RND, BF16, HAD, true>(a, s);
+  else launch_rows_mon<FMT, RND, BF16, HAD, false>(a, s);
 }
 
 template <int FMT, int RND, bool BF16, bool HAD>

@@ -71,4 +71,62 @@ __device__ __forceinline__ void hadamard_block(float x[B], uint32_t signs) {
   for (int i = 0; i < B; ++i) x[i] = x[i] * c;
 }
 
+// ---- quantization noise (the gradient-noise monitor) ----------------------
+// The value a block's scale byte stands for: E4M3 (NVFP4) or 2^(byte - 127).
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t byte) {
+  if constexpr (FMT == NV) return e4m3_decode(byte);
+  else return __builtin_ldexpf(1.0f, (int)byte - 127);
+}
+
+// Adds sum x^2 and sum (xhat - x)^2 of 8 quantized values to g and e (FP32):
+// xhat = e2m1 * bs (* sg for NVFP4) is the value of code nibble i of w; the
+// code-scale product is exact, the difference is rounded once (one fma for
+// NVFP4), the squares accumulate by fma.
+template <int FMT>
+__device__ __forceinline__ void noise8(const float x[8], uint32_t w, float bs, float sg, float& g,
+                                       float& e) {
+  float q[8];
+  {
+    const auto q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    q[0] = q0[0]; q[1] = q0[1]; q[2] = q1[0]; q[3] = q1[1];
+    q[4] = q2[0]; q[5] = q2[1]; q[6] = q3[0]; q[7] = q3[1];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float qs = q[i] * bs;
+    const float d = (FMT == NV) ? __builtin_fmaf(qs, sg, -x[i]) : qs - x[i];
+    e = __builtin_fmaf(d, d, e);
+    g = __builtin_fmaf(x[i], x[i], g);
+  }
+}
+
+// Launches with the noise monitor cap their grid at this many workgroups
+// (each then loops over several tiles or tasks): every workgroup ends with two
+// FP64 atomic adds per sum pair on the same two addresses, which serialize.
+constexpr uint32_t kNoiseGrid = 1024;
+
+// Workgroup sum of (g, e), then out[0] += g, out[1] += e. Every thread of the
+// workgroup calls it (it synchronizes).
+__device__ __forceinline__ void noise_reduce(double g, double e, double* out) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    g += __shfl_xor(g, off, 64);
+    e += __shfl_xor(e, off, 64);
+  }
+  __shared__ double part[4][2];
+  if ((threadIdx.x & 63) == 0) {
+    part[threadIdx.x >> 6][0] = g;
+    part[threadIdx.x >> 6][1] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(out, (part[0][0] + part[1][0]) + (part[2][0] + part[3][0]));
+    atomicAdd(out + 1, (part[0][1] + part[1][1]) + (part[2][1] + part[3][1]));
+  }
+}
+
 }  // namespace fp4q

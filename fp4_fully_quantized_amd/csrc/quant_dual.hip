@@ -21,15 +21,16 @@ namespace {
 // Each orientation has its own rounding mode, SR stream, rotation (on or off,
 // and its mask) and, for NVFP4, tensor amax (the rotated values' amax differs
 // per rotation axis); the results equal the two separate passes bit for bit.
-template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR>
+template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
 __global__ __launch_bounds__(256) void k_quant_dual(
-    const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c,
+    const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
     uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
     const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
     float* tscale_r, float* amax_copy,
     uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
-    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r) {
+    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    double* noise_r) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
   constexpr int T = 128;                  // tile rows = tile columns
@@ -54,184 +55,210 @@ __global__ __launch_bounds__(256) void k_quant_dual(
       if (amax_copy) *amax_copy = ac;
     }
   }
-  const uint32_t tr = blockIdx.x / tiles_c;
-  const uint32_t tc = blockIdx.x - tr * tiles_c;
-  const int64_t r0 = (int64_t)tr * T;
-  const int64_t c0 = (int64_t)tc * T;
-  const int tid = threadIdx.x;
+  double ngc = 0.0, nec = 0.0, ngr = 0.0, ner = 0.0;  // quantization noise, when asked for
+  // One tile per workgroup; with the noise monitor (MON) a capped grid loops
+  // over the tiles.
+  const uint32_t n_it = MON ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 1u;
+  for (uint32_t it = 0; it < n_it; ++it) {
+    const uint32_t ti = blockIdx.x + it * gridDim.x;
+    const uint32_t tr = ti / tiles_c;
+    const uint32_t tc = ti - tr * tiles_c;
+    const int64_t r0 = (int64_t)tr * T;
+    const int64_t c0 = (int64_t)tc * T;
+    const int tid = threadIdx.x;
 
-  // 1. tile load, 16 bytes per load.
-  constexpr int CPR = T * ES / 16;
+    // 1. tile load, 16 bytes per load.
+    constexpr int CPR = T * ES / 16;
 #pragma unroll
-  for (int k = 0; k < T * CPR / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int rr = idx / CPR;
-    const int cc = idx % CPR;
-    const int64_t col = c0 + cc * (16 / ES);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < R && col < C)
-      v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-    uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
-    d[0] = make_uint2(v.x, v.y);
-    d[1] = make_uint2(v.z, v.w);
-  }
-  __syncthreads();
-
-  const int64_t rows_here = R - r0 < T ? R - r0 : T;  // multiples of B
-  const int64_t cols_here = C - c0 < T ? C - c0 : T;
-
-  // (a) blocks down the columns: output row c0 + cl, elements r0 ..
-  {
-    const int b = tid / TPB;
-    const int cl0 = (tid % TPB) * NCOL;
-    const int64_t rg = r0 + (int64_t)b * B;
-    float x[NCOL][B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
-      if constexpr (BF16) {
-        if constexpr (NCOL == 4) {
-          const uint2 w = *reinterpret_cast<const uint2*>(p);
-          x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
-        } else {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-          x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < NCOL; k += 2) {
-          const float2 w = *reinterpret_cast<const float2*>(p + 4 * k);
-          x[k][i] = w.x; x[k + 1][i] = w.y;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NCOL; ++k) {
-      const int cl = cl0 + k;
-      const int64_t cg = c0 + cl;
-      float* xk = x[k];
-      if constexpr (HR) hadamard_block<B>(xk, signs_r);
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
-      float rcp;
-      const uint32_t sbyte = block_scale<FMT>(m, sg_r, rcp);
-      uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
-#pragma unroll
-      for (int g = 0; g < B / 8; ++g) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
-        if constexpr (RR == 0) {
-          sc[g] = e2m1_rtn_pack8(v);
-        } else {
-          uint32_t h[4];
-          sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
-          sc[g] = e2m1_sr_pack8(v, h);
-        }
-      }
-      stage_s[cl * NB + b] = (uint8_t)sbyte;
-    }
-  }
-
-  // (b) blocks along the rows: row r0 + row, elements c0 + 64 * half ..
-  {
-    const int row = tid >> 1;
-    const int half = tid & 1;
-    const int64_t rgl = r0 + row;
-    constexpr int NBT = 64 / B;  // blocks per thread
-    uint32_t w[8];
-    uint32_t sb[NBT];
-#pragma unroll
-    for (int bb = 0; bb < NBT; ++bb) {
-      float x[B];
-      const uint8_t* p = &tile[row * PITCH + (half * 64 + bb * B) * ES];
-#pragma unroll
-      for (int i = 0; i < B; i += 4) {
-        if constexpr (BF16) {
-          const uint2 u = *reinterpret_cast<const uint2*>(p + 2 * i);
-          x[i] = bf16_lo(u.x); x[i + 1] = bf16_hi(u.x); x[i + 2] = bf16_lo(u.y); x[i + 3] = bf16_hi(u.y);
-        } else {
-          const float2 a = *reinterpret_cast<const float2*>(p + 4 * i);
-          const float2 c = *reinterpret_cast<const float2*>(p + 4 * i + 8);
-          x[i] = a.x; x[i + 1] = a.y; x[i + 2] = c.x; x[i + 3] = c.y;
-        }
-      }
-      if constexpr (HC) hadamard_block<B>(x, signs_c);
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
-      float rcp;
-      sb[bb] = block_scale<FMT>(m, sg_c, rcp);
-      const int64_t col0 = c0 + half * 64 + bb * B;
-#pragma unroll
-      for (int g = 0; g < B / 8; ++g) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
-        if constexpr (RC == 0) {
-          w[bb * (B / 8) + g] = e2m1_rtn_pack8(v);
-        } else {
-          uint32_t h[4];
-          sr_draws8(seed_c, (off_c + (uint64_t)rgl * (uint64_t)C + (uint64_t)col0) / 8 + g, h);
-          w[bb * (B / 8) + g] = e2m1_sr_pack8(v, h);
-        }
-      }
-    }
-    if (row < rows_here && half * 64 < cols_here) {
-      uint8_t* dst = codes_c + rgl * (C / 2) + (c0 + half * 64) / 2;
-      const bool full = half * 64 + 64 <= cols_here;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (full || (half * 64 + 16 * k) < cols_here)
-          *reinterpret_cast<uint2*>(dst + 8 * k) = make_uint2(w[2 * k], w[2 * k + 1]);
-      uint8_t* sdst = scales_c + rgl * (C / B) + (c0 + half * 64) / B;
-      if (scale_words_c && full) {
-        if constexpr (NBT == 4) *reinterpret_cast<uint32_t*>(sdst) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-        else *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)(sb[0] | (sb[1] << 8));
-      } else {
-#pragma unroll
-        for (int bb = 0; bb < NBT; ++bb)
-          if (half * 64 + bb * B < cols_here) sdst[bb] = (uint8_t)sb[bb];
-      }
-    }
-  }
-  __syncthreads();
-
-  // write out (a): output row c0 + cl gets T/2 code bytes (8-byte pieces) and NB scale bytes.
-#pragma unroll
-  for (int k = 0; k < T * (T / 16) / 256; ++k) {
-    const int idx = k * 256 + tid;
-    const int cl = idx / (T / 16);
-    const int seg = idx % (T / 16);
-    if (cl < cols_here && seg * 16 < rows_here) {
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
-      *reinterpret_cast<uint2*>(codes_r + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
-    }
-  }
-  if (scale_words_r) {
-    // (R / B) % 4 == 0: 4-byte words, NB / 4 per output row.
-    constexpr int WPR = NB / 4;
-    if (tid < T * WPR) {
-      const int cl = tid / WPR;
-      const int wd = tid % WPR;
-      if (cl < cols_here && wd * 4 * B < rows_here)
-        *reinterpret_cast<uint32_t*>(scales_r + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
-            *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < (T * NB + 255) / 256; ++k) {
+    for (int k = 0; k < T * CPR / 256; ++k) {
       const int idx = k * 256 + tid;
-      const int cl = idx / NB;
-      const int bb = idx % NB;
-      if (idx < T * NB && cl < cols_here && bb * B < rows_here)
-        scales_r[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
+      const int rr = idx / CPR;
+      const int cc = idx % CPR;
+      const int64_t col = c0 + cc * (16 / ES);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r0 + rr < R && col < C)
+        v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
+      uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
+      d[0] = make_uint2(v.x, v.y);
+      d[1] = make_uint2(v.z, v.w);
     }
+    __syncthreads();
+
+    const int64_t rows_here = R - r0 < T ? R - r0 : T;  // multiples of B
+    const int64_t cols_here = C - c0 < T ? C - c0 : T;
+
+
+    // (a) blocks down the columns: output row c0 + cl, elements r0 ..
+    {
+      const int b = tid / TPB;
+      const int cl0 = (tid % TPB) * NCOL;
+      const int64_t rg = r0 + (int64_t)b * B;
+      float x[NCOL][B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
+        if constexpr (BF16) {
+          if constexpr (NCOL == 4) {
+            const uint2 w = *reinterpret_cast<const uint2*>(p);
+            x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
+          } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+            x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < NCOL; k += 2) {
+            const float2 w = *reinterpret_cast<const float2*>(p + 4 * k);
+            x[k][i] = w.x; x[k + 1][i] = w.y;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NCOL; ++k) {
+        const int cl = cl0 + k;
+        const int64_t cg = c0 + cl;
+        float* xk = x[k];
+        if constexpr (HR) hadamard_block<B>(xk, signs_r);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
+        float rcp;
+        const uint32_t sbyte = block_scale<FMT>(m, sg_r, rcp);
+        uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
+        float bg = 0.0f, be = 0.0f;
+        const float bs = (MON && noise_r) ? scale_value<FMT>(sbyte) : 0.0f;
+#pragma unroll
+        for (int g = 0; g < B / 8; ++g) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
+          uint32_t cw;
+          if constexpr (RR == 0) {
+            cw = e2m1_rtn_pack8(v);
+          } else {
+            uint32_t h[4];
+            sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+            cw = e2m1_sr_pack8(v, h);
+          }
+          sc[g] = cw;
+          if (MON && noise_r) noise8<FMT>(xk + 8 * g, cw, bs, sg_r, bg, be);
+        }
+        stage_s[cl * NB + b] = (uint8_t)sbyte;
+        ngr += (double)bg;
+        ner += (double)be;
+      }
+    }
+
+    // (b) blocks along the rows: row r0 + row, elements c0 + 64 * half ..
+    {
+      const int row = tid >> 1;
+      const int half = tid & 1;
+      const int64_t rgl = r0 + row;
+      constexpr int NBT = 64 / B;  // blocks per thread
+      uint32_t w[8];
+      uint32_t sb[NBT];
+#pragma unroll
+      for (int bb = 0; bb < NBT; ++bb) {
+        float x[B];
+        const uint8_t* p = &tile[row * PITCH + (half * 64 + bb * B) * ES];
+#pragma unroll
+        for (int i = 0; i < B; i += 4) {
+          if constexpr (BF16) {
+            const uint2 u = *reinterpret_cast<const uint2*>(p + 2 * i);
+            x[i] = bf16_lo(u.x); x[i + 1] = bf16_hi(u.x); x[i + 2] = bf16_lo(u.y); x[i + 3] = bf16_hi(u.y);
+          } else {
+            const float2 a = *reinterpret_cast<const float2*>(p + 4 * i);
+            const float2 c = *reinterpret_cast<const float2*>(p + 4 * i + 8);
+            x[i] = a.x; x[i + 1] = a.y; x[i + 2] = c.x; x[i + 3] = c.y;
+          }
+        }
+        if constexpr (HC) hadamard_block<B>(x, signs_c);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
+        float rcp;
+        sb[bb] = block_scale<FMT>(m, sg_c, rcp);
+        const int64_t col0 = c0 + half * 64 + bb * B;
+        float bg = 0.0f, be = 0.0f;
+        const float bs = (MON && noise_c) ? scale_value<FMT>(sb[bb]) : 0.0f;
+#pragma unroll
+        for (int g = 0; g < B / 8; ++g) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
+          if constexpr (RC == 0) {
+            w[bb * (B / 8) + g] = e2m1_rtn_pack8(v);
+          } else {
+            uint32_t h[4];
+            sr_draws8(seed_c, (off_c + (uint64_t)rgl * (uint64_t)C + (uint64_t)col0) / 8 + g, h);
+            w[bb * (B / 8) + g] = e2m1_sr_pack8(v, h);
+          }
+          if (MON && noise_c) noise8<FMT>(x + 8 * g, w[bb * (B / 8) + g], bs, sg_c, bg, be);
+        }
+        ngc += (double)bg;
+        nec += (double)be;
+      }
+      if (row < rows_here && half * 64 < cols_here) {
+        uint8_t* dst = codes_c + rgl * (C / 2) + (c0 + half * 64) / 2;
+        const bool full = half * 64 + 64 <= cols_here;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (full || (half * 64 + 16 * k) < cols_here)
+            *reinterpret_cast<uint2*>(dst + 8 * k) = make_uint2(w[2 * k], w[2 * k + 1]);
+        uint8_t* sdst = scales_c + rgl * (C / B) + (c0 + half * 64) / B;
+        if (scale_words_c && full) {
+          if constexpr (NBT == 4) *reinterpret_cast<uint32_t*>(sdst) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+          else *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)(sb[0] | (sb[1] << 8));
+        } else {
+#pragma unroll
+          for (int bb = 0; bb < NBT; ++bb)
+            if (half * 64 + bb * B < cols_here) sdst[bb] = (uint8_t)sb[bb];
+        }
+      }
+    }
+    __syncthreads();
+
+    // write out (a): output row c0 + cl gets T/2 code bytes (8-byte pieces) and NB scale bytes.
+#pragma unroll
+    for (int k = 0; k < T * (T / 16) / 256; ++k) {
+      const int idx = k * 256 + tid;
+      const int cl = idx / (T / 16);
+      const int seg = idx % (T / 16);
+      if (cl < cols_here && seg * 16 < rows_here) {
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(&stage_c[cl * SP + seg * 8]);
+        *reinterpret_cast<uint2*>(codes_r + (c0 + cl) * (R / 2) + r0 / 2 + seg * 8) = make_uint2(sp[0], sp[1]);
+      }
+    }
+    if (scale_words_r) {
+      // (R / B) % 4 == 0: 4-byte words, NB / 4 per output row.
+      constexpr int WPR = NB / 4;
+      if (tid < T * WPR) {
+        const int cl = tid / WPR;
+        const int wd = tid % WPR;
+        if (cl < cols_here && wd * 4 * B < rows_here)
+          *reinterpret_cast<uint32_t*>(scales_r + (c0 + cl) * (R / B) + r0 / B + wd * 4) =
+              *reinterpret_cast<const uint32_t*>(&stage_s[cl * NB + wd * 4]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < (T * NB + 255) / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int cl = idx / NB;
+        const int bb = idx % NB;
+        if (idx < T * NB && cl < cols_here && bb * B < rows_here)
+          scales_r[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
+      }
+    }
+    if constexpr (MON) __syncthreads();  // the next tile reuses the LDS buffers
+  }
+  if constexpr (MON) {
+    if (noise_c) noise_reduce(ngc, nec, noise_c);
+    if (noise_c && noise_r) __syncthreads();
+    if (noise_r) noise_reduce(ngr, ner, noise_r);
   }
 }
 
-template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR>
+template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
 void launch_dual(const DualArgs& a, hipStream_t s) {
   constexpr int B = FMT == NV ? 16 : 32;
   const uint32_t tiles_c = (uint32_t)((a.C + 127) / 128);
@@ -239,31 +266,40 @@ void launch_dual(const DualArgs& a, hipStream_t s) {
   // Scale bytes of a tile go out as words when every row start keeps them aligned.
   const uint32_t words_c = FMT == NV ? (a.C / B) % 4 == 0 : (a.C / B) % 2 == 0;
   const uint32_t words_r = (a.R / B) % 4 == 0;
-  hipLaunchKernelGGL((k_quant_dual<FMT, RC, RR, BF16, HC, HR>), dim3(tiles_c * tiles_r), dim3(256), 0,
-                     s, a.src, a.R, a.C, a.ld, tiles_c, a.codes_c, a.scales_c, a.codes_r, a.scales_r,
+  const uint32_t ntiles = tiles_c * tiles_r;
+  const uint32_t grid = MON && ntiles > kNoiseGrid ? kNoiseGrid : ntiles;
+  hipLaunchKernelGGL((k_quant_dual<FMT, RC, RR, BF16, HC, HR, MON>), dim3(grid), dim3(256), 0,
+                     s, a.src, a.R, a.C, a.ld, tiles_c, ntiles, a.codes_c, a.scales_c, a.codes_r, a.scales_r,
                      a.amax_c, a.amax_r, a.tscale_c, a.tscale_r, a.amax_copy, a.seed_c, a.offset_c,
-                     a.signs_c, a.seed_r, a.offset_r, a.signs_r, words_c, words_r);
+                     a.signs_c, a.seed_r, a.offset_r, a.signs_r, words_c, words_r, a.noise_c,
+                     a.noise_r);
+}
+
+template <int FMT, bool BF16, bool HC, bool HR, bool MON>
+void launch_dual_rnd(const DualArgs& a, hipStream_t s) {
+  if (a.sr_c) {
+    if (a.sr_r) launch_dual<FMT, 1, 1, BF16, HC, HR, MON>(a, s);
+    else launch_dual<FMT, 1, 0, BF16, HC, HR, MON>(a, s);
+  } else {
+    if (a.sr_r) launch_dual<FMT, 0, 1, BF16, HC, HR, MON>(a, s);
+    else launch_dual<FMT, 0, 0, BF16, HC, HR, MON>(a, s);
+  }
 }
 
 template <int FMT, bool BF16, bool HC, bool HR>
-void launch_dual_rnd(const DualArgs& a, hipStream_t s) {
-  if (a.sr_c) {
-    if (a.sr_r) launch_dual<FMT, 1, 1, BF16, HC, HR>(a, s);
-    else launch_dual<FMT, 1, 0, BF16, HC, HR>(a, s);
-  } else {
-    if (a.sr_r) launch_dual<FMT, 0, 1, BF16, HC, HR>(a, s);
-    else launch_dual<FMT, 0, 0, BF16, HC, HR>(a, s);
-  }
+void launch_dual_mon(const DualArgs& a, hipStream_t s) {
+  if (a.noise_c || a.noise_r) launch_dual_rnd<FMT, BF16, HC, HR, true>(a, s);
+  else launch_dual_rnd<FMT, BF16, HC, HR, false>(a, s);
 }
 
 template <int FMT, bool BF16>
 void launch_dual_had(const DualArgs& a, hipStream_t s) {
   if (a.had_c) {
-    if (a.had_r) launch_dual_rnd<FMT, BF16, true, true>(a, s);
-    else launch_dual_rnd<FMT, BF16, true, false>(a, s);
+    if (a.had_r) launch_dual_mon<FMT, BF16, true, true>(a, s);
+    else launch_dual_mon<FMT, BF16, true, false>(a, s);
   } else {
-    if (a.had_r) launch_dual_rnd<FMT, BF16, false, true>(a, s);
-    else launch_dual_rnd<FMT, BF16, false, false>(a, s);
+    if (a.had_r) launch_dual_mon<FMT, BF16, false, true>(a, s);
+    else launch_dual_mon<FMT, BF16, false, false>(a, s);
   }
 }
 

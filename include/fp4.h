@@ -186,6 +186,36 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
                              int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
                              fp4_stream_t stream);
 
+/* Gradient-noise monitor ("FP4 All the Way", Summary: a threshold relating the
+ * gradient norm to the quantization noise marks where quantized training stops
+ * paying off). fp4_quantize, plus, in the same pass:
+ *   noise[0] += sum x^2           over the values quantized (rotated when had_on)
+ *   noise[1] += sum (xhat - x)^2  xhat = the exact value each code and its scales
+ *                                 stand for (e2m1 * sdec * s_g, or e2m1 * 2^e)
+ * noise: device, two doubles, 8-byte aligned; accumulated into (several calls,
+ * e.g. micro-batches or shards, add up; the caller clears it first).
+ * sqrt(noise[0] / noise[1]) is the gradient-to-noise norm ratio the threshold
+ * is stated on; the threshold itself is the caller's. Each 8-element (COLS) or
+ * block (ROWS) partial is formed in FP32 (each difference rounded once, squares
+ * accumulated by fma) and added in FP64: relative error below 1e-5 of each sum.
+ * The FP64 additions across workgroups are atomic, in no fixed order, so the
+ * last bits can differ between runs. Codes, scales and s_g are identical to
+ * fp4_quantize's. Requires the squares to be finite in FP32 (|x| < 2^63);
+ * otherwise as fp4_quantize, and FP4_ERR_NULL for a NULL noise. */
+fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                              fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                              int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream);
+
+/* fp4_quantize_dual with the noise monitor of fp4_quantize_noise on either
+ * orientation: noise_cols for out_cols, noise_rows for out_rows (each two
+ * device doubles, accumulated into, or NULL to skip; FP4_ERR_NULL if both are
+ * NULL). Partials are per block in both orientations. */
+fp4_status fp4_quantize_dual_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                                   fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
+                                   fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
+                                   int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
+                                   double* noise_cols, double* noise_rows, fp4_stream_t stream);
+
 /* Dequantize q to dst (device, q->rows x q->cols row-major, leading dimension
  * ld >= cols, FP32 or bf16):
  *   NVFP4: (e2m1 * sdec) * s_g, the last product rounded once to FP32;

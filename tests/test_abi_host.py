@@ -144,6 +144,22 @@ def test_quantize_dual_rejects_null_descriptors(fp4):
                                        ctypes.byref(d), None) == 1
 
 
+def test_noise_entry_points_reject_bad_arguments(fp4):
+    L = fp4.lib()
+    d = _t(fp4)
+    args = (0x1000, 1, 64, 128, 128, 0, 0, 0, 0, 1, ctypes.byref(d))
+    assert L.fp4_quantize_noise(*args, None, None) == 1
+    assert L.fp4_quantize_noise(*args, 0x60004, None) == 3          # noise not 8-byte aligned
+    assert L.fp4_quantize_noise(0x1000, 1, 64, 120, 128, 0, 0, 0, 0, 1, ctypes.byref(d), 0x60000,
+                                None) == 2                            # checks of fp4_quantize still apply
+    dc, dr = _t(fp4), _t(fp4)
+    dargs = (0x1000, 1, 64, 128, 128, 0, 0, 0, 1, 0, 0, 1, ctypes.byref(dc), ctypes.byref(dr))
+    assert L.fp4_quantize_dual_noise(*dargs, None, None, None) == 1
+    assert L.fp4_quantize_dual_noise(*dargs, None, 0x60002, None) == 3
+    assert L.fp4_quantize_dual_noise(0x1000, 1, 40, 128, 128, 0, 0, 0, 1, 0, 0, 1, ctypes.byref(dc),
+                                     ctypes.byref(dr), 0x60000, None, None) == 2
+
+
 AMAX_H16_BAD = [
     # (src, dtype, R, C, ld, axis, amax, expected)
     (0, 1, 64, 128, 128, 0, 0x30000, 1),

@@ -268,3 +268,86 @@ def test_full_size_quantize_matches_oracle(fp4, orc, wl, role, axis, fmt, rnd, h
     want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=(1 << 8) | (axis + 1),
                         had_on=had, had_signs=signs or 0)
     assert_same_quant(got, want, f"{wl} {role}")
+
+
+# ------------------------------------------------------- gradient-noise monitor
+# Each partial sum is formed in FP32 over at most 32 elements (differences
+# rounded once, squares accumulated by fma): relative error <= 33 * 2^-24
+# (2e-6) of a sum of non-negative terms; the FP64 part is exact to 1e-15.
+NOISE_RTOL = 1e-5
+
+
+def _assert_noise(got, want, what):
+    got = got.cpu().numpy()
+    for k, name in ((0, "sum x^2"), (1, "sum (xhat - x)^2")):
+        assert abs(got[k] - want[k]) <= NOISE_RTOL * want[k], (what, name, got[k], want[k])
+
+
+NOISE = [(fmt, rnd, axis, had) for fmt in (0, 1) for rnd in (0, 1) for axis in (0, 1) for had in (False, True)]
+
+
+@pytest.mark.parametrize("fmt,rnd,axis,had", NOISE)
+@pytest.mark.parametrize("shape,bf16", [((96, 1056), True), ((256, 256), False)])
+def test_quantize_noise_matches_oracle(fp4, orc, fmt, rnd, axis, had, shape, bf16):
+    import torch
+    say("quantize noise", shape, "fmt", fmt, "rnd", rnd, "axis", axis, "had", had, "bf16", bf16)
+    xh = _mixed(shape, 51 + shape[0], bf16)
+    signs = orc.hadamard_signs(7) if had else 0
+    want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=13, had_on=had, had_signs=signs, noise=True)
+    noise = torch.zeros(2, dtype=torch.float64, device="cuda")
+    x = to_device(xh)
+    q = fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=13, had_signs=signs if had else None, noise=noise)
+    assert_same_quant(q_to_host(q), want, "quantize with the noise monitor")
+    _assert_noise(noise, want["noise"], "one call")
+    fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=13, had_signs=signs if had else None, noise=noise)
+    _assert_noise(noise, 2 * want["noise"], "accumulated over two calls")
+
+
+DUAL_NOISE = [(0, 1, 1, (False, False)), (0, 0, 1, (False, True)), (1, 1, 1, (True, True)),
+              (1, 0, 1, (False, False))]
+
+
+@pytest.mark.parametrize("fmt,rc,rr,had", DUAL_NOISE)
+@pytest.mark.parametrize("which", ["both", "cols", "rows"])
+def test_quantize_dual_noise_matches_oracle(fp4, orc, fmt, rc, rr, had, which):
+    import torch
+    say("quantize_dual noise", "fmt", fmt, "rnd", rc, rr, "had", had, which)
+    xh = _mixed((160, 1056), 61)
+    hc, hr = had
+    sc = orc.hadamard_signs(8) if hc else 0
+    sr = orc.hadamard_signs(9) if hr else 0
+    want_c = orc.quantize(xh, axis=0, fmt=fmt, rnd=rc, seed=5, had_on=hc, had_signs=sc, noise=True)
+    want_r = orc.quantize(xh, axis=1, fmt=fmt, rnd=rr, seed=6, had_on=hr, had_signs=sr, noise=True)
+    nc = torch.zeros(2, dtype=torch.float64, device="cuda") if which != "rows" else None
+    nr = torch.zeros(2, dtype=torch.float64, device="cuda") if which != "cols" else None
+    qc, qr = fp4.quantize_dual(to_device(xh), fmt=fmt, rnd_cols=rc, seed_cols=5, rnd_rows=rr, seed_rows=6,
+                               had_signs_cols=sc if hc else None, had_signs_rows=sr if hr else None,
+                               noise_cols=nc, noise_rows=nr)
+    assert_same_quant(q_to_host(qc), want_c, "dual cols")
+    assert_same_quant(q_to_host(qr), want_r, "dual rows")
+    if nc is not None:
+        _assert_noise(nc, want_c["noise"], "dual cols")
+    if nr is not None:
+        _assert_noise(nr, want_r["noise"], "dual rows")
+
+
+def test_noise_monitor_full_size_gradient(fp4, orc):
+    """The Llama-7B layer's dY, SR in both orientations, with the monitor on both."""
+    import torch
+    from fp4_fully_quantized_amd import workloads
+    say("noise monitor full size dY")
+    x = workloads.device_tensor("llama7b", "dY")
+    nc = torch.zeros(2, dtype=torch.float64, device="cuda")
+    nr = torch.zeros(2, dtype=torch.float64, device="cuda")
+    qc, qr = fp4.quantize_dual(x, rnd_cols=1, seed_cols=(2 << 8) | 1, rnd_rows=1, seed_rows=(2 << 8) | 2,
+                               noise_cols=nc, noise_rows=nr)
+    torch.cuda.synchronize()
+    got_c = q_to_host(qc)
+    xh = to_host(x)
+    del qc, qr, x
+    want_c = orc.quantize(xh, axis=0, rnd=1, seed=(2 << 8) | 1, noise=True)
+    assert_same_quant(got_c, want_c, "dY cols")
+    _assert_noise(nc, want_c["noise"], "dY cols")
+    want_r = orc.quantize(xh, axis=1, rnd=1, seed=(2 << 8) | 2, noise=True)
+    _assert_noise(nr, want_r["noise"], "dY rows")
+    say("gradient / noise norm ratio", fp4.noise_ratio(nc), fp4.noise_ratio(nr))
