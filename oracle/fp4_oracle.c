@@ -328,6 +328,48 @@ static void quant_noise(const float* x, const uint8_t* codes, const uint8_t* sca
     free(part);
 }
 
+/* Block scale "amax/6" of a block with amax amax_b: returns the scale byte and
+ * sets the element multiplier r.
+ * NVFP4: E4M3 scale relative to the tensor scale, rounded to nearest; the
+ * element multiplier is the reciprocal of the full decoded scale, rounded once
+ * (zero scale -> zero). MXFP4: the power of two of o_e8m0_exponent. */
+static unsigned block_scale(float amax_b, int fmt, float sg, float* rcp)
+{
+    if (fmt == O_FMT_NVFP4) {
+        float q = amax_b / 6.0f;
+        q = q / sg;
+        unsigned sbyte = o_e4m3_encode(q);
+        float sdec = (float)o_e4m3_value(sbyte);
+        float d = sdec * sg;
+        *rcp = (d == 0.0f) ? 0.0f : 1.0f / d;
+        return sbyte;
+    }
+    int e = o_e8m0_exponent(amax_b);
+    *rcp = (float)ldexp(1.0, -e);
+    return (unsigned)(e + 127);
+}
+
+/* The E2M1 code of x with element multiplier rcp: RTN, or SR with the 16-bit
+ * draw of element index idx under seed. */
+static unsigned encode_elem(float x, float rcp, int rnd, uint64_t seed, uint64_t idx)
+{
+    float v = x * rcp;
+    float a = fabsf(v);
+    if (a > 6.0f) a = 6.0f;
+    unsigned mag = (rnd == O_SR) ? o_e2m1_sr_mag(a, o_sr_draw16(seed, idx)) : o_e2m1_rtn_mag(a);
+    return (signbit(v) ? 8u : 0u) | mag;
+}
+
+/* Code nibble at packed position pos (element 2t in the low nibble of byte t). */
+static void put_code(uint8_t* codes, int64_t pos, unsigned code)
+{
+    uint8_t* byte = &codes[pos >> 1];
+    if ((pos & 1) == 0)
+        *byte = (uint8_t)((*byte & 0xF0u) | code);
+    else
+        *byte = (uint8_t)((*byte & 0x0Fu) | (code << 4));
+}
+
 static int quantize_impl(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld,
                          int axis, int fmt, int rnd, uint64_t seed, uint64_t index_offset,
                          int had_on, uint32_t had_signs, int amax_given, float amax_in,
@@ -395,44 +437,13 @@ static int quantize_impl(const void* src, int src_bf16, int64_t R, int64_t C, in
             for (int j = 0; j < B; ++j)
                 if (fabsf(x[j]) > amax_b) amax_b = fabsf(x[j]);
 
-            /* Block scale "amax/6" and the element multiplier r. */
             float rcp;
-            unsigned sbyte;
-            if (fmt == O_FMT_NVFP4) {
-                /* E4M3 scale relative to the tensor scale, rounded to
-                 * nearest; the element multiplier is the reciprocal of the
-                 * full decoded scale, rounded once (zero scale -> zero). */
-                float q = amax_b / 6.0f;
-                q = q / sg;
-                sbyte = o_e4m3_encode(q);
-                float sdec = (float)o_e4m3_value(sbyte);
-                float d = sdec * sg;
-                rcp = (d == 0.0f) ? 0.0f : 1.0f / d;
-            } else {
-                int e = o_e8m0_exponent(amax_b);
-                sbyte = (unsigned)(e + 127);
-                rcp = (float)ldexp(1.0, -e);
-            }
+            unsigned sbyte = block_scale(amax_b, fmt, sg, &rcp);
             scales[r * nblk + b] = (uint8_t)sbyte;
 
             for (int j = 0; j < B; ++j) {
-                float v = x[j] * rcp;
-                float a = fabsf(v);
-                if (a > 6.0f) a = 6.0f;
-                unsigned mag;
-                if (rnd == O_SR) {
-                    uint64_t idx = index_offset + (uint64_t)(r * cols_q + b * B + j);
-                    mag = o_e2m1_sr_mag(a, o_sr_draw16(seed, idx));
-                } else {
-                    mag = o_e2m1_rtn_mag(a);
-                }
-                unsigned code = (signbit(v) ? 8u : 0u) | mag;
-                int64_t pos = r * cols_q + b * B + j;
-                uint8_t* byte = &codes[pos >> 1];
-                if ((pos & 1) == 0)
-                    *byte = (uint8_t)((*byte & 0xF0u) | code);
-                else
-                    *byte = (uint8_t)((*byte & 0x0Fu) | (code << 4));
+                uint64_t idx = index_offset + (uint64_t)(r * cols_q + b * B + j);
+                put_code(codes, r * cols_q + b * B + j, encode_elem(x[j], rcp, rnd, seed, idx));
             }
         }
     }
@@ -459,6 +470,63 @@ int o_quantize_noise(const void* src, int src_bf16, int64_t R, int64_t C, int64_
     if (!noise) return -1;
     return quantize_impl(src, src_bf16, R, C, ld, axis, fmt, rnd, seed, index_offset, had_on,
                          had_signs, amax_given, amax_in, codes, scales, amax_out, sg_out, noise);
+}
+
+/* Two-dimensional block quantization (Robots Atlas "FP4", How it works: two-
+ * dimensional quantization among the stabilizers). Reading: square B x B
+ * blocks (B = 16 NVFP4, 32 MXFP4), one scale per block from the block's amax
+ * by the same rule as a 1-D block, so that the matrix and its transpose are
+ * the same quantization. Element index for SR: row-major position in the
+ * R x C source + index_offset, for both outputs, so out_t is exactly the
+ * transpose of out. Outputs in the layouts of o_quantize:
+ *   codes   [R][C/2], scales   [R][C/B]   (the block's byte on each of its rows)
+ *   codes_t [C][R/2], scales_t [C][R/B]   (the transpose) */
+int o_quantize_2d(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld, int fmt, int rnd,
+                  uint64_t seed, uint64_t index_offset, int amax_given, float amax_in,
+                  uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                  float* amax_out, float* sg_out)
+{
+    if (!src || !codes || !scales || !codes_t || !scales_t || R <= 0 || C <= 0 || ld < C) return -1;
+    if (fmt != O_FMT_NVFP4 && fmt != O_FMT_MXFP4) return -1;
+    const int B = (fmt == O_FMT_NVFP4) ? 16 : 32;
+    if (R % B != 0 || C % B != 0) return -1;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c)
+            if (!isfinite(load_elem(src, src_bf16, r * ld + c))) return -2;
+
+    float sg = 1.0f;
+    if (fmt == O_FMT_NVFP4) {
+        float amax = amax_given ? amax_in : o_tensor_amax(src, src_bf16, R, C, ld);
+        sg = nv_tensor_scale(amax);
+        if (amax_out) *amax_out = amax;
+        if (sg_out) *sg_out = sg;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t br = 0; br < R / B; ++br) {
+        for (int64_t bc = 0; bc < C / B; ++bc) {
+            float amax_b = 0.0f;
+            for (int i = 0; i < B; ++i)
+                for (int j = 0; j < B; ++j) {
+                    float a = fabsf(load_elem(src, src_bf16, (br * B + i) * ld + bc * B + j));
+                    if (a > amax_b) amax_b = a;
+                }
+            float rcp;
+            unsigned sbyte = block_scale(amax_b, fmt, sg, &rcp);
+            for (int i = 0; i < B; ++i) {
+                int64_t r = br * B + i, c0 = bc * B;
+                scales[r * (C / B) + bc] = (uint8_t)sbyte;
+                scales_t[(c0 + i) * (R / B) + br] = (uint8_t)sbyte;
+                for (int j = 0; j < B; ++j) {
+                    int64_t c = c0 + j;
+                    unsigned code = encode_elem(load_elem(src, src_bf16, r * ld + c), rcp, rnd, seed,
+                                                index_offset + (uint64_t)(r * C + c));
+                    put_code(codes, r * C + c, code);
+                    put_code(codes_t, c * R + r, code);
+                }
+            }
+        }
+    }
+    return 0;
 }
 
 static double scale_value(const uint8_t* scales, int64_t i, int fmt)

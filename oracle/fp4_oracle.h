@@ -86,6 +86,14 @@ int o_quantize_noise(const void* src, int src_bf16, int64_t R, int64_t C, int64_
                      int had_on, uint32_t had_signs, int amax_given, float amax_in,
                      uint8_t* codes, uint8_t* scales, float* amax_out, float* sg_out,
                      double noise[2]);
+/* Two-dimensional B x B block quantization of an R x C matrix (R, C multiples
+ * of B): one scale per square block, element index for SR = row-major [R][C]
+ * position + index_offset. codes/scales as o_quantize with axis COLS, and
+ * codes_t/scales_t as axis ROWS; the two are transposes of each other. */
+int o_quantize_2d(const void* src, int src_bf16, int64_t R, int64_t C, int64_t ld, int fmt, int rnd,
+                  uint64_t seed, uint64_t index_offset, int amax_given, float amax_in,
+                  uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                  float* amax_out, float* sg_out);
 int o_dequantize_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int fmt, float sg, float* out);
 /* Exact dequantized values in FP64 (e2m1 * scale * tensor_scale is exact in FP64). */

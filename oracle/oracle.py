@@ -80,6 +80,10 @@ def lib():
                                  c.POINTER(c.c_float)]
         L.o_quantize_noise.restype = c.c_int
         L.o_quantize_noise.argtypes = L.o_quantize.argtypes + [c.c_void_p]
+        L.o_quantize_2d.restype = c.c_int
+        L.o_quantize_2d.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_int,
+                                    c.c_uint64, c.c_uint64, c.c_int, c.c_float, c.c_void_p, c.c_void_p,
+                                    c.c_void_p, c.c_void_p, c.POINTER(c.c_float), c.POINTER(c.c_float)]
         L.o_dequantize_f32.restype = c.c_int
         L.o_dequantize_f32.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                        c.c_float, c.c_void_p]
@@ -210,6 +214,37 @@ def quantize(x: np.ndarray, axis: int = AXIS_COLS, fmt: int = FMT_NVFP4, rnd: in
     if noise:
         out["noise"] = nz
     return out
+
+
+def quantize_2d(x: np.ndarray, fmt: int = FMT_NVFP4, rnd: int = RTN, seed: int = 0,
+                index_offset: int = 0, amax: float | None = None):
+    """Two-dimensional B x B block quantization. Returns (q, q_t): the [R, C]
+    quantization (blocks along C) and its transpose [C, R] (blocks along R),
+    both in the layout of quantize()."""
+    a, bf = _src(x)
+    R, C = a.shape
+    B = BLOCK[fmt]
+    codes = np.zeros((R, C // 2), dtype=np.uint8)
+    scales = np.zeros((R, C // B), dtype=np.uint8)
+    codes_t = np.zeros((C, R // 2), dtype=np.uint8)
+    scales_t = np.zeros((C, R // B), dtype=np.uint8)
+    am = ctypes.c_float(0.0)
+    sg = ctypes.c_float(1.0)
+    rc = lib().o_quantize_2d(a.ctypes.data, bf, R, C, C, fmt, rnd, seed, index_offset,
+                             int(amax is not None), float(amax or 0.0), codes.ctypes.data,
+                             scales.ctypes.data, codes_t.ctypes.data, scales_t.ctypes.data,
+                             ctypes.byref(am), ctypes.byref(sg))
+    if rc != 0:
+        raise ValueError(f"oracle quantize_2d rejected its input (rc={rc})")
+    out = []
+    for cd, scl, rows, cols in ((codes, scales, R, C), (codes_t, scales_t, C, R)):
+        q = {"codes": cd, "scales": scl, "fmt": fmt, "rows": rows, "cols": cols}
+        if fmt == FMT_NVFP4:
+            q["amax"], q["sg"] = float(am.value), float(sg.value)
+        else:
+            q["amax"], q["sg"] = None, 1.0
+        out.append(q)
+    return out[0], out[1]
 
 
 def dequantize_f32(q: dict) -> np.ndarray:

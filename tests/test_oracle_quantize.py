@@ -331,3 +331,72 @@ def test_sr_noise_has_the_bernoulli_expectation(orc):
     n = 400
     e2 = np.array([orc.quantize(x, fmt=1, rnd=1, seed=1000 + k, noise=True)["noise"][1] for k in range(n)])
     assert abs(e2.mean() - mean.sum()) <= 4.5 * np.sqrt(var.sum() / n) + 1e-12
+
+
+# ------------------------------------------------------ 2-D block quantization
+def test_2d_worked_example(orc):
+    f = fields("nvfp4_2d_worked.txt")
+    x = np.ones((16, 32), dtype=np.float32)
+    x[:, 16:] = 0.5
+    x[3, 5], x[10, 20] = 6.0, 3.0
+    q, qt = orc.quantize_2d(x)
+    want_row = [int(v, 16) for v in f["scales_row"]]
+    assert all(list(r) == want_row for r in q["scales"])
+    assert [list(r) for r in qt["scales"]] == [[want_row[0]]] * 16 + [[want_row[1]]] * 16
+    u = unpack(q["codes"])
+    at = [int(v) for v in f["code7_at"]]
+    want = np.full((16, 32), 2)
+    want[at[0], at[1]] = want[at[2], at[3]] = 7
+    assert np.array_equal(u, want)
+    assert orc.quantize(x)["scales"][0, 0] == int(f["scale_1d_row0"][0], 16)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_2d_outputs_are_transposes(orc, fmt, rnd):
+    x = _randn((96, 128), 15, outliers=True)
+    q, qt = orc.quantize_2d(x, fmt=fmt, rnd=rnd, seed=7, index_offset=64)
+    assert np.array_equal(unpack(qt["codes"]), unpack(q["codes"]).T)
+    B = 16 if fmt == 0 else 32
+    s_full = np.repeat(q["scales"], B, axis=1)               # [R][C]: each element's block byte
+    st_full = np.repeat(qt["scales"], B, axis=1)             # [C][R]
+    assert np.array_equal(st_full, s_full.T)
+    # one byte per square block
+    blocks = s_full.reshape(96 // B, B, 128 // B, B)
+    assert (blocks == blocks[:, :1, :, :1]).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_2d_reduces_to_1d_when_every_row_and_column_holds_the_block_amax(orc, fmt):
+    # Put each block's amax on its diagonal: every row and every column of the
+    # block then has the block amax as its own 1-D block amax, so the 2-D
+    # scales equal the 1-D ones and the codes equal the 1-D quantizations along
+    # either axis (RTN; SR along rows, where both use the row-major index).
+    B = 16 if fmt == 0 else 32
+    x = _randn((2 * B, 3 * B), 16)
+    for br in range(2):
+        for bc in range(3):
+            blk = x[br * B:(br + 1) * B, bc * B:(bc + 1) * B]
+            m = np.abs(blk).max() * np.float32(1.5)
+            idx = np.arange(B)
+            blk[idx, idx] = m * np.where(idx % 2 == 0, 1, -1)
+    for rnd in (0, 1):
+        q, qt = orc.quantize_2d(x, fmt=fmt, rnd=rnd, seed=9)
+        a = orc.quantize(x, axis=orc.AXIS_COLS, fmt=fmt, rnd=rnd, seed=9)
+        assert np.array_equal(q["codes"], a["codes"]) and np.array_equal(q["scales"], a["scales"])
+        if rnd == 0:
+            b = orc.quantize(x, axis=orc.AXIS_ROWS, fmt=fmt)
+            assert np.array_equal(qt["codes"], b["codes"]) and np.array_equal(qt["scales"], b["scales"])
+        if fmt == 0:
+            assert q["sg"] == a["sg"]
+
+
+def test_2d_error_bound(orc):
+    # RTN with a block scale covering the block: |xhat - x| <= half the largest
+    # grid step (1 for E2M1) times the block's decoded scale, for every element
+    x = _randn((64, 64), 17, outliers=True)
+    q, _ = orc.quantize_2d(x)
+    xhat = orc.dequantize_f64(q)
+    sdec = np.array([[orc.e4m3_value(int(b)) for b in row] for row in q["scales"]])
+    bound = np.repeat(sdec, 16, axis=1) * q["sg"] * 1.0 * (1 + 2.0 ** -20)
+    assert (np.abs(xhat - x.astype(np.float64)) <= bound).all()
