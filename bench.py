@@ -121,13 +121,14 @@ def make_step(fp4, X, W, dY, signs, separate=False):
     return ops, outs, q
 
 
-def make_extras(fp4, X, dY, signs16):
+def make_extras(fp4, X, W, dY, signs16):
     """Adjacent passes timed beside the step (not part of it): the NVFP4
     quantizations of the wgrad operands with the 16-wide random-sign Hadamard
     along the tokens (with a rotation on one orientation the two orientations
     have their own tensor amax, the plain one and the rotated one, both taken
-    in one read of the tensor before the dual pass), and dY's dual SR pass with
-    the gradient-noise monitor on both orientations."""
+    in one read of the tensor before the dual pass); dY's dual SR pass with
+    the gradient-noise monitor on both orientations; the two-dimensional
+    (16 x 16) quantization of W that serves the forward GEMM and dgrad."""
     Q = fp4.QTensor
     NV = fp4.FP4_NVFP4
     COLS, ROWS, RTN, SR = fp4.FP4_AXIS_COLS, fp4.FP4_AXIS_ROWS, fp4.FP4_RTN, fp4.FP4_SR
@@ -138,7 +139,9 @@ def make_extras(fp4, X, dY, signs16):
         "X": Q(TOKENS, D_IN, NV), "Xt": Q(D_IN, TOKENS, NV, had_signs=signs16),
         "dY": Q(TOKENS, D_OUT, NV), "dYt": Q(D_OUT, TOKENS, NV, had_signs=signs16),
         "dYm": Q(TOKENS, D_OUT, NV), "dYmt": Q(D_OUT, TOKENS, NV),
+        "W2": Q(D_OUT, D_IN, NV), "W2t": Q(D_IN, D_OUT, NV),
     }
+    q["W2t"].amax = q["W2"].amax
     q["dYmt"].amax = q["dYm"].amax
     noise = torch.zeros(4, dtype=torch.float64, device="cuda")
     dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
@@ -151,6 +154,9 @@ def make_extras(fp4, X, dY, signs16):
         ("quant dY nv dual (sr K, sr+had16 tokens)", "q",
          lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
          algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
+        ("quant W nv 2-D 16x16 (rtn, W and W^T)", "q",
+         lambda: fp4.fp4_quantize_2d(W, RTN, 0, 0, False, q["W2"], q["W2t"]),
+         algorithmic_bytes(D_OUT * D_IN, 2, 16, True, 2)),
         ("quant dY nv dual (sr both) + noise monitor on both", "q",
          lambda: fp4.fp4_quantize_dual_noise(dY, SR, seed(1), 0, SR, seed(2), 0, False, q["dYm"], q["dYmt"],
                                              noise[0:2], noise[2:4]),
@@ -317,7 +323,7 @@ def main():
               for i, (name, kind, _, units) in enumerate(ops)]
 
     # Adjacent passes, timed after the step's timed region.
-    extra_ops, extra_q = make_extras(fp4, X, dY, fp4.fp4_hadamard_signs(4))
+    extra_ops, extra_q = make_extras(fp4, X, W, dY, fp4.fp4_hadamard_signs(4))
     extras = time_ops(extra_ops, args.steps, 2)
     del extra_ops, extra_q
 

@@ -23,7 +23,8 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
-           "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_dequantize", "fp4_gemm"]
+           "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_quantize_2d", "fp4_dequantize",
+           "fp4_gemm"]
 
 
 class Fp4Error(RuntimeError):
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.fp4_quantize_dual_noise.restype = c.c_int
         L.fp4_quantize_dual_noise.argtypes = L.fp4_quantize_dual.argtypes[:-1] + [c.c_void_p, c.c_void_p,
                                                                                   c.c_void_p]
+        L.fp4_quantize_2d.restype = c.c_int
+        L.fp4_quantize_2d.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64, c.c_int,
+                                      c.c_uint64, c.c_uint64, c.c_int, c.POINTER(fp4_tensor),
+                                      c.POINTER(fp4_tensor), c.c_void_p]
         L.fp4_dequantize.restype = c.c_int
         L.fp4_dequantize.argtypes = [c.POINTER(fp4_tensor), c.c_int, c.c_void_p, c.c_int64,
                                      c.c_void_p]
@@ -231,6 +236,37 @@ def fp4_quantize_dual_noise(src, rnd_cols: int, seed_cols: int, index_offset_col
                                          _stream(stream)), "fp4_quantize_dual_noise")
     out_cols.rows, out_cols.cols = dc.rows, dc.cols
     out_rows.rows, out_rows.cols = dr.rows, dr.cols
+
+
+def fp4_quantize_2d(src, rnd: int, seed: int, index_offset: int, amax_ready: bool, out: QTensor,
+                    out_t: QTensor, stream=None) -> None:
+    R, C = src.shape
+    if src.stride(1) != 1:
+        raise ValueError("src must be row-major with unit column stride")
+    d, dt = out.desc(), out_t.desc()
+    _check(lib().fp4_quantize_2d(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), rnd, seed,
+                                 index_offset, int(bool(amax_ready)), ctypes.byref(d), ctypes.byref(dt),
+                                 _stream(stream)), "fp4_quantize_2d")
+    out.rows, out.cols = d.rows, d.cols
+    out_t.rows, out_t.cols = dt.rows, dt.cols
+
+
+def quantize_2d(src, fmt: int = FP4_NVFP4, rnd: int = FP4_RTN, seed: int = 0, index_offset: int = 0,
+                amax_from: QTensor | None = None, stream=None):
+    """Allocate both QTensors and quantize src with B x B blocks. Returns
+    (q [R, C] blocked along C, q_t [C, R] blocked along R), one quantization
+    sharing the tensor amax (NVFP4)."""
+    R, C = src.shape
+    q = QTensor(R, C, fmt, device=src.device)
+    qt = QTensor(C, R, fmt, device=src.device)
+    ready = False
+    if amax_from is not None and fmt == FP4_NVFP4:
+        q.amax = amax_from.amax
+        ready = True
+    if fmt == FP4_NVFP4:
+        qt.amax = q.amax
+    fp4_quantize_2d(src, rnd, seed, index_offset, ready, q, qt, stream)
+    return q, qt
 
 
 def noise_ratio(noise) -> float:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4.so")
-SOURCES = ["quant.hip", "quant_dual.hip", "gemm.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "quant_dual.hip", "quant_2d.hip", "gemm.hip", "abi.cpp"]
 ARCH = os.environ.get("FP4_OFFLOAD_ARCH", "gfx950")
 
 

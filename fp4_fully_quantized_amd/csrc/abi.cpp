@@ -271,6 +271,58 @@ fp4_status fp4_quantize_dual_noise(const void* src, fp4_dtype src_t, int64_t R, 
                             noise_rows, stream);
 }
 
+fp4_status fp4_quantize_2d(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                           fp4_rounding rnd, uint64_t seed, uint64_t index_offset, int amax_ready,
+                           fp4_tensor* out, fp4_tensor* out_t, fp4_stream_t stream) {
+  if (!out || !out_t) return FP4_ERR_NULL;
+  fp4_status st = check_matrix(src, src_t, R, C, ld);
+  if (st != FP4_OK) return st;
+  if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ARG;
+  if (!valid_fmt(out->fmt) || !valid_fmt(out_t->fmt)) return FP4_ERR_ARG;
+  if (out->fmt != out_t->fmt) return FP4_ERR_UNSUPPORTED;
+  if (out->had_on || out_t->had_on) return FP4_ERR_UNSUPPORTED;
+  for (const fp4_tensor* o : {out, out_t}) {
+    if (!o->codes || !o->scales) return FP4_ERR_NULL;
+    if (!aligned16(o->codes) || !aligned16(o->scales)) return FP4_ERR_ALIGN;
+  }
+  const bool nv = out->fmt == FP4_NVFP4;
+  if (nv && (!out->amax || !out->tscale || !out_t->tscale)) return FP4_ERR_NULL;
+  const int B = block_of(out->fmt);
+  if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
+  if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
+  if ((R + 127) / 128 * ((C + 127) / 128) > 0x7FFFFFFF) return FP4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nv && !amax_ready) {
+    fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
+    st = hip_status();
+    if (st != FP4_OK) return st;
+  }
+  Quant2dArgs a;
+  a.src = src;
+  a.bf16 = src_t == FP4_DTYPE_BF16;
+  a.R = R;
+  a.C = C;
+  a.ld = ld;
+  a.fmt = out->fmt;
+  a.sr = rnd == FP4_SR;
+  a.seed = seed;
+  a.offset = index_offset;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.codes_t = out_t->codes;
+  a.scales_t = out_t->scales;
+  a.amax = out->amax;
+  a.tscale = out->tscale;
+  a.tscale_t = out_t->tscale;
+  a.amax_copy = (nv && out_t->amax && out_t->amax != out->amax) ? out_t->amax : nullptr;
+  fp4i_launch_quant_2d(a, s);
+  out->rows = R;
+  out->cols = C;
+  out_t->rows = C;
+  out_t->cols = R;
+  return hip_status();
+}
+
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
                           fp4_stream_t stream) {
   if (!q || !dst) return FP4_ERR_NULL;

@@ -40,6 +40,21 @@ struct DualArgs {
   double *noise_c, *noise_r;       // null, or receive += (sum x^2, sum (xhat - x)^2)
 };
 
+// Two-dimensional block quantization (fp4_quantize_2d): codes/scales blocks
+// along C ([R][C]), codes_t/scales_t the transpose ([C][R]).
+struct Quant2dArgs {
+  const void* src;
+  bool bf16;
+  int64_t R, C, ld;
+  int fmt;
+  bool sr;
+  uint64_t seed, offset;
+  uint8_t *codes, *scales, *codes_t, *scales_t;
+  const float* amax;               // NVFP4: the tensor amax (already computed)
+  float *tscale, *tscale_t;        // NVFP4: receive s_g
+  float* amax_copy;                // NVFP4: receives a copy of the amax, or null
+};
+
 struct GemmArgs {
   const uint8_t* a_codes;
   const uint8_t* a_scales;
@@ -69,6 +84,7 @@ void fp4i_launch_amax_pair(const void* src, bool bf16, int64_t R, int64_t C, int
                            float* amax_r, hipStream_t s);
 void fp4i_launch_quant(const QuantArgs& a, hipStream_t s);
 void fp4i_launch_quant_dual(const DualArgs& a, hipStream_t s);
+void fp4i_launch_quant_2d(const Quant2dArgs& a, hipStream_t s);
 void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);

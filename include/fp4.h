@@ -216,6 +216,27 @@ fp4_status fp4_quantize_dual_noise(const void* src, fp4_dtype src_t, int64_t R, 
                                    int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
                                    double* noise_cols, double* noise_rows, fp4_stream_t stream);
 
+/* Two-dimensional block quantization (Robots Atlas, "FP4", How it works:
+ * two-dimensional quantization among the stabilizers of FP4 training): one
+ * scale per B x B block of the R x C source (16 x 16 NVFP4, 32 x 32 MXFP4),
+ * from the block's amax by the same rule as a 1-D block, so the matrix and its
+ * transpose are one quantization (a weight quantized once serves the forward
+ * GEMM, blocked along K, and dgrad, blocked along N).
+ *   out     R x C, blocks along C; every row of a block carries its byte.
+ *   out_t   C x R, blocks along R: exactly the transpose of out.
+ *   rnd     RTN, or SR with element index = row-major position in the R x C
+ *           source + index_offset for both outputs (unlike fp4_quantize with
+ *           FP4_AXIS_ROWS, whose index follows the transposed orientation).
+ *   amax_ready  NVFP4: 1 if *out->amax holds the tensor amax, 0 to compute it;
+ *           *out_t->amax, when another scalar, receives a copy; both tscale
+ *           scalars receive s_g.
+ * Requires: same fmt on both, had_on 0 on both (FP4_ERR_UNSUPPORTED); R and C
+ * multiples of B; C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned;
+ * SR index_offset % 8 == 0. Errors as fp4_quantize. */
+fp4_status fp4_quantize_2d(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                           fp4_rounding rnd, uint64_t seed, uint64_t index_offset, int amax_ready,
+                           fp4_tensor* out, fp4_tensor* out_t, fp4_stream_t stream);
+
 /* Dequantize q to dst (device, q->rows x q->cols row-major, leading dimension
  * ld >= cols, FP32 or bf16):
  *   NVFP4: (e2m1 * sdec) * s_g, the last product rounded once to FP32;

@@ -160,6 +160,31 @@ def test_noise_entry_points_reject_bad_arguments(fp4):
                                      ctypes.byref(dr), 0x60000, None, None) == 2
 
 
+Q2D_BAD = [
+    # (src, R, C, ld, rnd, offset, out overrides, out_t overrides, expected)
+    (0, 64, 128, 128, 0, 0, {}, {}, 1),
+    (0x1000, 40, 128, 128, 0, 0, {}, {}, 2),            # R not a multiple of 16
+    (0x1000, 64, 136, 136, 0, 0, {}, {}, 2),            # C not a multiple of 16
+    (0x1000, 64, 80, 128, 0, 0, {"fmt": 1}, {"fmt": 1}, 2),  # C not a multiple of 32 (MXFP4)
+    (0x1000, 64, 128, 128, 0, 0, {"fmt": 1}, {}, 4),    # formats differ
+    (0x1000, 64, 128, 128, 0, 0, {"had_on": 1}, {}, 4),  # no rotation with 2-D blocks
+    (0x1000, 64, 128, 128, 1, 4, {}, {}, 3),            # SR offset % 8
+    (0x1000, 64, 128, 128, 2, 0, {}, {}, 5),            # bad rounding
+    (0x1000, 64, 128, 128, 0, 0, {}, {"codes": 0}, 1),
+    (0x1000, 64, 128, 128, 0, 0, {}, {"tscale": 0}, 1),
+    (0x1000, 64, 128, 128, 0, 0, {"scales": 0x20008}, {}, 3),
+]
+
+
+@pytest.mark.parametrize("case", Q2D_BAD)
+def test_quantize_2d_rejects_bad_arguments(fp4, case):
+    src, R, C, ld, rnd, off, over, over_t, want = case
+    d, dt = _t(fp4, **over), _t(fp4, **over_t)
+    st = fp4.lib().fp4_quantize_2d(src, 1, R, C, ld, rnd, 0, off, 1, ctypes.byref(d), ctypes.byref(dt), None)
+    assert st == want
+    assert fp4.lib().fp4_quantize_2d(0x1000, 1, 64, 128, 128, 0, 0, 0, 1, ctypes.byref(d), None, None) == 1
+
+
 AMAX_H16_BAD = [
     # (src, dtype, R, C, ld, axis, amax, expected)
     (0, 1, 64, 128, 128, 0, 0x30000, 1),

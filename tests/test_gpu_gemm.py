@@ -103,6 +103,26 @@ def test_nvfp4_rotated_wgrad_end_to_end(fp4, orc):
     assert rel < 1.5 * rel_plain, (rel, rel_plain)
 
 
+def test_2d_weight_serves_forward_and_dgrad(fp4, orc):
+    """W quantized once with 16 x 16 blocks: the forward GEMM takes it blocked
+    along K, dgrad takes its transpose blocked along N; both match the oracle's
+    GEMMs of the oracle's 2-D quantization."""
+    import torch
+    T, N, K = 384, 256, 512
+    xh, wh, dyh = _data((T, K), 8, outliers=True), _data((N, K), 9, std=0.02), _data((T, N), 10)
+    qw, qwt = fp4.quantize_2d(to_device(wh))
+    qx = fp4.quantize(to_device(xh))
+    qdy = fp4.quantize(to_device(dyh), rnd=1, seed=4)
+    y = to_host(fp4.gemm(qx, qw, dtype=torch.float32))
+    dx = to_host(fp4.gemm(qdy, qwt, dtype=torch.float32))
+    ow, owt = orc.quantize_2d(wh)
+    for got, a, b, what in ((y, orc.quantize(xh), ow, "forward"),
+                            (dx, orc.quantize(dyh, rnd=1, seed=4), owt, "dgrad")):
+        ref, S = orc.gemm_ref(a, b)
+        ok, worst = orc.gemm_check(got, ref, S, "fp32")
+        assert ok, (what, worst)
+
+
 def _rows_of(q, rows):
     d = dict(q)
     d["codes"], d["scales"], d["rows"] = q["codes"][rows], q["scales"][rows], len(rows)

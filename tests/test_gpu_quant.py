@@ -351,3 +351,36 @@ def test_noise_monitor_full_size_gradient(fp4, orc):
     want_r = orc.quantize(xh, axis=1, rnd=1, seed=(2 << 8) | 2, noise=True)
     _assert_noise(nr, want_r["noise"], "dY rows")
     say("gradient / noise norm ratio", fp4.noise_ratio(nc), fp4.noise_ratio(nr))
+
+
+# ------------------------------------------------------ 2-D block quantization
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("shape,bf16", [((96, 1056), True), ((256, 256), True), ((160, 96), False),
+                                        ((32, 64), True), ((384, 4128), True)])
+def test_quantize_2d_matches_oracle(fp4, orc, fmt, rnd, shape, bf16):
+    B = 16 if fmt == 0 else 32
+    if shape[0] % B or shape[1] % B:
+        pytest.skip("2-D blocks need both dimensions blocked")
+    say("quantize_2d", shape, "fmt", fmt, "rnd", rnd, "bf16", bf16)
+    xh = _mixed(shape, 71 + shape[1], bf16)
+    want, want_t = orc.quantize_2d(xh, fmt=fmt, rnd=rnd, seed=31, index_offset=24)
+    q, qt = fp4.quantize_2d(to_device(xh), fmt=fmt, rnd=rnd, seed=31, index_offset=24)
+    assert_same_quant(q_to_host(q), want, "2-D, blocks along C")
+    assert_same_quant(q_to_host(qt), want_t, "2-D, transpose")
+
+
+def test_quantize_2d_full_size_weight(fp4, orc):
+    """The Llama-7B layer's W (11008 x 4096 bf16), 16 x 16 NVFP4 blocks, RTN."""
+    import torch
+    from fp4_fully_quantized_amd import workloads
+    say("quantize_2d full size W")
+    x = workloads.device_tensor("llama7b", "W")
+    q, qt = fp4.quantize_2d(x)
+    torch.cuda.synchronize()
+    got, got_t = q_to_host(q), q_to_host(qt)
+    xh = to_host(x)
+    del q, qt, x
+    want, want_t = orc.quantize_2d(xh)
+    assert_same_quant(got, want, "W 2-D")
+    assert_same_quant(got_t, want_t, "W^T 2-D")
