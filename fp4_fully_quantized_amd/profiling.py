@@ -81,7 +81,7 @@ def source_digest() -> str:
 # MI355X after `cd /tmp && export TMPDIR=/tmp` (OUT = their output folder).
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_bench -o bench -- "
-             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
              "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
@@ -103,7 +103,9 @@ GROUPS = [
     ("tensor amax", r"^k_amax<"),
     ("tensor amax of the values rotated down the columns", r"^k_amax_rot_rows<"),
     ("both orientations' amaxes, one rotated (one read)", r"^k_amax_pair<"),
+    ("2-D block quantize (both orientations)", r"^k_quant_2d<"),
 ]
+STEPS, WARMUP = 10, 3   # of the stats command
 
 
 def _trace_groups(trace_csv: str):
@@ -145,22 +147,35 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
         "",
         "One step = NVFP4 quantization of X, W and dY, each tensor read once for both of its orientations "
         "(X, W: RTN along K + SR along the other axis; dY: SR along both), the fwd GEMM (bf16 out), dgrad and "
-        "wgrad GEMMs (fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). 7 steps traced "
-        "(2 warm-up + 5 timed); torch kernels are the one-time input generation.",
+        f"wgrad GEMMs (fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). {WARMUP + STEPS} steps "
+        f"traced ({WARMUP} warm-up + {STEPS} timed), then the adjacent passes the benchmark times after the "
+        "step (`extras`: NVFP4 16-wide rotation of the wgrad operands with their amax pass, the noise-monitored "
+        "dY pass, the 2-D quantization of W), 2 warm-up + 10 timed calls each; torch kernels are the "
+        "one-time input generation.",
+        "",
+        "`avg us (timed)` (GEMMs, which only the step launches) leaves out the warm-up steps' launches (the "
+        "first launches of a run are slower while the clock settles); that is the figure to set against the "
+        "benchmark's HIP-event times.",
         "",
         "`k_gemm<0, 256, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *>` = MXFP4 GEMM (scaled FP4 MFMA); "
         "the last template flag = bf16 output.",
         "",
         "## Kernel groups (from the kernel trace)",
         "",
-        "| group | launches | avg us | min us | max us |",
-        "|---|---|---|---|---|",
+        "| group | launches | avg us | avg us (timed) | min us | max us |",
+        "|---|---|---|---|---|---|",
     ]
     for label, _ in GROUPS:
         d = groups[label]
         if d:
-            lines.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
-                         f"{max(d) / 1e3:.1f} |")
+            # Kernels launched only by the step (the GEMMs): drop the warm-up launches.
+            timed = "-"
+            if label.endswith("GEMM") or "GEMM (" in label:
+                per_step = len(d) // (WARMUP + STEPS)
+                t = d[per_step * WARMUP:]
+                timed = f"{sum(t) / len(t) / 1e3:.1f}"
+            lines.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {timed} | "
+                         f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
     lines += ["", "## Per kernel (`--stats` summary)", "", kernel_stats_table(stats_csv), ""]
     with open(os.path.join(profiles_dir, "llama7b_step_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines))
