@@ -19,8 +19,11 @@ using namespace fp4dev;
 constexpr int NV = 0;
 constexpr int MX = 1;
 
+// s_g = amax / 2688; 1 for an amax of 0 or below 2^-100 (such a tensor
+// quantizes to signed zeros instead of reaching 0/0 or an infinite reciprocal
+// through a zero or subnormal s_g).
 __device__ __forceinline__ float nv_tensor_scale(float amax) {
-  return amax == 0.0f ? 1.0f : amax / 2688.0f;
+  return amax < 0x1p-100f ? 1.0f : amax / 2688.0f;
 }
 
 // Block scale of one block with amax m. Returns the scale byte, sets the

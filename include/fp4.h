@@ -27,7 +27,8 @@
  *
  * Conventions (fixed where the pages are silent):
  *   E2M1 code  S|E1E0|M, bias 1; element 2t of a row in the low nibble of byte t.
- *   NVFP4      s_g = amax / 2688 (6 * 448; 1 when amax = 0); block byte = E4M3
+ *   NVFP4      s_g = amax / 2688 (6 * 448; 1 when amax < 2^-100, so a zero
+ *              or vanishingly small tensor quantizes to signed zeros); block byte = E4M3
  *              round-to-nearest-even, saturating at 448, of (amax_b / 6) / s_g;
  *              element v = x * (1 / (sdec * s_g)), the reciprocal rounded once.
  *   MXFP4      block exponent e = the smallest e with 6 * 2^e >= amax_b

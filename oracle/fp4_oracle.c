@@ -283,9 +283,16 @@ float o_tensor_amax(const void* src, int src_bf16, int64_t R, int64_t C, int64_t
  * FP32 tensor scale maps the tensor amax onto the product of the largest
  * E2M1 magnitude and the largest E4M3 value, s_g = amax / (6 * 448); an
  * all-zero tensor takes s_g = 1. */
+/* NVFP4 tensor scale (Robots Atlas "FP4", How it works: the per-tensor FP32
+ * scale of two-level scaling): amax / (6 * 448). Degenerate tensors: an amax
+ * of 0, or below 2^-100, takes s_g = 1. For such a tensor every block scale
+ * then encodes to E4M3 0 and every code is a signed zero; without the floor
+ * s_g could be 0 or subnormal and the block scale's reciprocal 0/0 or
+ * infinite. Above it, s_g >= 2^-112 and every nonzero decoded block scale
+ * times s_g stays a normal FP32 number. */
 static float nv_tensor_scale(float amax)
 {
-    if (amax == 0.0f) return 1.0f;
+    if (amax < 0x1p-100f) return 1.0f;
     return amax / 2688.0f;
 }
 

@@ -384,3 +384,28 @@ def test_quantize_2d_full_size_weight(fp4, orc):
     want, want_t = orc.quantize_2d(xh)
     assert_same_quant(got, want, "W 2-D")
     assert_same_quant(got_t, want_t, "W^T 2-D")
+
+
+# --------------------------------------------------------- degenerate magnitudes
+def _tiny(shape, seed, scale):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape) * scale).astype(np.float32)
+
+
+TINY = [1e-32, 2.0 ** -99, 1e-38, 3e-39]   # below the NVFP4 floor, just above it, FP32 subnormal range
+
+
+@pytest.mark.parametrize("scale", TINY)
+@pytest.mark.parametrize("fmt,axis", [(0, 0), (0, 1), (1, 0)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_tiny_and_subnormal_magnitudes(fp4, orc, scale, fmt, axis, bf16):
+    """Tensors near and inside FP32's subnormal range (bf16 inputs round to
+    bf16 subnormals): the tensor-scale floor and the block-scale rules agree
+    with the oracle bit for bit, in RTN and SR."""
+    say("tiny magnitudes", scale, "fmt", fmt, "axis", axis, "bf16", bf16)
+    x = _tiny((64, 256), 81, scale)
+    xh = orc.f32_to_bf16_bits(x) if bf16 else x
+    for rnd in (0, 1):
+        want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=5)
+        q = fp4.quantize(to_device(xh), axis=axis, fmt=fmt, rnd=rnd, seed=5)
+        assert_same_quant(q_to_host(q), want, f"tiny {scale} rnd {rnd}")

@@ -150,7 +150,7 @@ def test_rtn_error_bound(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("k", [-7, 3, 11])
+@pytest.mark.parametrize("k", [-95, -7, 3, 11])
 def test_power_of_two_scale_invariance(orc, fmt, k):
     x = _randn((16, 256), 3)
     q0 = orc.quantize(x, fmt=fmt)
@@ -171,6 +171,24 @@ def test_rows_axis_equals_cols_axis_of_the_transpose(orc, fmt, rnd, had):
     b = orc.quantize(np.ascontiguousarray(x.T), axis=orc.AXIS_COLS, fmt=fmt, rnd=rnd,
                      seed=9, had_on=had, had_signs=0x1234567)
     assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_vanishing_tensor_quantizes_to_signed_zeros(orc, rnd):
+    # NVFP4 amax below 2^-100: s_g = 1, every block byte 0, every code a signed zero
+    x = _randn((32, 64), 18) * np.float32(1e-32)
+    assert np.abs(x).max() < 2.0 ** -100
+    q = orc.quantize(x, fmt=0, rnd=rnd, seed=2)
+    assert q["sg"] == 1.0 and q["amax"] == float(np.abs(x).max())
+    assert (q["scales"] == 0).all()
+    u = unpack(q["codes"])
+    assert np.array_equal(u, np.where(np.signbit(x), 8, 0))
+    # just above the floor the tensor is quantized as usual (power-of-two invariance)
+    y = _randn((32, 64), 18)
+    k = -100 - int(np.floor(np.log2(np.abs(y).max())))
+    q0, q1 = orc.quantize(y, fmt=0), orc.quantize(y * np.float32(2.0 ** k), fmt=0)
+    assert q1["amax"] >= 2.0 ** -100
+    assert np.array_equal(q0["codes"], q1["codes"]) and np.array_equal(q0["scales"], q1["scales"])
 
 
 def test_bf16_input_equals_its_fp32_value(orc):
