@@ -250,7 +250,10 @@ fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64
 /* C[i][j] = alpha * sum_k A_hat[i][k] * B_hat[j][k] with FP32 accumulation,
  * where A_hat, B_hat are the dequantized operands (both blocked along the
  * shared contraction axis K), M = A->rows, N = B->rows, K = A->cols = B->cols,
- * alpha = (*A->tscale) * (*B->tscale) for NVFP4 and 1 for MXFP4.
+ * alpha = (*A->tscale) * (*B->tscale) for NVFP4 and 1 for MXFP4. alpha is
+ * one FP32 product applied to the FP32 accumulators: for operands whose
+ * tensor scales multiply below 2^-126 (both tensor amaxes below about 1e-15)
+ * it is subnormal or zero, and the output loses precision or becomes 0.
  *   MXFP4 runs on the gfx950 block-scaled FP4 MFMA with the E8M0 bytes as its
  *   scale operands. NVFP4 decodes e2m1 * E4M3 exactly into f16 in registers
  *   (at most 6 significant bits, magnitudes in [2^-10, 2688]) and runs the
