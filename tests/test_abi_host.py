@@ -214,6 +214,8 @@ GEMM_BAD = [
     ({"tscale": 0}, {}, 1, 128, 1),
     ({"codes": 0x10008}, {}, 1, 128, 3),
     ({}, {}, 3, 128, 5),
+    ({"rows": 2 ** 20, "cols": 4096}, {"cols": 4096}, 1, 128, 2),   # A codes reach 2^31 bytes
+    ({"cols": 4096}, {"rows": 2 ** 20, "cols": 4096}, 1, 2 ** 20, 2),  # B codes reach 2^31 bytes
 ]
 
 

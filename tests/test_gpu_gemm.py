@@ -188,3 +188,34 @@ def test_full_size_gemm_sampled_rows(fp4, orc, wl, which, out):
     ok, worst = orc.gemm_check(yh, ref, S, out)
     say("worst error / bound", worst)
     assert ok, worst
+
+
+def test_gemm_at_the_operand_size_limit(fp4, orc):
+    """The largest A the ABI accepts (codes just below 2^31 bytes: M = 1048575
+    rows at K = 4096) against a ragged N = 200, NVFP4, FP32 out; operands are
+    random codes and E4M3 scale bytes (the GEMM's own inputs), checked on
+    sampled rows including the last row tile."""
+    import torch
+    M, N, K = (2 ** 31 - 1) // 2048, 200, 4096
+    say("gemm at the size limit", M, N, K)
+    rng = np.random.default_rng(91)
+
+    def operand(rows, seed):
+        r = np.random.default_rng(seed)
+        q = {"codes": r.integers(0, 256, (rows, K // 2), dtype=np.uint8),
+             "scales": r.integers(0x30, 0x48, (rows, K // 16), dtype=np.uint8),
+             "fmt": 0, "rows": rows, "cols": K, "amax": 1.0, "sg": 0.5 if seed % 2 else 0.25}
+        return q
+
+    qa, qb = operand(M, 3), operand(N, 4)
+    A, B = q_from_oracle(qa), q_from_oracle(qb)
+    y = fp4.gemm(A, B, dtype=torch.float32)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(M - 300, M), rng.integers(0, M, 64)]))
+    yh = to_host(y[torch.from_numpy(rows).cuda()])
+    del y, A
+    sub = dict(qa)
+    sub["codes"], sub["scales"], sub["rows"] = qa["codes"][rows], qa["scales"][rows], len(rows)
+    ref, S = orc.gemm_ref(sub, qb)
+    ok, worst = orc.gemm_check(yh, ref, S, "fp32")
+    say("worst error / bound", worst)
+    assert ok, worst
