@@ -15,7 +15,9 @@
 //   e2m1 * sdec has at most 6 significant bits and lies in [2^-10, 2688], so
 //   it is exact in f16: codes are decoded with v_cvt_scalef32_pk_f16_fp4
 //   (scale 1), multiplied by sdec with v_pk_mul_f16 (exact), and fed to
-//   v_mfma_f32_32x32x16_f16. alpha = s_gA * s_gB is applied in the epilogue.
+//   v_mfma_f32_32x32x16_f16; the decode of the next substep's operands is
+//   interleaved with the current substep's MFMAs. alpha = s_gA * s_gB is
+//   applied in the epilogue.
 //   For the f16 MFMA the K order inside an instruction is free as long as A
 //   and B agree: lane half g of substep s carries K values 32g + 8s .. +7 of a
 //   64-value group, so each lane reads 16 contiguous bytes per group.
@@ -52,6 +54,7 @@ constexpr int WM = 128, WN = 128;
 constexpr int FM = 4, FN = 4;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
@@ -323,6 +326,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
       }
     }
   } else {
+    // Chunk pair c2 of a K tile = 64 K values = 4 substeps of K = 16. The
+    // operands of substep t + 1 are decoded (e2m1 -> f16, times the block's
+    // E4M3 scale) while the 16 MFMAs of substep t run, a few VALU after each
+    // MFMA, so the decode issues under the matrix pipe instead of in bursts
+    // between MFMAs.
     constexpr int NC = BK / 64;                          // chunk pairs; each is 4 substeps of K=16
     constexpr int PER = (C::CODE_LOADS + NC - 2) / (NC - 1);
     uint32_t sw[FM + FN][2];                             // scale words of the tile (A frags, then B)
@@ -344,31 +352,41 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
 #pragma unroll
       for (int f = 0; f < FM + FN; ++f) raw[dst][f] = frag(L, f < FM ? arow[f] : brow[f - FM], g + 2 * c2);
     };
+    // The two E4M3 scales of chunk pair c2 (blocks 2c, 2c+1 of chunk c) as one
+    // exact f16 pair per fragment; the multiplies broadcast one half.
+    auto scales_of = [&](int c2, v2h* sd) {
+#pragma unroll
+      for (int f = 0; f < FM + FN; ++f)
+        sd[f] = (c2 & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[f][c2 >> 1], 1.0f, true)
+                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[f][c2 >> 1], 1.0f, false);
+    };
+    auto decode = [&](const uint4* R, const v2h* sd, int s, v8h* op) {
+#pragma unroll
+      for (int f = 0; f < FM + FN; ++f) {
+        const uint32_t w = s == 0 ? R[f].x : s == 1 ? R[f].y : s == 2 ? R[f].z : R[f].w;
+        const v2h sd2 = (s >> 1) ? sd[f].yy : sd[f].xx;
+        const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
+        const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
+        const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
+        const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
+        op[f] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      }
+    };
     read_scales(lds_s[0]);
     read_raw(lds_c[0], 0, 0);
+    v2h sdc[FM + FN];
+    v8h op[FM + FN];
+    scales_of(0, sdc);
+    decode(raw[0], sdc, 0, op);
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
       const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
-      uint32_t sw_cur[FM + FN][2];
 #pragma unroll
       for (int c2 = 0; c2 < NC; ++c2) {
         const int cur = c2 & 1;
-        if (c2 == 0) {
-#pragma unroll
-          for (int f = 0; f < FM + FN; ++f) { sw_cur[f][0] = sw[f][0]; sw_cur[f][1] = sw[f][1]; }
-        }
-        // The two E4M3 scales of this chunk pair (blocks 2c, 2c+1 of chunk c), as f16 pairs.
-        v2h sd[FM + FN][2];
-#pragma unroll
-        for (int f = 0; f < FM + FN; ++f) {
-          const uint32_t w = sw_cur[f][c2 >> 1];
-          const float lo = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 2) : __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-          const float hi = (c2 & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)w, 3) : __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-          sd[f][0] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(lo, lo));
-          sd[f][1] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(hi, hi));
-        }
         if (c2 == NC - 1) {
           __syncthreads();
+          // first operands and the scales of tile kt+1 (its buffer is complete after the barrier)
           read_scales(lds_s[buf ^ 1]);
           read_raw(lds_c[buf ^ 1], 0, cur ^ 1);
         } else {
@@ -380,22 +398,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          v8h op[FM + FN];
+          v8h opn[FM + FN];
+          if (s < 3) {
+            decode(raw[cur], sdc, s + 1, opn);
+          } else {
+            // first substep of the next chunk pair (or of tile kt+1)
+            v2h sdn[FM + FN];
+            scales_of(c2 == NC - 1 ? 0 : c2 + 1, sdn);
+            decode(raw[cur ^ 1], sdn, 0, opn);
 #pragma unroll
-          for (int f = 0; f < FM + FN; ++f) {
-            const uint32_t w = s == 0 ? raw[cur][f].x : s == 1 ? raw[cur][f].y : s == 2 ? raw[cur][f].z : raw[cur][f].w;
-            const v2h sd2 = sd[f][s >> 1];
-            const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sd2;
-            const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sd2;
-            const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sd2;
-            const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sd2;
-            op[f] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+            for (int f = 0; f < FM + FN; ++f) sdc[f] = sdn[f];
           }
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[FM + j], op[i], acc[i][j], 0, 0, 0);
+          // The next substep's decode (64 VALU: 8 fragments x 4 converts + 4
+          // multiplies) in groups of five after the MFMAs, so it is done by the
+          // 13th MFMA and the last ones leave room for the LDS and memory work
+          // (groups of 4 and 6 measured slower, 3 much slower).
+#pragma unroll
+          for (int m = 0; m < FM * FN; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
+          }
+#pragma unroll
+          for (int f = 0; f < FM + FN; ++f) op[f] = opn[f];
         }
       }
     }
