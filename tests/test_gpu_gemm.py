@@ -219,3 +219,44 @@ def test_gemm_at_the_operand_size_limit(fp4, orc):
     ok, worst = orc.gemm_check(yh, ref, S, "fp32")
     say("worst error / bound", worst)
     assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out,pad", [("fp32", 4), ("fp32", 1), ("bf16", 8), ("bf16", 3)])
+def test_gemm_into_a_strided_output(fp4, orc, fmt, out, pad):
+    """Output with a leading dimension ldc = N + pad: 16-byte aligned rows
+    (pad 4 fp32 / 8 bf16) take the staged row-store epilogue, the others the
+    element-wise one; the padding columns stay untouched."""
+    import torch
+    M, N, K = 320, 256, 512
+    say("gemm strided output", fmt, out, pad)
+    qa = orc.quantize(_data((M, K), 11, outliers=True), fmt=fmt)
+    qb = orc.quantize(_data((N, K), 12, std=0.02), fmt=fmt)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    full = torch.full((M, N + pad), 7.0, dtype=dt, device="cuda")
+    fp4.gemm(q_from_oracle(qa), q_from_oracle(qb), out=full[:, :N])
+    yh = to_host(full)
+    if out == "bf16":
+        yh = orc.bf16_bits_to_f32(yh)
+    assert (yh[:, N:] == 7.0).all()
+    ref, S = orc.gemm_ref(qa, qb)
+    ok, worst = orc.gemm_check(yh[:, :N], ref, S, out)
+    assert ok, worst
+
+
+def test_mxfp4_rotated_wgrad_end_to_end(fp4, orc):
+    """MXFP4 wgrad with both operands rotated 32-wide along the tokens by the
+    GPU quantizer (ROWS axis, SR): equal to the oracle's GEMM of the oracle's
+    quantizations."""
+    import torch
+    T, N, K = 512, 192, 256
+    dyh, xh = _data((T, N), 13), _data((T, K), 14, outliers=True)
+    signs = orc.hadamard_signs(22)
+    a = fp4.quantize(to_device(dyh), axis=1, fmt=1, rnd=1, seed=2, had_signs=signs)
+    b = fp4.quantize(to_device(xh), axis=1, fmt=1, rnd=1, seed=3, had_signs=signs)
+    y = to_host(fp4.gemm(a, b, dtype=torch.float32))
+    qa = orc.quantize(dyh, axis=1, fmt=1, rnd=1, seed=2, had_on=True, had_signs=signs)
+    qb = orc.quantize(xh, axis=1, fmt=1, rnd=1, seed=3, had_on=True, had_signs=signs)
+    ref, S = orc.gemm_ref(qa, qb)
+    ok, worst = orc.gemm_check(y, ref, S, "fp32")
+    assert ok, worst

@@ -107,14 +107,29 @@ def test_nvfp4_hadamard_with_a_given_amax(fp4, orc):
     assert_same_quant(q_to_host(q), want, "rows, rotated, given amax")
 
 
-def test_strided_source(fp4, orc):
-    import torch
-    xh = _mixed((64, 1024), 4)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("kind", ["cols", "rows", "dual", "2d"])
+def test_strided_source(fp4, orc, fmt, kind):
+    """A column window of a wider matrix (leading dimension 1024 > 512 columns)
+    in every quantize entry point."""
+    xh = _mixed((96, 1024), 4)
     full = to_device(xh)
-    view = full[:, 256:768]                      # leading dimension 1024, 512 columns
-    want = orc.quantize(np.ascontiguousarray(xh[:, 256:768]), fmt=1, rnd=1, seed=1)
-    q = fp4.quantize(view, fmt=1, rnd=1, seed=1)
-    assert_same_quant(q_to_host(q), want, "strided")
+    view = full[:, 256:768]
+    sub = np.ascontiguousarray(xh[:, 256:768])
+    say("strided source", kind, "fmt", fmt)
+    if kind in ("cols", "rows"):
+        axis = 0 if kind == "cols" else 1
+        want = orc.quantize(sub, axis=axis, fmt=fmt, rnd=1, seed=1)
+        assert_same_quant(q_to_host(fp4.quantize(view, axis=axis, fmt=fmt, rnd=1, seed=1)), want, kind)
+    elif kind == "dual":
+        qc, qr = fp4.quantize_dual(view, fmt=fmt, rnd_cols=0, rnd_rows=1, seed_rows=3)
+        assert_same_quant(q_to_host(qc), orc.quantize(sub, axis=0, fmt=fmt), "dual cols")
+        assert_same_quant(q_to_host(qr), orc.quantize(sub, axis=1, fmt=fmt, rnd=1, seed=3), "dual rows")
+    else:
+        q, qt = fp4.quantize_2d(view, fmt=fmt, rnd=1, seed=5)
+        w, wt = orc.quantize_2d(sub, fmt=fmt, rnd=1, seed=5)
+        assert_same_quant(q_to_host(q), w, "2-D")
+        assert_same_quant(q_to_host(qt), wt, "2-D transpose")
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
