@@ -111,7 +111,8 @@ fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64
   const bool two_amax = nv && (had_c || had_r);
   if (nv && (!out_cols->amax || !out_cols->tscale || !out_rows->tscale)) return FP4_ERR_NULL;
   if (two_amax && !out_rows->amax) return FP4_ERR_NULL;
-  if (two_amax && out_rows->amax == out_cols->amax) return FP4_ERR_UNSUPPORTED;
+  if (two_amax && (out_rows->amax == out_cols->amax || out_rows->tscale == out_cols->tscale))
+    return FP4_ERR_UNSUPPORTED;
   const int B = block_of(out_cols->fmt);
   if (R % B != 0 || C % B != 0) return FP4_ERR_SHAPE;
   if ((rnd_cols == FP4_SR && index_offset_cols % 8 != 0) || (rnd_rows == FP4_SR && index_offset_rows % 8 != 0))

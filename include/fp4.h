@@ -174,10 +174,11 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
  *                is another scalar, receives a copy; both tscale scalars
  *                receive s_g.
  *                NVFP4 with had_on in either descriptor: the two orientations'
- *                values have different amaxes, so out_rows->amax must be its
- *                own scalar (FP4_ERR_NULL if NULL, FP4_ERR_UNSUPPORTED if it is
- *                out_cols->amax); 1 if each already holds its orientation's
- *                amax, 0 to compute both first; each tscale receives its own s_g.
+ *                values have different amaxes, so out_rows->amax and
+ *                out_rows->tscale must be scalars of their own (FP4_ERR_NULL if
+ *                NULL, FP4_ERR_UNSUPPORTED if shared with out_cols); 1 if each
+ *                amax already holds its orientation's amax, 0 to compute both
+ *                first; each tscale receives its own s_g.
  * The two descriptors must have the same fmt; had_on and had_signs are each
  * descriptor's own. Requires: R, C >= 1, both multiples of B; C % 8 == 0;
  * ld >= C and ld % 8 == 0; src 16-byte aligned. Errors as fp4_quantize. */

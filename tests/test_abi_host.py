@@ -120,6 +120,7 @@ DUAL_BAD = [
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"had_on": 1}, 4),
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {}, {"had_on": 1}, 4),
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {"had_on": 1}, {"amax": 0}, 1),
+    (0x1000, 1, 64, 128, 128, 0, 0, 1, 0, {}, {"had_on": 1, "amax": 0x30008}, 4),  # shared tscale
     (0x1000, 1, 64, 128, 128, 1, 4, 1, 0, {}, {}, 3),          # SR offset % 8 (cols)
     (0x1000, 1, 64, 128, 128, 0, 0, 1, 12, {}, {}, 3),         # SR offset % 8 (rows)
     (0x1000, 1, 64, 128, 128, 2, 0, 1, 0, {}, {}, 5),          # bad rounding
