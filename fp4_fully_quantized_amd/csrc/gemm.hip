@@ -426,6 +426,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
 #pragma unroll
           for (int f = 0; f < FM + FN; ++f) op[f] = opn[f];
         }
+        // One scheduling region per chunk pair (128 groups): as one region, the
+        // K tile's 512 groups took the scheduler over ten minutes to place.
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

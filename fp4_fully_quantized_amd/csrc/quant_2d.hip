@@ -51,8 +51,9 @@ __global__ __launch_bounds__(256) void k_quant_2d(
       if (amax_copy) *amax_copy = a;
     }
   }
-  const uint32_t tr = blockIdx.x / tiles_c;
-  const uint32_t tc = blockIdx.x - tr * tiles_c;
+  const uint32_t ti = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const uint32_t tr = ti / tiles_c;
+  const uint32_t tc = ti - tr * tiles_c;
   const int64_t r0 = (int64_t)tr * T;
   const int64_t c0 = (int64_t)tc * T;
   const int tid = threadIdx.x;

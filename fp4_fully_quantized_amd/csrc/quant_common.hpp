@@ -132,4 +132,15 @@ __device__ __forceinline__ void noise_reduce(double g, double e, double* out) {
   }
 }
 
+// The dispatcher hands workgroups to the 8 XCDs in turn (workgroup b to XCD
+// b % 8), each XCD with its own L2. This maps workgroup b to a tile index so
+// that every XCD takes one contiguous range of the n tiles: row-major
+// neighbours, whose partial output lines (half-line code runs, 8-byte scale
+// runs) complete each other, then meet in one L2 instead of being written
+// back as separate partial lines. A bijection on [0, n).
+__device__ inline uint32_t xcd_contiguous_tile(uint32_t b, uint32_t n) {
+  const uint32_t x = b % 8, l = b / 8, per = n / 8, rem = n % 8;
+  return x * per + (x < rem ? x : rem) + l;
+}
+
 }  // namespace fp4q

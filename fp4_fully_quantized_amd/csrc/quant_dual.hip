@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_quant_dual(
   // over the tiles.
   const uint32_t n_it = MON ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 1u;
   for (uint32_t it = 0; it < n_it; ++it) {
-    const uint32_t ti = blockIdx.x + it * gridDim.x;
+    const uint32_t ti = MON ? blockIdx.x + it * gridDim.x : xcd_contiguous_tile(blockIdx.x, ntiles);
     const uint32_t tr = ti / tiles_c;
     const uint32_t tc = ti - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * T;
