@@ -18,6 +18,10 @@ read of the tensor (fp4_quantize_dual); `--separate-passes` runs them as
 separate fp4_quantize calls instead (same outputs).
 
 Printed: one JSON line. `value` = GEMM FLOPs of the step / step time (TFLOP/s).
+Quantize records give GB/s of algorithmic bytes, as a fraction of 8 TB/s
+(`frac_hbm`) and of a 1 GiB device copy measured in the same run
+(`frac_copy`, `hbm_copy_GBps`); `per_op_cold` times the step's quantize calls
+with the caches evicted before each call.
 `roofline` is for the dominant kernel (the NVFP4 GEMM), timed with HIP events
 on the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded
 sample of the same step and scales it to the same unit.
@@ -165,8 +169,11 @@ def make_extras(fp4, X, W, dY, signs16):
     return ops, q
 
 
-def time_ops(ops, steps, warmup):
-    """Per-op records (HIP events around each call on the current stream)."""
+def time_ops(ops, steps, warmup, flush=None):
+    """Per-op records (HIP events around each call on the current stream).
+    With `flush` (a device buffer larger than the 256 MB last-level cache),
+    each timed call is preceded by a read of that buffer, so the call finds
+    none of its input in L2 or the memory-side cache."""
     import torch
 
     for _ in range(warmup):
@@ -177,12 +184,43 @@ def time_ops(ops, steps, warmup):
     torch.cuda.synchronize()
     for s in range(steps):
         for i, (_, _, fn, _) in enumerate(ops):
+            if flush is not None:
+                flush.sum()
             ev[s][i][0].record()
             fn()
             ev[s][i][1].record()
     torch.cuda.synchronize()
     return [op_record(name, kind, units, [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)])
             for i, (name, kind, _, units) in enumerate(ops)]
+
+
+def measure_copy_GBps(steps: int = 10) -> float:
+    """Device-to-device copy of 1 GiB with the runtime's own copy (one read
+    and one write of every byte): what a plain streaming pass reaches on this
+    GPU, the practical ceiling beside the 8 TB/s data-sheet figure."""
+    import torch
+
+    n = 1 << 29                                  # bf16 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    avg_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    del src, dst
+    return 2.0 * n * 2 / (avg_ms * 1e-3) / 1e9
+
+
+def add_copy_frac(records, copy_gbps):
+    for r in records:
+        if "GBps" in r:
+            r["frac_copy"] = round(r["GBps"] / copy_gbps, 3)
 
 
 def op_record(name, kind, units, times_ms):
@@ -326,6 +364,15 @@ def main():
     extra_ops, extra_q = make_extras(fp4, X, W, dY, fp4.fp4_hadamard_signs(4))
     extras = time_ops(extra_ops, args.steps, 2)
     del extra_ops, extra_q
+    # The step's quantize calls again, each after a 1 GiB read that evicts the
+    # caches (in the step, a tensor's second read -- the amax pass, then the
+    # quantize pass -- can hit the 256 MB memory-side cache).
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    cold = time_ops([o for o in ops if o[1] == "q"], args.steps, 2, flush=flush)
+    del flush
+    copy_gbps = measure_copy_GBps()
+    for recs in (per_op, extras, cold):
+        add_copy_frac(recs, copy_gbps)
 
     nv = [r for r, o in zip(per_op, ops) if o[1] == "g_nv"]
     nv_avg_ms = sum(r["avg_ms"] for r in nv) / len(nv)
@@ -367,7 +414,9 @@ def main():
             "quantize_launches": "separate" if args.separate_passes else "one read per NVFP4 tensor",
         },
         "quantize_GBps_aggregate": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "hbm_copy_GBps": round(copy_gbps, 1),
         "per_op": per_op,
+        "per_op_cold": cold,
         "extras": extras,
         "roofline": {
             "kernel": "NVFP4 GEMM (e2m1*E4M3 decoded exactly to f16, f16 MFMA)",

@@ -86,6 +86,9 @@ PROFILE_COMMANDS = {
              "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
              "-d OUT/pmc_write -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+    "util": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA "
+            "GRBM_GUI_ACTIVE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
+            "-d OUT/pmc_util -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o copy -- "
                   "python3 -m fp4_fully_quantized_amd.profiling copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o copy -- "
@@ -106,6 +109,74 @@ GROUPS = [
     ("2-D block quantize (both orientations)", r"^k_quant_2d<"),
 ]
 STEPS, WARMUP = 10, 3   # of the stats command
+PMC_STEPS, PMC_WARMUP = 1, 1   # of the counter commands
+CUS, SIMDS_PER_CU, XCDS = 256, 4, 8
+
+
+# The library's dispatches in one `bench.py --steps K --warmup W` run, in launch
+# order: (label, kernel-name regex, algorithmic bytes or FLOPs per dispatch,
+# elements x orientations a quantize or amax dispatch processes). The
+# benchmark runs the step W + K times, then the adjacent passes 2 + K times, then
+# the step's quantize calls 2 + K times with the caches evicted before each.
+TOKENS, D_IN, D_OUT = 32768, 4096, 11008
+_NX, _NW, _NY = TOKENS * D_IN, D_OUT * D_IN, TOKENS * D_OUT
+_DUAL = 2 + 2 * (0.5 + 1 / 16)      # bf16 read + two orientations of codes and E4M3 scales
+_MX = 2 + 0.5 + 1 / 32
+_GF = 2.0 * TOKENS * D_IN * D_OUT
+STEP_DISPATCHES = [
+    ("amax X", r"^k_amax<", 2 * _NX, _NX),
+    ("dual X (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NX, 2 * _NX),
+    ("amax W", r"^k_amax<", 2 * _NW, _NW),
+    ("dual W (RTN along K, SR along out)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NW, 2 * _NW),
+    ("NVFP4 GEMM fwd (bf16 out)", r"^k_gemm<0, 256, true>", _GF, 0),
+    ("amax dY", r"^k_amax<", 2 * _NY, _NY),
+    ("dual dY (SR both)", r"^k_quant_dual<0, 1, 1,", _DUAL * _NY, 2 * _NY),
+    ("NVFP4 GEMM dgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
+    ("NVFP4 GEMM wgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
+    ("MXFP4+Hadamard X", r"^k_quant_cols<1,", _MX * _NX, _NX),
+    ("MXFP4+Hadamard W", r"^k_quant_cols<1,", _MX * _NW, _NW),
+    ("MXFP4 GEMM fwd (bf16 out)", r"^k_gemm<1, 256, true>", _GF, 0),
+]
+EXTRA_DISPATCHES = [
+    ("amax dY rotated 16-wide along tokens", r"^k_amax_rot_rows<", 2 * _NY, _NY),
+    ("amax pair X (plain, rotated along tokens)", r"^k_amax_pair<", 2 * _NX, _NX),
+    ("dual X, 16-wide rotation along tokens", r"^k_quant_dual<0, 0, 1, true, false, true,", _DUAL * _NX, 2 * _NX),
+    ("amax pair dY (plain, rotated along tokens)", r"^k_amax_pair<", 2 * _NY, _NY),
+    ("dual dY, 16-wide rotation along tokens", r"^k_quant_dual<0, 1, 1, true, false, true,", _DUAL * _NY, 2 * _NY),
+    ("amax W (2-D)", r"^k_amax<", 2 * _NW, _NW),
+    ("2-D 16x16 W", r"^k_quant_2d<", _DUAL * _NW, 2 * _NW),
+    ("amax dY (monitored)", r"^k_amax<", 2 * _NY, _NY),
+    ("dual dY + noise monitor", r"^k_quant_dual<0, 1, 1, true, false, false, true>", _DUAL * _NY, 2 * _NY),
+]
+
+
+def label_dispatches(names, steps: int, warmup: int):
+    """Labels of a benchmark run's dispatches (kernel short names in launch
+    order, as filtered by the profiling commands), checked against the kernel
+    each position must run."""
+    import re
+
+    cold = [(l + " (cold)", rx, u, e) for l, rx, u, e in STEP_DISPATCHES if not rx.startswith("^k_gemm")]
+    expect = STEP_DISPATCHES * (warmup + steps) + EXTRA_DISPATCHES * (2 + steps) + cold * (2 + steps)
+    if len(names) != len(expect):
+        raise ValueError(f"{len(names)} dispatches, expected {len(expect)}")
+    for n, (l, rx, _, _) in zip(names, expect):
+        if not re.search(rx, n):
+            raise ValueError(f"dispatch {n!r} where {l} ({rx}) was expected")
+    return [(l, u, e) for l, _, u, e in expect]
+
+
+def _per_dispatch(csv_path: str):
+    """[(kernel name, {counter: value}, duration ns)] in dispatch order."""
+    import csv
+
+    d = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = int(r["Dispatch_Id"])
+        e = d.setdefault(k, [short_name(r["Kernel_Name"]), {},
+                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+        e[1][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [tuple(d[k]) for k in sorted(d)]
 
 
 def _trace_groups(trace_csv: str):
@@ -150,8 +221,10 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
         f"wgrad GEMMs (fp32 out), MXFP4+Hadamard fwd (quantize X, W; GEMM bf16 out). {WARMUP + STEPS} steps "
         f"traced ({WARMUP} warm-up + {STEPS} timed), then the adjacent passes the benchmark times after the "
         "step (`extras`: NVFP4 16-wide rotation of the wgrad operands with their amax pass, the noise-monitored "
-        "dY pass, the 2-D quantization of W), 2 warm-up + 10 timed calls each; torch kernels are the "
-        "one-time input generation.",
+        "dY pass, the 2-D quantization of W), 2 warm-up + 10 timed calls each, then the step's quantize "
+        "calls again with the caches evicted before each call (torch's reduction over a 1 GiB buffer), "
+        "2 + 10 calls each, and a 1 GiB device copy (`__amd_rocclr_copyBuffer`, 13 launches) that measures "
+        "the copy bandwidth; the other torch kernels are the one-time input generation.",
         "",
         "`avg us (timed)` (GEMMs, which only the step launches) leaves out the warm-up steps' launches (the "
         "first launches of a run are slower while the clock settles); that is the figure to set against the "
@@ -230,6 +303,87 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
     ]
     with open(os.path.join(profiles_dir, "nvfp4_gemm_llama7b_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines))
+    # ---- HBM bytes of the quantize-side dispatches
+    fd = _per_dispatch(os.path.join(out_dir, "pmc_fetch", "bench_counter_collection.csv"))
+    wd = _per_dispatch(os.path.join(out_dir, "pmc_write", "bench_counter_collection.csv"))
+    labels = label_dispatches([n for n, _, _ in fd], PMC_STEPS, PMC_WARMUP)
+    assert [n for n, _, _ in fd] == [n for n, _, _ in wd]
+    agg = {}
+    for (l, units, _), (_, fc, _), (_, wc, _) in zip(labels, fd, wd):
+        if l.startswith(("NVFP4 GEMM", "MXFP4 GEMM")):
+            continue
+        a = agg.setdefault(l, [0, 0.0, 0.0, units])
+        a[0] += 1
+        a[1] += fc["FETCH_SIZE"] * f_fac * 1024
+        a[2] += wc["WRITE_SIZE"] * w_fac * 1024
+    lines = [
+        "# HBM traffic of the quantize-side kernels (Llama-7B layer step and adjacent passes)",
+        "",
+        "Same counter runs and copy calibration as the NVFP4 GEMM traffic "
+        "(`nvfp4_gemm_llama7b_hbm_traffic.md`):",
+        "",
+        "```", cmd("fetch"), cmd("write"), cmd("copy_fetch"), cmd("copy_write"), "```",
+        "",
+        "Read and write bytes are FETCH_SIZE and WRITE_SIZE per dispatch (averaged over the run's launches of "
+        f"that dispatch), times the copy factors {f_fac:.3f} and {w_fac:.3f}. The counters see the traffic "
+        "between L2 and the memory fabric, so a read served by the 256 MB memory-side cache counts as a read "
+        "here. Algorithmic bytes: the bf16 input once, 0.5 B of codes and 1/16 B (NVFP4) or 1/32 B (MXFP4) "
+        "of scale per element and orientation written; an amax pass reads the input once. `(cold)` = the "
+        "benchmark's repeat of the step's quantize calls with the caches evicted before each call.",
+        "",
+        "| dispatch | launches | read MB | written MB | total MB | algorithmic MB | total / algorithmic |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for l, (n, fb, wb, units) in agg.items():
+        lines.append(f"| {l} | {n} | {fb / n / 1e6:.1f} | {wb / n / 1e6:.1f} | {(fb + wb) / n / 1e6:.1f} | "
+                     f"{units / 1e6:.1f} | {(fb + wb) / n / units:.3f} |")
+    lines.append("")
+    with open(os.path.join(profiles_dir, "quantize_llama7b_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines))
+
+    # ---- MFMA and VALU utilisation
+    ud = _per_dispatch(os.path.join(out_dir, "pmc_util", "bench_counter_collection.csv"))
+    labels = label_dispatches([n for n, _, _ in ud], PMC_STEPS, PMC_WARMUP)
+    simds = CUS * SIMDS_PER_CU
+    agg = {}
+    for (l, units, elems), (_, c, dur) in zip(labels, ud):
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        a = agg.setdefault(l, [0, 0.0, 0.0, 0.0, 0.0, 0.0, units])
+        a[0] += 1
+        a[1] += dur
+        a[2] += cyc / dur                                        # GHz
+        a[3] += c["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)
+        a[4] += 4 * c["SQ_ACTIVE_INST_VALU"] / (simds * cyc)
+        a[5] += c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] if elems == 0 else c["SQ_INSTS_VALU"] * 64 / elems
+    lines = [
+        "# MFMA and VALU utilisation of the Llama-7B layer step's kernels",
+        "",
+        "Command (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`):",
+        "",
+        "```", cmd("util"), "```",
+        "",
+        f"Per dispatch, averaged over the run's launches of that dispatch. GRBM_GUI_ACTIVE sums the "
+        f"{XCDS} XCDs' cycles, so the kernel's cycles are GRBM_GUI_ACTIVE / {XCDS} (the `clock` column, "
+        f"those cycles over the dispatch's duration, checks it). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+        f"({simds} SIMDs x cycles). VALU issue = 4 x SQ_ACTIVE_INST_VALU / ({simds} SIMDs x cycles): "
+        "SQ_ACTIVE_INST_VALU counts one per VALU instruction of a wave (it equals SQ_INSTS_VALU to 0.01% "
+        "here), and a wave64 instruction holds a 16-lane SIMD for 4 cycles, so 1.0 = every SIMD issuing "
+        "VALU work every cycle. `VALU / unit` = VALU instructions (MFMA included) per MFMA for GEMMs; "
+        "VALU instructions x 64 lanes per element and orientation for quantize passes (per element for "
+        "amax passes). Durations are longer than in unprofiled runs (counters serialise the dispatches). "
+        "A clock above the 2.4 GHz maximum means the counters' window outlasted the dispatch (short "
+        "kernels); the busy fractions of those rows are then low by that ratio.",
+        "",
+        "| dispatch | launches | avg us | clock GHz | MFMA busy | VALU issue | VALU / unit |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for l, (n, dur, ghz, mf, va, per, _) in agg.items():
+        lines.append(f"| {l} | {n} | {dur / n / 1e3:.1f} | {ghz / n:.2f} | {mf / n:.3f} | {va / n:.3f} | "
+                     f"{per / n:.2f} |")
+    lines.append("")
+    with open(os.path.join(profiles_dir, "llama7b_step_mfma_valu_utilisation.md"), "w") as f:
+        f.write("\n".join(lines))
+
     with open(os.path.join(profiles_dir, "traffic.json"), "w") as f:
         json.dump({"nv_gemm_bytes_per_launch": round(avg), "source_digest": source_digest(),
                    "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}, f, indent=1)
