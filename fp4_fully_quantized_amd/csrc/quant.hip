@@ -14,7 +14,8 @@
 // Memory-bound passes: every element is read once from HBM with 16-byte loads
 // and written once as a nibble; block scales are one byte per block.
 //  * k_amax        wave-strided 16-byte loads, per-lane max, wave and workgroup
-//                  reduction, one atomicMax per workgroup on the float bits;
+//                  reduction, an atomicMax on the float bits by each
+//                  workgroup whose max exceeds the value read there;
 //                  optionally of the 16-wide rotated values along rows (pairs
 //                  of lanes hold a block: one DPP butterfly stage).
 //  * k_amax_rot_rows  the same for the rotation down columns: each lane reads
@@ -59,8 +60,12 @@ __device__ __forceinline__ void hadamard16_lane_pair(float x[8], uint32_t signs,
   for (int i = 0; i < 8; ++i) x[i] = x[i] * 0.25f;
 }
 
-// Wave and workgroup max of m >= 0, one atomicMax per workgroup on the float
-// bits (monotone for non-negative floats).
+// Wave and workgroup max of m >= 0, then at most one atomicMax per workgroup
+// on the float bits (monotone for non-negative floats). The value at *amax
+// only grows, so a workgroup whose max does not exceed a value read from it
+// has nothing to add: reading first skips nearly all of the same-address
+// atomics, which the L2 serializes (with one per workgroup they set a floor
+// of about 30 us under every amax pass).
 __device__ __forceinline__ void amax_reduce(float m, float* amax) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -69,8 +74,9 @@ __device__ __forceinline__ void amax_reduce(float m, float* amax) {
   if (lane == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(b));
+    const float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    unsigned int* const a = reinterpret_cast<unsigned int*>(amax);
+    if (__float_as_uint(b) > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, __float_as_uint(b));
   }
 }
 
