@@ -110,7 +110,10 @@ __device__ __forceinline__ void noise8(const float x[8], uint32_t w, float bs, f
 // Launches with the noise monitor cap their grid at this many workgroups
 // (each then loops over several tiles or tasks): every workgroup ends with two
 // FP64 atomic adds per sum pair on the same two addresses, which serialize.
-constexpr uint32_t kNoiseGrid = 1024;
+// 768 = 3 workgroups on each of the 256 CUs, as many as the tiled kernels'
+// LDS lets run at once: a larger grid would leave its last workgroups a whole
+// loop of tiles to run alone after the others have finished.
+constexpr uint32_t kNoiseGrid = 768;
 
 // Workgroup sum of (g, e), then out[0] += g, out[1] += e. Every thread of the
 // workgroup calls it (it synchronizes).
