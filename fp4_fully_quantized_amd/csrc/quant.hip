@@ -535,7 +535,7 @@ void launch_cols(const QuantArgs& a, hipStream_t s) {
   const uint32_t spr = (uint32_t)((a.C + 511) / 512);
   const uint32_t ntasks = (uint32_t)(a.R * spr);
   uint32_t grid = strided_grid(ntasks);
-  if (a.noise && grid > kNoiseGrid) grid = kNoiseGrid;
+  if (a.noise) grid = noise_grid(k_quant_cols<FMT, RND, BF16, HAD, true>, grid);
   if (a.noise)
     hipLaunchKernelGGL((k_quant_cols<FMT, RND, BF16, HAD, true>), dim3(grid), dim3(256), 0, s,
                        a.src, a.C, a.ld, spr, ntasks, a.codes, a.scales, a.amax, a.tscale, a.seed,
@@ -553,7 +553,7 @@ void launch_rows_mon(const QuantArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.R + 255) / 256);
   const uint32_t scale_words = (a.R / B) % 4 == 0;
   const uint32_t ntiles = tiles_c * tiles_r;
-  const uint32_t grid = MON && ntiles > kNoiseGrid ? kNoiseGrid : ntiles;
+  const uint32_t grid = MON ? noise_grid(k_quant_rows<FMT, RND, BF16, HAD, MON>, ntiles) : ntiles;
   hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD, MON>), dim3(grid), dim3(256), 0, s, a.src, a.R,
                      a.C, a.ld, tiles_c, ntiles, a.codes, a.scales, a.amax, a.tscale, a.seed, a.offset,
                      a.signs, scale_words, a.noise);

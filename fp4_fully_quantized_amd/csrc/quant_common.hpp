@@ -107,13 +107,24 @@ __device__ __forceinline__ void noise8(const float x[8], uint32_t w, float bs, f
   }
 }
 
-// Launches with the noise monitor cap their grid at this many workgroups
-// (each then loops over several tiles or tasks): every workgroup ends with two
-// FP64 atomic adds per sum pair on the same two addresses, which serialize.
-// 768 = 3 workgroups on each of the 256 CUs, as many as the tiled kernels'
-// LDS lets run at once: a larger grid would leave its last workgroups a whole
-// loop of tiles to run alone after the others have finished.
-constexpr uint32_t kNoiseGrid = 768;
+// Grid of a noise-monitored launch over n tiles or tasks: as many workgroups
+// of 256 threads as the device runs at once (the kernel's occupancy per CU
+// times the CUs), at most n; each workgroup then loops over several tiles.
+// Every workgroup ends with two FP64 atomic adds per sum pair on the same two
+// addresses, which serialize, so the grid must not be one per tile; and a grid
+// beyond what runs at once leaves its last workgroups a whole loop of tiles to
+// run alone after the others have finished.
+template <typename Kernel>
+inline uint32_t noise_grid(Kernel kernel, uint32_t n) {
+  int per_cu = 0, dev = 0, cus = 0;
+  uint32_t g = 512;  // if the queries fail
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess &&
+      hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      per_cu > 0 && cus > 0)
+    g = (uint32_t)per_cu * (uint32_t)cus;
+  return n < g ? (n ? n : 1) : g;
+}
 
 // Workgroup sum of (g, e), then out[0] += g, out[1] += e. Every thread of the
 // workgroup calls it (it synchronizes).

@@ -11,18 +11,18 @@ namespace {
 
 // Both orientations from one read of the source. A workgroup takes a
 // 128 x 128 tile into LDS once (input format), then
-//  (a) quantizes it with blocks down its columns (the transposed, ROWS
-//      orientation), as k_quant_rows does: thread (b, q) handles block b of
-//      NCOL adjacent columns; codes and scales are staged in LDS per output
-//      row and written out after (b);
 //  (b) quantizes it with blocks along its rows (the COLS orientation): thread
 //      (row, half) takes 64 consecutive elements of one row (4 NVFP4 or 2
-//      MXFP4 blocks) and writes their codes (32 bytes) and scales directly.
+//      MXFP4 blocks) and writes their codes (32 bytes) and scales directly;
+//  (a) quantizes it with blocks down its columns (the transposed, ROWS
+//      orientation), as k_quant_rows does: thread (b, q) handles block b of
+//      NCOL adjacent columns; codes and scales are staged in LDS (over the
+//      tile, which is no longer read) per output row and written out last.
 // Each orientation has its own rounding mode, SR stream, rotation (on or off,
 // and its mask) and, for NVFP4, tensor amax (the rotated values' amax differs
 // per rotation axis); the results equal the two separate passes bit for bit.
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
-__global__ __launch_bounds__(256) void k_quant_dual(
+__device__ __forceinline__ void quant_dual_body(
     const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
     uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
@@ -40,8 +40,11 @@ __global__ __launch_bounds__(256) void k_quant_dual(
   constexpr int PITCH = T * ES + 8;       // row pitch in bytes (8-byte reads stay aligned)
   constexpr int SP = T / 2 + 4;           // staged code bytes per output row of (a)
   __shared__ __attribute__((aligned(16))) uint8_t tile[T * PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_c[T * SP];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_s[T * NB];
+  // (a)'s staged codes and scales reuse the tile once every thread has read
+  // its part of it: 33 KB of LDS per workgroup (bf16), four per CU.
+  static_assert(T * SP + T * NB <= T * PITCH && (T * SP) % 16 == 0, "staging fits in the tile");
+  uint8_t* const stage_c = tile;
+  uint8_t* const stage_s = tile + T * SP;
 
   float sg_c = 1.0f, sg_r = 1.0f;
   if constexpr (FMT == NV) {
@@ -87,67 +90,6 @@ __global__ __launch_bounds__(256) void k_quant_dual(
     const int64_t rows_here = R - r0 < T ? R - r0 : T;  // multiples of B
     const int64_t cols_here = C - c0 < T ? C - c0 : T;
 
-
-    // (a) blocks down the columns: output row c0 + cl, elements r0 ..
-    {
-      const int b = tid / TPB;
-      const int cl0 = (tid % TPB) * NCOL;
-      const int64_t rg = r0 + (int64_t)b * B;
-      float x[NCOL][B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
-        if constexpr (BF16) {
-          if constexpr (NCOL == 4) {
-            const uint2 w = *reinterpret_cast<const uint2*>(p);
-            x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
-          } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-            x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < NCOL; k += 2) {
-            const float2 w = *reinterpret_cast<const float2*>(p + 4 * k);
-            x[k][i] = w.x; x[k + 1][i] = w.y;
-          }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NCOL; ++k) {
-        const int cl = cl0 + k;
-        const int64_t cg = c0 + cl;
-        float* xk = x[k];
-        if constexpr (HR) hadamard_block<B>(xk, signs_r);
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
-        float rcp;
-        const uint32_t sbyte = block_scale<FMT>(m, sg_r, rcp);
-        uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
-        float bg = 0.0f, be = 0.0f;
-        const float bs = (MON && noise_r) ? scale_value<FMT>(sbyte) : 0.0f;
-#pragma unroll
-        for (int g = 0; g < B / 8; ++g) {
-          float v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
-          uint32_t cw;
-          if constexpr (RR == 0) {
-            cw = e2m1_rtn_pack8(v);
-          } else {
-            uint32_t h[4];
-            sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
-            cw = e2m1_sr_pack8(v, h);
-          }
-          sc[g] = cw;
-          if (MON && noise_r) noise8<FMT>(xk + 8 * g, cw, bs, sg_r, bg, be);
-        }
-        stage_s[cl * NB + b] = (uint8_t)sbyte;
-        ngr += (double)bg;
-        ner += (double)be;
-      }
-    }
 
     // (b) blocks along the rows: row r0 + row, elements c0 + 64 * half ..
     {
@@ -216,6 +158,70 @@ __global__ __launch_bounds__(256) void k_quant_dual(
         }
       }
     }
+    // (a) blocks down the columns: output row c0 + cl, elements r0 ..
+    {
+      const int b = tid / TPB;
+      const int cl0 = (tid % TPB) * NCOL;
+      const int64_t rg = r0 + (int64_t)b * B;
+      float x[NCOL][B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const uint8_t* p = &tile[(b * B + i) * PITCH + cl0 * ES];
+        if constexpr (BF16) {
+          if constexpr (NCOL == 4) {
+            const uint2 w = *reinterpret_cast<const uint2*>(p);
+            x[0][i] = bf16_lo(w.x); x[1][i] = bf16_hi(w.x); x[2][i] = bf16_lo(w.y); x[3][i] = bf16_hi(w.y);
+          } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+            x[0][i] = bf16_lo(w); x[1][i] = bf16_hi(w);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < NCOL; k += 2) {
+            const float2 w = *reinterpret_cast<const float2*>(p + 4 * k);
+            x[k][i] = w.x; x[k + 1][i] = w.y;
+          }
+        }
+      }
+      // The staging below overwrites the tile: every thread has read its
+      // part of it ((b) before, its own columns just now) past this barrier.
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NCOL; ++k) {
+        const int cl = cl0 + k;
+        const int64_t cg = c0 + cl;
+        float* xk = x[k];
+        if constexpr (HR) hadamard_block<B>(xk, signs_r);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
+        float rcp;
+        const uint32_t sbyte = block_scale<FMT>(m, sg_r, rcp);
+        uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
+        float bg = 0.0f, be = 0.0f;
+        const float bs = (MON && noise_r) ? scale_value<FMT>(sbyte) : 0.0f;
+#pragma unroll
+        for (int g = 0; g < B / 8; ++g) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = xk[8 * g + i] * rcp;
+          uint32_t cw;
+          if constexpr (RR == 0) {
+            cw = e2m1_rtn_pack8(v);
+          } else {
+            uint32_t h[4];
+            sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+            cw = e2m1_sr_pack8(v, h);
+          }
+          sc[g] = cw;
+          if (MON && noise_r) noise8<FMT>(xk + 8 * g, cw, bs, sg_r, bg, be);
+        }
+        stage_s[cl * NB + b] = (uint8_t)sbyte;
+        ngr += (double)bg;
+        ner += (double)be;
+      }
+    }
+
     __syncthreads();
 
     // write out (a): output row c0 + cl gets T/2 code bytes (8-byte pieces) and NB scale bytes.
@@ -258,6 +264,41 @@ __global__ __launch_bounds__(256) void k_quant_dual(
   }
 }
 
+// The kernels. The NVFP4 bf16 noise-monitored variants ask for 3 waves per
+// SIMD (at most 168 registers, which they fit without spilling), so that 3
+// workgroups run on each CU; the others need about 100 registers, or their
+// LDS (fp32 input) allows only 2 workgroups per CU anyway.
+template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
+__global__ __launch_bounds__(256) void k_quant_dual(
+    const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
+    uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
+    uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+    const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
+    float* tscale_r, float* amax_copy,
+    uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
+    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    double* noise_r) {
+  quant_dual_body<FMT, RC, RR, BF16, HC, HR, MON>(src, R, C, ld, tiles_c, ntiles, codes_c, scales_c, codes_r, scales_r,
+                                                  amax_c, amax_r, tscale_c, tscale_r, amax_copy, seed_c, off_c,
+                                                  signs_c, seed_r, off_r, signs_r, scale_words_c, scale_words_r,
+                                                  noise_c, noise_r);
+}
+template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
+__global__ __launch_bounds__(256, 3) void k_quant_dual_w3(
+    const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
+    uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
+    uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
+    const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
+    float* tscale_r, float* amax_copy,
+    uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
+    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    double* noise_r) {
+  quant_dual_body<FMT, RC, RR, BF16, HC, HR, MON>(src, R, C, ld, tiles_c, ntiles, codes_c, scales_c, codes_r, scales_r,
+                                                  amax_c, amax_r, tscale_c, tscale_r, amax_copy, seed_c, off_c,
+                                                  signs_c, seed_r, off_r, signs_r, scale_words_c, scale_words_r,
+                                                  noise_c, noise_r);
+}
+
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
 void launch_dual(const DualArgs& a, hipStream_t s) {
   constexpr int B = FMT == NV ? 16 : 32;
@@ -267,8 +308,12 @@ void launch_dual(const DualArgs& a, hipStream_t s) {
   const uint32_t words_c = FMT == NV ? (a.C / B) % 4 == 0 : (a.C / B) % 2 == 0;
   const uint32_t words_r = (a.R / B) % 4 == 0;
   const uint32_t ntiles = tiles_c * tiles_r;
-  const uint32_t grid = MON && ntiles > kNoiseGrid ? kNoiseGrid : ntiles;
-  hipLaunchKernelGGL((k_quant_dual<FMT, RC, RR, BF16, HC, HR, MON>), dim3(grid), dim3(256), 0,
+  const auto kernel = [] {
+    if constexpr (MON && FMT == NV && BF16) return k_quant_dual_w3<FMT, RC, RR, BF16, HC, HR, MON>;
+    else return k_quant_dual<FMT, RC, RR, BF16, HC, HR, MON>;
+  }();
+  const uint32_t grid = MON ? noise_grid(kernel, ntiles) : ntiles;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0,
                      s, a.src, a.R, a.C, a.ld, tiles_c, ntiles, a.codes_c, a.scales_c, a.codes_r, a.scales_r,
                      a.amax_c, a.amax_r, a.tscale_c, a.tscale_r, a.amax_copy, a.seed_c, a.offset_c,
                      a.signs_c, a.seed_r, a.offset_r, a.signs_r, words_c, words_r, a.noise_c,

@@ -19,7 +19,7 @@ def _names(steps, warmup):
               "k_quant_dual<0, 0, 1, true, false, true, false>", "k_amax_pair<true, false, true>",
               "k_quant_dual<0, 1, 1, true, false, true, false>", "k_amax<true, false>",
               "k_quant_2d<0, 0, true>", "k_amax<true, false>",
-              "k_quant_dual<0, 1, 1, true, false, false, true>"]
+              "k_quant_dual_w3<0, 1, 1, true, false, false, true>"]
     cold = [n for n in step if not n.startswith("k_gemm")]
     return step * (warmup + steps) + extras * (2 + steps) + cold * (2 + steps)
 
