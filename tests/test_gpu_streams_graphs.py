@@ -121,3 +121,52 @@ def test_graph_replays_match_eager(fp4):
             _same(got[0][k], eager[r][0][k])
         for a, b in zip(got[1:], eager[r][1:]):
             assert np.array_equal(a, b), f"replay {r}"
+
+
+def test_graph_replays_noise_monitor(fp4):
+    """The noise-monitored dual pass (its grid sized from the kernel's
+    occupancy at launch) captured with a fill kernel that clears the four
+    sums, replayed three times on new inputs: codes and scales equal the
+    eager run's bit for bit, the FP64 sums (added by atomics in any order)
+    to 1e-12 relative."""
+    import torch
+    say("graph capture, noise monitor")
+    T, F = 4096, 4096    # 1024 tiles of 128 x 128: more than run at once, so workgroups loop
+    dY = to_device(_data((T, F), 61, 1e-3))
+    Q = fp4.QTensor
+    qc, qr = Q(T, F, 0), Q(F, T, 0)
+    qr.amax = qc.amax
+    noise = torch.zeros(4, dtype=torch.float64, device="cuda")
+
+    def step(s=None):
+        noise.zero_()
+        fp4.fp4_quantize_dual_noise(dY, 1, 7, 0, 1, 8, 0, False, qc, qr, noise[0:2], noise[2:4], stream=s)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return q_to_host(qc), q_to_host(qr), noise.cpu().numpy().copy()
+
+    inputs = [_data((T, F), 71 + r, 1e-3) for r in range(3)]
+    eager = []
+    for h in inputs:
+        dY.copy_(to_device(h))
+        step()
+        eager.append(snapshot())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        step(s)
+    torch.cuda.synchronize()
+    for r, h in enumerate(inputs):
+        dY.copy_(to_device(h))
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        _same(got[0], eager[r][0])
+        _same(got[1], eager[r][1])
+        assert np.all(got[2] > 0)
+        np.testing.assert_allclose(got[2], eager[r][2], rtol=1e-12, atol=0)
