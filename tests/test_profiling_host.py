@@ -1,5 +1,7 @@
 """Host-side checks of the profiling summaries: the labelling of a benchmark
 run's dispatches, which every per-kernel counter table rests on."""
+import json
+
 import pytest
 
 from fp4_fully_quantized_amd import profiling as p
@@ -47,3 +49,66 @@ def test_label_dispatches_rejects_a_changed_run():
     swapped[0], swapped[1] = swapped[1], swapped[0]
     with pytest.raises(ValueError):
         p.label_dispatches(swapped, 1, 1)
+
+
+def _write_csv(path, header, rows):
+    import csv
+    import os
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _raw(name):
+    # as rocprofv3 prints it
+    return f"void (anonymous namespace)::{name}(void const*, long)"
+
+
+def test_summarize_on_synthetic_counters(tmp_path):
+    """summarize() on made-up counter files whose figures are known: every
+    quantize dispatch moves exactly its algorithmic bytes (ratio 1.000 after
+    the copy calibration), every dispatch runs at 2 GHz with the MFMA pipe half
+    busy and VALU issuing a quarter of the time."""
+    out, prof = tmp_path / "out", tmp_path / "profiles"
+    prof.mkdir()
+    names = _names(p.PMC_STEPS, p.PMC_WARMUP)
+    labels = p.label_dispatches(names, p.PMC_STEPS, p.PMC_WARMUP)
+    ph = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+          "End_Timestamp"]
+    fetch, write, util = [], [], []
+    cyc, dur = 2_000_000, 1_000_000          # cycles per XCD over 1 ms: 2 GHz
+    for i, (n, (_, units, elems)) in enumerate(zip(names, labels)):
+        t0 = 10_000_000 * (i + 1)
+        row = lambda c, v: [i + 1, _raw(n), 1024, c, v, t0, t0 + dur]
+        fetch.append(row("FETCH_SIZE", units * 0.6 / 2048))      # read bytes / 1024 / factor 2
+        write.append(row("WRITE_SIZE", units * 0.4 / 1024))      # written bytes / 1024 / factor 1
+        util += [row("GRBM_GUI_ACTIVE", 8 * cyc), row("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * cyc),
+                 row("SQ_ACTIVE_INST_VALU", 0.25 * 1024 * cyc / 4), row("SQ_INSTS_VALU", 1000.0),
+                 row("SQ_INSTS_MFMA", 100.0)]
+    _write_csv(str(out / "pmc_fetch" / "bench_counter_collection.csv"), ph, fetch)
+    _write_csv(str(out / "pmc_write" / "bench_counter_collection.csv"), ph, write)
+    _write_csv(str(out / "pmc_util" / "bench_counter_collection.csv"), ph, util)
+    copy = lambda c, v: [[k + 2, "__amd_rocclr_copyBuffer", 1, c, v, 0, 1] for k in range(3)]
+    _write_csv(str(out / "pmc_copy_fetch" / "copy_counter_collection.csv"), ph,
+               [[1, "fill", 1, "FETCH_SIZE", 7.0, 0, 1]] + copy("FETCH_SIZE", (1 << 30) / 1024 / 2))
+    _write_csv(str(out / "pmc_copy_write" / "copy_counter_collection.csv"), ph, copy("WRITE_SIZE", (1 << 30) / 1024))
+    trace = [[_raw(n), 0, 1000 * (k + 1)] for k, n in enumerate(_names(p.STEPS, p.WARMUP))]
+    _write_csv(str(out / "prof_bench" / "bench_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp",
+                                                                    "End_Timestamp"], trace)
+    _write_csv(str(out / "prof_bench" / "bench_kernel_stats.csv"),
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+               [[_raw("k_gemm<0, 256, true>"), 13, 2e6, 1.9e6, 2.1e6, 30.0]])
+    p.summarize(str(out), str(prof))
+
+    q = (prof / "quantize_llama7b_hbm_traffic.md").read_text()
+    rows = [l for l in q.splitlines() if l.startswith("| ") and not l.startswith("| dispatch")]
+    assert len(rows) == 8 + 9 + 8 and all(l.rstrip(" |").endswith("1.000") for l in rows)
+    u = 32768 * 11008 * (2 + 2 * (0.5 + 1 / 16))   # bf16 read + two orientations written
+    assert f"| dual dY (SR both) | 2 | {0.6 * u / 1e6:.1f} | {0.4 * u / 1e6:.1f} | {u / 1e6:.1f} | {u / 1e6:.1f} | 1.000 |" in q
+    u = (prof / "llama7b_step_mfma_valu_utilisation.md").read_text()
+    assert "| NVFP4 GEMM fwd (bf16 out) | 2 | 1000.0 | 2.00 | 0.500 | 0.250 | 10.00 |" in u
+    t = json.loads((prof / "traffic.json").read_text())
+    assert t["fetch_factor"] == 2.0 and t["write_factor"] == 1.0
+    assert t["nv_gemm_bytes_per_launch"] == round(p._GF * 1.0)
