@@ -205,14 +205,15 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
 
     stats_csv = os.path.join(out_dir, "prof_bench", "bench_kernel_stats.csv")
     trace_csv = os.path.join(out_dir, "prof_bench", "bench_kernel_trace.csv")
-    cmd = lambda k: PROFILE_COMMANDS[k].replace("OUT", "gpurun_out")
+    cmd = lambda k: PROFILE_COMMANDS[k]   # OUT: the folder the runs write their CSV files to
 
     # ---- kernel time of the step
     groups = _trace_groups(trace_csv)
     lines = [
         "# Kernel time of the Llama-7B layer step (bench.py)",
         "",
-        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first):",
+        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; "
+        "`OUT` = the folder the run writes its CSV files to):",
         "",
         "```", cmd("stats"), "```",
         "",
@@ -276,7 +277,8 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
     lines = [
         "# HBM traffic of the NVFP4 GEMM (Llama-7B layer: fwd, dgrad, wgrad)",
         "",
-        "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`):",
+        "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; "
+        "`OUT` = the folder the runs write their CSV files to):",
         "",
         "```", cmd("fetch"), cmd("write"), cmd("copy_fetch"), cmd("copy_write"), "```",
         "",
@@ -358,7 +360,8 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
     lines = [
         "# MFMA and VALU utilisation of the Llama-7B layer step's kernels",
         "",
-        "Command (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`):",
+        "Command (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; "
+        "`OUT` = the folder the run writes its CSV files to):",
         "",
         "```", cmd("util"), "```",
         "",
