@@ -180,28 +180,68 @@ int main() {
 """
 
 
-def test_philox_matches_aten_engine(orc):
-    # ATen's header-only Philox4x32-10: key = seed, counter = (offset lo/hi,
-    # subsequence lo/hi). Compiled here with g++; a library run, not a retype.
+@pytest.fixture(scope="module")
+def aten_philox():
+    """ATen's header-only Philox4x32-10 engine, compiled here with g++ (a
+    library run, not a retype): a function mapping (seed, subsequence, offset)
+    triples to the four output words of the engine's first block. ATen's engine
+    uses key = seed and counter = (offset lo/hi, subsequence lo/hi)."""
     inc = os.path.join(os.path.dirname(torch.__file__), "include")
     if not os.path.exists(os.path.join(inc, "ATen", "core", "PhiloxRNGEngine.h")):
         pytest.skip("ATen headers not installed")
+    d = tempfile.mkdtemp()
+    src = os.path.join(d, "drv.cpp")
+    exe = os.path.join(d, "drv")
+    with open(src, "w") as f:
+        f.write(ATEN_DRIVER)
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, src, "-o", exe], check=True)
+
+    def run(triples):
+        inp = "\n".join(f"{int(s):x} {int(u):x} {int(o):x}" for s, u, o in triples)
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+        return [[int(t, 16) for t in line.split()] for line in out.strip().split("\n")]
+
+    yield run
+    os.remove(exe)
+    os.remove(src)
+    os.rmdir(d)
+
+
+def test_philox_matches_aten_engine(orc, aten_philox):
     rng = np.random.default_rng(11)
     cases = rng.integers(0, 2 ** 63, size=(4000, 3), dtype=np.uint64) * np.uint64(2) + \
         rng.integers(0, 2, size=(4000, 3), dtype=np.uint64)
-    with tempfile.TemporaryDirectory() as d:
-        src = os.path.join(d, "drv.cpp")
-        exe = os.path.join(d, "drv")
-        with open(src, "w") as f:
-            f.write(ATEN_DRIVER)
-        subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, src, "-o", exe], check=True)
-        inp = "\n".join(f"{int(s):x} {int(u):x} {int(o):x}" for s, u, o in cases)
-        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
-    for (s, u, o), line in zip(cases, out.strip().split("\n")):
+    out = aten_philox(cases)
+    for (s, u, o), words in zip(cases, out):
         s, u, o = int(s), int(u), int(o)
         ctr = [o & 0xFFFFFFFF, o >> 32, u & 0xFFFFFFFF, u >> 32]
         key = [s & 0xFFFFFFFF, s >> 32]
-        assert orc.philox4x32_10(ctr, key) == [int(t, 16) for t in line.split()]
+        assert orc.philox4x32_10(ctr, key) == words
+
+
+def test_sr_stream_layout_from_known_answer_vector(orc):
+    # Seed 0, elements 0..7: the eight 16-bit halves of the published first
+    # known-answer block, in little-endian order (derivation in the fixture).
+    for seed, i, draw in rows("sr_stream_layout.txt"):
+        assert orc.sr_draw16(int(seed), int(i)) == int(draw, 16), (seed, i)
+
+
+def test_sr_stream_layout_matches_aten_engine(orc, aten_philox):
+    # Element i's draw is half number i % 8 (little-endian) of the 16-byte
+    # output block of ATen's engine at offset i / 8 (subsequence 0), for seeds
+    # with both key words set and for indices whose block counter needs its
+    # high word (i / 8 >= 2^32).
+    rng = np.random.default_rng(12)
+    seeds = [0, 1, 0x1234_5678_9ABC_DEF0, (2 << 8) | 3] + \
+        [int(v) for v in rng.integers(0, 2 ** 63, size=4, dtype=np.uint64)]
+    bases = [0, 8, 4096 * 8 + 8, (1 << 35) - 8, (1 << 35), (3 << 40) + 16] + \
+        [int(v) * 8 for v in rng.integers(0, 2 ** 58, size=6, dtype=np.uint64)]
+    triples = [(s, 0, b >> 3) for s in seeds for b in bases]
+    blocks = aten_philox(triples)
+    for (s, _, call), words in zip(triples, blocks):
+        halves = np.frombuffer(np.array(words, dtype="<u4").tobytes(), dtype="<u2")
+        for j in range(8):
+            assert orc.sr_draw16(s, call * 8 + j) == int(halves[j]), (hex(s), call, j)
 
 
 def test_sr_draws_are_uniform_and_distinct_per_seed(orc):
