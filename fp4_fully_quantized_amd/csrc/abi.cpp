@@ -35,9 +35,9 @@ fp4_status check_matrix(const void* src, int dt, int64_t R, int64_t C, int64_t l
 
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
-                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
-                         int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream) {
+// Every check of a single-orientation quantization, before anything is enqueued.
+fp4_status check_quant(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld, fp4_axis axis,
+                       fp4_rounding rnd, uint64_t index_offset, const fp4_tensor* out) {
   if (!out) return FP4_ERR_NULL;
   fp4_status st = check_matrix(src, src_t, R, C, ld);
   if (st != FP4_OK) return st;
@@ -54,14 +54,21 @@ fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C,
   if (rnd == FP4_SR && index_offset % 8 != 0) return FP4_ERR_ALIGN;
   if (axis == FP4_AXIS_ROWS && (R + 255) / 256 * ((C + 63) / 64) > 0x7FFFFFFF)
     return FP4_ERR_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return FP4_OK;
+}
+
+// Enqueue a quantization that check_quant accepted.
+fp4_status launch_quant(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld, fp4_axis axis,
+                        fp4_rounding rnd, uint64_t seed, uint64_t index_offset, int amax_ready,
+                        fp4_tensor* out, double* noise, hipStream_t s) {
+  const bool nv = out->fmt == FP4_NVFP4;
   if (nv && !amax_ready) {
     if (out->had_on)
       fp4i_launch_amax_rot16(src, src_t == FP4_DTYPE_BF16, R, C, ld, axis == FP4_AXIS_ROWS,
                              out->had_signs, out->amax, s);
     else
       fp4i_launch_amax(src, src_t == FP4_DTYPE_BF16, R, C, ld, out->amax, s);
-    st = hip_status();
+    const fp4_status st = hip_status();
     if (st != FP4_OK) return st;
   }
   QuantArgs a;
@@ -86,6 +93,141 @@ fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C,
   out->rows = a.rows_axis ? C : R;
   out->cols = a.rows_axis ? R : C;
   return hip_status();
+}
+
+fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
+                         int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream) {
+  const fp4_status st = check_quant(src, src_t, R, C, ld, axis, rnd, index_offset, out);
+  if (st != FP4_OK) return st;
+  return launch_quant(src, src_t, R, C, ld, axis, rnd, seed, index_offset, amax_ready, out, noise,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- GEMM operands
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// The matrix a GEMM operand stands for (rows x K, blocked along K), and for a
+// RAW operand the quantization that produces it.
+struct OperandView {
+  int64_t rows = 0, k = 0;
+  int32_t fmt = 0, had_on = 0;
+  uint32_t had_signs = 0;
+  bool raw = false;
+  fp4_tensor q{};       // the quantized operand (for RAW: carved from the workspace)
+  size_t ws_bytes = 0;  // RAW: workspace this operand takes
+};
+
+// Workspace pieces of a RAW operand: codes, scales, then (NVFP4) amax and
+// tscale, each on a 256-byte boundary.
+size_t raw_ws_bytes(int64_t rows, int64_t k, int32_t fmt) {
+  size_t n = round_up((size_t)rows * (size_t)(k / 2)) + round_up((size_t)rows * (size_t)(k / block_of(fmt)));
+  if (fmt == FP4_NVFP4) n += kWsAlign;
+  return n;
+}
+
+// Shape, kind and format of an operand (what fp4_gemm_workspace_bytes needs).
+fp4_status view_operand(const fp4_operand* op, OperandView* v) {
+  if (!op) return FP4_ERR_NULL;
+  if (op->kind == FP4_OPERAND_QUANTIZED) {
+    if (!op->q) return FP4_ERR_NULL;
+    if (!valid_fmt(op->q->fmt)) return FP4_ERR_ARG;
+    v->raw = false;
+    v->q = *op->q;
+    v->rows = op->q->rows;
+    v->k = op->q->cols;
+    v->fmt = op->q->fmt;
+    v->had_on = op->q->had_on != 0;
+    v->had_signs = op->q->had_signs;
+    return FP4_OK;
+  }
+  if (op->kind != FP4_OPERAND_RAW) return FP4_ERR_ARG;
+  if (!valid_fmt(op->fmt)) return FP4_ERR_ARG;
+  if (op->rows <= 0 || op->k <= 0 || op->k % block_of(op->fmt) != 0) return FP4_ERR_SHAPE;
+  v->raw = true;
+  v->rows = op->rows;
+  v->k = op->k;
+  v->fmt = op->fmt;
+  v->had_on = op->had_on != 0;
+  v->had_signs = op->had_signs;
+  v->ws_bytes = raw_ws_bytes(op->rows, op->k, op->fmt);
+  return FP4_OK;
+}
+
+// Source matrix of a RAW operand as fp4_quantize sees it: N stores rows x K
+// (blocks along C), T stores K x rows (blocks along R).
+struct RawSource {
+  int64_t R, C;
+  fp4_axis axis;
+};
+RawSource raw_source(const fp4_operand* op) {
+  if (op->layout == FP4_LAYOUT_T) return {op->k, op->rows, FP4_AXIS_ROWS};
+  return {op->rows, op->k, FP4_AXIS_COLS};
+}
+
+// Point v->q at the operand's workspace pieces starting at base.
+void carve_raw(OperandView* v, uint8_t* base) {
+  const size_t nc = round_up((size_t)v->rows * (size_t)(v->k / 2));
+  const size_t ns = round_up((size_t)v->rows * (size_t)(v->k / block_of(v->fmt)));
+  v->q = fp4_tensor{};
+  v->q.codes = base;
+  v->q.scales = base + nc;
+  if (v->fmt == FP4_NVFP4) {
+    v->q.amax = reinterpret_cast<float*>(base + nc + ns);
+    v->q.tscale = reinterpret_cast<float*>(base + nc + ns + 4);
+  }
+  v->q.rows = v->rows;
+  v->q.cols = v->k;
+  v->q.fmt = v->fmt;
+  v->q.had_on = v->had_on;
+  v->q.had_signs = v->had_signs;
+}
+
+// Every check of a RAW operand's quantization (v->q already carved).
+fp4_status check_raw(const fp4_operand* op, const OperandView& v) {
+  if (op->layout != FP4_LAYOUT_N && op->layout != FP4_LAYOUT_T) return FP4_ERR_ARG;
+  const RawSource rs = raw_source(op);
+  return check_quant(op->data, (fp4_dtype)op->dtype, rs.R, rs.C, op->ld, rs.axis, (fp4_rounding)op->rnd,
+                     op->index_offset, &v.q);
+}
+
+// The GEMM proper on two quantized operands blocked along K.
+fp4_status check_gemm_pair(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, const void* C,
+                           int64_t ldc) {
+  if (!valid_dtype(out_t)) return FP4_ERR_ARG;
+  if (!A->codes || !A->scales || !B->codes || !B->scales) return FP4_ERR_NULL;
+  if (A->fmt != B->fmt) return FP4_ERR_UNSUPPORTED;
+  if ((A->had_on != 0) != (B->had_on != 0)) return FP4_ERR_UNSUPPORTED;
+  if (A->had_on && A->had_signs != B->had_signs) return FP4_ERR_UNSUPPORTED;
+  if (A->fmt == FP4_NVFP4 && (!A->tscale || !B->tscale)) return FP4_ERR_NULL;
+  if (A->rows <= 0 || B->rows <= 0 || A->cols <= 0 || A->cols != B->cols || A->cols % 128 != 0)
+    return FP4_ERR_SHAPE;
+  if (!fp4i_gemm_fits(A->rows, B->rows, A->cols)) return FP4_ERR_SHAPE;
+  if (ldc < B->rows) return FP4_ERR_SHAPE;
+  if (!aligned16(A->codes) || !aligned16(B->codes) || !aligned16(A->scales) || !aligned16(B->scales))
+    return FP4_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(C) & (out_t == FP4_DTYPE_F32 ? 3u : 1u)) != 0) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
+void launch_gemm_pair(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C, int64_t ldc,
+                      hipStream_t s) {
+  GemmArgs g;
+  g.a_codes = A->codes;
+  g.a_scales = A->scales;
+  g.b_codes = B->codes;
+  g.b_scales = B->scales;
+  g.a_tscale = A->tscale;
+  g.b_tscale = B->tscale;
+  g.M = A->rows;
+  g.N = B->rows;
+  g.K = A->cols;
+  g.fmt = A->fmt;
+  g.bf16out = out_t == FP4_DTYPE_BF16;
+  g.c = C;
+  g.ldc = ldc;
+  fp4i_launch_gemm(g, s);
 }
 
 fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
@@ -208,6 +350,7 @@ const char* fp4_status_str(fp4_status s) {
     case FP4_ERR_UNSUPPORTED: return "unsupported combination";
     case FP4_ERR_ARG: return "bad enum argument";
     case FP4_ERR_HIP: return "HIP launch or runtime error";
+    case FP4_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
   }
   return "unknown status";
 }
@@ -339,37 +482,55 @@ fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64
   return hip_status();
 }
 
-fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C,
-                    int64_t ldc, fp4_stream_t stream) {
-  if (!A || !B || !C) return FP4_ERR_NULL;
-  if (!valid_dtype(out_t) || !valid_fmt(A->fmt) || !valid_fmt(B->fmt)) return FP4_ERR_ARG;
-  if (!A->codes || !A->scales || !B->codes || !B->scales) return FP4_ERR_NULL;
-  if (A->fmt != B->fmt) return FP4_ERR_UNSUPPORTED;
-  if ((A->had_on != 0) != (B->had_on != 0)) return FP4_ERR_UNSUPPORTED;
-  if (A->had_on && A->had_signs != B->had_signs) return FP4_ERR_UNSUPPORTED;
-  if (A->fmt == FP4_NVFP4 && (!A->tscale || !B->tscale)) return FP4_ERR_NULL;
-  if (A->rows <= 0 || B->rows <= 0 || A->cols <= 0 || A->cols != B->cols || A->cols % 128 != 0)
-    return FP4_ERR_SHAPE;
-  if (!fp4i_gemm_fits(A->rows, B->rows, A->cols)) return FP4_ERR_SHAPE;
-  if (ldc < B->rows) return FP4_ERR_SHAPE;
-  if (!aligned16(A->codes) || !aligned16(B->codes) || !aligned16(A->scales) || !aligned16(B->scales))
-    return FP4_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(C) & (out_t == FP4_DTYPE_F32 ? 3u : 1u)) != 0) return FP4_ERR_ALIGN;
-  GemmArgs g;
-  g.a_codes = A->codes;
-  g.a_scales = A->scales;
-  g.b_codes = B->codes;
-  g.b_scales = B->scales;
-  g.a_tscale = A->tscale;
-  g.b_tscale = B->tscale;
-  g.M = A->rows;
-  g.N = B->rows;
-  g.K = A->cols;
-  g.fmt = A->fmt;
-  g.bf16out = out_t == FP4_DTYPE_BF16;
-  g.c = C;
-  g.ldc = ldc;
-  fp4i_launch_gemm(g, reinterpret_cast<hipStream_t>(stream));
+size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B) {
+  OperandView va, vb;
+  if (view_operand(A, &va) != FP4_OK || view_operand(B, &vb) != FP4_OK) return 0;
+  return va.ws_bytes + vb.ws_bytes;
+}
+
+fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
+                    int64_t ldc, void* ws, size_t ws_bytes, fp4_stream_t stream) {
+  if (!C) return FP4_ERR_NULL;
+  OperandView va, vb;
+  fp4_status st = view_operand(A, &va);
+  if (st != FP4_OK) return st;
+  st = view_operand(B, &vb);
+  if (st != FP4_OK) return st;
+  // Format, rotation and K agreement first: a RAW operand's K must suit the
+  // product before its workspace is sized.
+  if (va.fmt != vb.fmt) return FP4_ERR_UNSUPPORTED;
+  if (va.had_on != vb.had_on || (va.had_on && va.had_signs != vb.had_signs)) return FP4_ERR_UNSUPPORTED;
+  if (va.k != vb.k || va.k <= 0 || va.k % 128 != 0 || va.rows <= 0 || vb.rows <= 0) return FP4_ERR_SHAPE;
+  if (!fp4i_gemm_fits(va.rows, vb.rows, va.k)) return FP4_ERR_SHAPE;
+  const size_t need = va.ws_bytes + vb.ws_bytes;
+  if (need > 0) {
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) % kWsAlign) != 0) return FP4_ERR_WORKSPACE;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    if (va.raw) carve_raw(&va, base);
+    if (vb.raw) carve_raw(&vb, base + va.ws_bytes);
+    if (va.raw && (st = check_raw(A, va)) != FP4_OK) return st;
+    if (vb.raw && (st = check_raw(B, vb)) != FP4_OK) return st;
+  }
+  st = check_gemm_pair(&va.q, &vb.q, out_t, C, ldc);
+  if (st != FP4_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < 2; ++i) {
+    const fp4_operand* op = i == 0 ? A : B;
+    OperandView* v = i == 0 ? &va : &vb;
+    if (!v->raw) continue;
+    const RawSource rs = raw_source(op);
+    st = launch_quant(op->data, (fp4_dtype)op->dtype, rs.R, rs.C, op->ld, rs.axis, (fp4_rounding)op->rnd,
+                      op->seed, op->index_offset, 0, &v->q, nullptr, s);
+    if (st != FP4_OK) return st;
+  }
+  launch_gemm_pair(&va.q, &vb.q, out_t, C, ldc, s);
+  return hip_status();
+}
+
+fp4_status fp4_noise_ratio(const double* noise, double* ratio, fp4_stream_t stream) {
+  if (!noise || !ratio) return FP4_ERR_NULL;
+  if (!aligned8(noise) || !aligned8(ratio)) return FP4_ERR_ALIGN;
+  fp4i_launch_noise_ratio(noise, ratio, reinterpret_cast<hipStream_t>(stream));
   return hip_status();
 }
 

@@ -89,4 +89,6 @@ void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const floa
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);
 bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K);
+// *ratio = sqrt(noise[0] / noise[1]) on the device (the gradient-noise monitor's statistic).
+void fp4i_launch_noise_ratio(const double* noise, double* ratio, hipStream_t s);
 void fp4i_launch_gemm(const GemmArgs& g, hipStream_t s);

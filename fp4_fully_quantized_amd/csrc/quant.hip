@@ -43,6 +43,12 @@ namespace {
 
 __global__ void k_zero1(float* p) { *p = 0.0f; }
 
+// The monitor's ratio ||g|| / ||Q(g) - g|| from its two FP64 sums.
+__global__ void k_noise_ratio(const double* __restrict__ noise, double* __restrict__ ratio) {
+  const double g = noise[0], e = noise[1];
+  *ratio = e > 0.0 ? sqrt(g / e) : (g > 0.0 ? __builtin_inf() : 0.0);
+}
+
 // The 16-wide rotation of 8 elements per lane, lanes 2j and 2j+1 holding one
 // block (elements 0..7 and 8..15): signs, stages 1, 2, 4 in registers, stage
 // 8 across the lane pair, times 1/4. Every lane of the wave must take part.
@@ -642,6 +648,10 @@ void fp4i_launch_amax_pair(const void* src, bool bf16, int64_t R, int64_t C, int
     else FP4_AMAX_PAIR(false, false, true);
   }
 #undef FP4_AMAX_PAIR
+}
+
+void fp4i_launch_noise_ratio(const double* noise, double* ratio, hipStream_t s) {
+  hipLaunchKernelGGL(k_noise_ratio, dim3(1), dim3(1), 0, s, noise, ratio);
 }
 
 void fp4i_launch_quant(const QuantArgs& a, hipStream_t s) {

@@ -56,6 +56,9 @@
  * Errors: every call validates its arguments first; on a non-OK status
  * nothing has been enqueued and no output has been touched, except
  * FP4_ERR_HIP, which reports a failed launch (outputs then undefined).
+ * Stochastic rounding draws 8 elements' bits from one Philox call, so every
+ * call that takes an SR index_offset requires index_offset % 8 == 0
+ * (FP4_ERR_ALIGN otherwise).
  * Non-finite inputs are outside the contract: their outputs are unspecified.
  */
 #ifndef FP4_H
@@ -77,7 +80,8 @@ typedef enum fp4_status {
     FP4_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks 16-byte alignment */
     FP4_ERR_UNSUPPORTED = 4, /* a combination the library does not implement */
     FP4_ERR_ARG = 5,         /* an enum value out of range */
-    FP4_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+    FP4_ERR_HIP = 6,         /* a HIP launch or runtime call failed */
+    FP4_ERR_WORKSPACE = 7    /* the workspace is NULL, too small or misaligned */
 } fp4_status;
 
 typedef enum fp4_dtype { FP4_DTYPE_F32 = 0, FP4_DTYPE_BF16 = 1 } fp4_dtype;
@@ -141,7 +145,12 @@ fp4_status fp4_tensor_amax_hadamard16(const void* src, fp4_dtype src_t, int64_t 
                                       fp4_stream_t stream);
 
 /* Quantize the R x C matrix src (row-major, leading dimension ld, FP32 or bf16;
- * device) into *out.
+ * device) into *out: block-scaled FP4 with the format of out->fmt (Robots
+ * Atlas, "FP4", Components: NVFP4 and MXFP4; How it works: the block scale
+ * brings each block into the E2M1 range), round-to-nearest or stochastic
+ * ("FP4 All the Way", Key points: round to nearest in the forward pass,
+ * stochastic rounding in the backward and update passes), along either axis so
+ * that each GEMM operand is blocked along its contraction dimension.
  *   axis         FP4_AXIS_COLS: blocks along C, out is R x C;
  *                FP4_AXIS_ROWS: blocks along R, out is C x R (the transpose).
  *   rnd          FP4_RTN or FP4_SR.
@@ -154,7 +163,9 @@ fp4_status fp4_tensor_amax_hadamard16(const void* src, fp4_dtype src_t, int64_t 
  *                had_signs and, for NVFP4, amax and tscale. The call writes
  *                out->rows and out->cols; *out->tscale receives s_g.
  * Requires: R, C >= 1; the blocked dimension a multiple of B (C for COLS, R
- * for ROWS); C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned. */
+ * for ROWS); C % 8 == 0; ld >= C and ld % 8 == 0; src 16-byte aligned;
+ * codes and scales 16-byte aligned; with SR, index_offset % 8 == 0
+ * (FP4_ERR_ALIGN). */
 fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream);
@@ -181,7 +192,8 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
  *                first; each tscale receives its own s_g.
  * The two descriptors must have the same fmt; had_on and had_signs are each
  * descriptor's own. Requires: R, C >= 1, both multiples of B; C % 8 == 0;
- * ld >= C and ld % 8 == 0; src 16-byte aligned. Errors as fp4_quantize. */
+ * ld >= C and ld % 8 == 0; src 16-byte aligned; each orientation's SR
+ * index_offset % 8 == 0 (FP4_ERR_ALIGN). Errors as fp4_quantize. */
 fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                              fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
                              fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
@@ -203,7 +215,8 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
  * The FP64 additions across workgroups are atomic, in no fixed order, so the
  * last bits can differ between runs. Codes, scales and s_g are identical to
  * fp4_quantize's. Requires the squares to be finite in FP32 (|x| < 2^63);
- * otherwise as fp4_quantize, and FP4_ERR_NULL for a NULL noise. */
+ * otherwise as fp4_quantize (including SR index_offset % 8 == 0), and
+ * FP4_ERR_NULL for a NULL noise, FP4_ERR_ALIGN for one not 8-byte aligned. */
 fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                               fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                               int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream);
@@ -211,12 +224,24 @@ fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64
 /* fp4_quantize_dual with the noise monitor of fp4_quantize_noise on either
  * orientation: noise_cols for out_cols, noise_rows for out_rows (each two
  * device doubles, accumulated into, or NULL to skip; FP4_ERR_NULL if both are
- * NULL). Partials are per block in both orientations. */
+ * NULL). Partials are per block in both orientations. Otherwise as
+ * fp4_quantize_dual. */
 fp4_status fp4_quantize_dual_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                                    fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
                                    fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
                                    int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
                                    double* noise_cols, double* noise_rows, fp4_stream_t stream);
+
+/* The monitor's statistic ("FP4 All the Way", Summary: the threshold is stated
+ * on the ratio of the gradient norm to the quantization noise norm), computed
+ * on the device in stream order from the two sums an fp4_quantize_noise or
+ * fp4_quantize_dual_noise call accumulated:
+ *   *ratio = sqrt(noise[0] / noise[1])   (FP64; +inf when noise[1] == 0,
+ *                                          0 when both are 0)
+ * noise: device, two doubles; ratio: device, one double; both 8-byte aligned.
+ * Reading the ratio on the host is the caller's (after the stream is
+ * synchronized); the threshold itself is the caller's. */
+fp4_status fp4_noise_ratio(const double* noise, double* ratio, fp4_stream_t stream);
 
 /* Two-dimensional block quantization (Robots Atlas, "FP4", How it works:
  * two-dimensional quantization among the stabilizers of FP4 training): one
@@ -240,32 +265,99 @@ fp4_status fp4_quantize_2d(const void* src, fp4_dtype src_t, int64_t R, int64_t 
                            fp4_tensor* out, fp4_tensor* out_t, fp4_stream_t stream);
 
 /* Dequantize q to dst (device, q->rows x q->cols row-major, leading dimension
- * ld >= cols, FP32 or bf16):
+ * ld >= cols, FP32 or bf16): the value each code stands for, its E2M1 value
+ * times the block scale (times the tensor scale for NVFP4) (Robots Atlas,
+ * "FP4", How it works: two-level scaling; Components: E2M1, E4M3 and E8M0):
  *   NVFP4: (e2m1 * sdec) * s_g, the last product rounded once to FP32;
  *   MXFP4: e2m1 * 2^e (exact); values stay in the rotated domain when had_on.
  * A bf16 output is the FP32 value rounded to nearest even.
- * Requires ld % 8 == 0 and dst 16-byte aligned. */
+ * Requires q->rows, q->cols >= 1, q->cols a multiple of B, ld >= q->cols,
+ * ld % 8 == 0, dst and q->codes 16-byte aligned. */
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
                           fp4_stream_t stream);
 
-/* C[i][j] = alpha * sum_k A_hat[i][k] * B_hat[j][k] with FP32 accumulation,
- * where A_hat, B_hat are the dequantized operands (both blocked along the
- * shared contraction axis K), M = A->rows, N = B->rows, K = A->cols = B->cols,
- * alpha = (*A->tscale) * (*B->tscale) for NVFP4 and 1 for MXFP4. alpha is
+/* GEMM operands. Each operand stands for a rows x K matrix (A: M x K,
+ * B: N x K) whose values the GEMM contracts along K. It is either already
+ * quantized, or a raw matrix that fp4_gemm quantizes into the caller's
+ * workspace first, with the layout, format and rounding flags below (the
+ * three linear-layer GEMMs on FP4 operands: "Quartet", one-line summary and
+ * Approach; FP4 weights, activations and gradients: "FP4 All the Way", Key
+ * points):
+ *   FP4_OPERAND_QUANTIZED  q: a quantized tensor blocked along K
+ *                          (rows = q->rows, K = q->cols).
+ *   FP4_OPERAND_RAW        data: device FP32 or bf16 (dtype), leading
+ *                          dimension ld, and
+ *                          layout FP4_LAYOUT_N: data is rows x K, K contiguous
+ *                                 (quantized with FP4_AXIS_COLS);
+ *                          layout FP4_LAYOUT_T: data is K x rows, rows
+ *                                 contiguous (quantized with FP4_AXIS_ROWS:
+ *                                 e.g. W for dgrad, dY and X for wgrad);
+ *                          fmt, rnd, seed, index_offset, had_on, had_signs as
+ *                          for fp4_quantize (the element index follows the
+ *                          rows x K orientation). NVFP4 takes the tensor amax
+ *                          of the values quantized (an amax pass first).
+ *                          Requirements are fp4_quantize's for the stored
+ *                          matrix (rows x K for N, K x rows for T). */
+typedef enum fp4_operand_kind { FP4_OPERAND_QUANTIZED = 0, FP4_OPERAND_RAW = 1 } fp4_operand_kind;
+typedef enum fp4_layout { FP4_LAYOUT_N = 0, FP4_LAYOUT_T = 1 } fp4_layout;
+
+typedef struct fp4_operand {
+    int32_t kind;            /* fp4_operand_kind */
+    int32_t dtype;           /* RAW: fp4_dtype of data */
+    const fp4_tensor* q;     /* QUANTIZED */
+    const void* data;        /* RAW: device */
+    int64_t rows;            /* RAW: M (A) or N (B) */
+    int64_t k;               /* RAW: K */
+    int64_t ld;              /* RAW: leading dimension of the stored matrix, elements */
+    int32_t layout;          /* RAW: fp4_layout */
+    int32_t fmt;             /* RAW: fp4_format */
+    int32_t rnd;             /* RAW: fp4_rounding */
+    int32_t had_on;          /* RAW: 1 to rotate (see Conventions) */
+    uint64_t seed;           /* RAW, SR: the stream's seed */
+    uint64_t index_offset;   /* RAW, SR: added to the element index; % 8 == 0 */
+    uint32_t had_signs;      /* RAW: the rotation's sign mask when had_on */
+    uint32_t reserved;
+} fp4_operand;
+
+/* Bytes of device workspace fp4_gemm needs for these operands: for each RAW
+ * operand, in the order A then B, its codes, its scale bytes and (NVFP4) its
+ * two FP32 scalars, each piece starting on a 256-byte boundary. 0 when
+ * neither operand is RAW, or when an operand is NULL or its kind, format,
+ * rows or K is invalid (fp4_gemm reports which). Host-only. */
+size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B);
+
+/* C[i][j] = alpha * sum_k A_hat[i][k] * B_hat[j][k] with FP32 accumulation
+ * (Robots Atlas, "FP4", How it works: FP4 products accumulated in higher
+ * precision; "Quartet", one-line summary: forward, dgrad and wgrad all run as
+ * FP4 GEMMs), where A_hat, B_hat are the dequantized operands (both blocked
+ * along the shared contraction axis K), M = A's rows, N = B's rows, K the
+ * operands' common K, alpha = s_gA * s_gB for NVFP4 and 1 for MXFP4. alpha is
  * one FP32 product applied to the FP32 accumulators: for operands whose
  * tensor scales multiply below 2^-126 (both tensor amaxes below about 1e-15)
  * it is subnormal or zero, and the output loses precision or becomes 0.
+ *   The three GEMMs of a linear layer: forward Y = X W^T (A = X, B = W, both
+ *   layout N); dgrad dX = dY W (A = dY layout N, B = W layout T); wgrad
+ *   dW = dY^T X (A = dY layout T, B = X layout T).
  *   MXFP4 runs on the gfx950 block-scaled FP4 MFMA with the E8M0 bytes as its
  *   scale operands. NVFP4 decodes e2m1 * E4M3 exactly into f16 in registers
  *   (at most 6 significant bits, magnitudes in [2^-10, 2688]) and runs the
  *   f16 MFMA.
+ * RAW operands are quantized into ws (see fp4_gemm_workspace_bytes) on the
+ * stream before the product; ws: device, 256-byte aligned, ws_bytes at least
+ * fp4_gemm_workspace_bytes(A, B) (FP4_ERR_WORKSPACE otherwise; ws may be NULL
+ * when neither operand is RAW). The workspace holds the quantized operands
+ * when the call's work has run.
  * C: device, M x N row-major, leading dimension ldc >= N, FP32 or bf16
  * (rounded to nearest even once, after alpha).
- * Requires: same fmt, had_on and had_signs on both operands; K % 128 == 0;
- * M, N >= 1 (any value); each operand's codes below 2^31 bytes (rows * K / 2);
- * ldc >= N (any value); C aligned to its element size. */
-fp4_status fp4_gemm(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C,
-                    int64_t ldc, fp4_stream_t stream);
+ * Requires: same fmt, had_on and had_signs on both operands
+ * (FP4_ERR_UNSUPPORTED); the same K, K % 128 == 0; M, N >= 1 (any value);
+ * each operand's codes below 2^31 bytes (rows * K / 2); ldc >= N (any value);
+ * C aligned to its element size; a QUANTIZED operand's codes and scales
+ * 16-byte aligned and, for NVFP4, its tscale set; a RAW operand as above.
+ * Validation covers both operands and the workspace before anything is
+ * enqueued. */
+fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
+                    int64_t ldc, void* ws, size_t ws_bytes, fp4_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -216,6 +216,18 @@ def quantize(x: np.ndarray, axis: int = AXIS_COLS, fmt: int = FMT_NVFP4, rnd: in
     return out
 
 
+def noise_ratio(sums) -> float:
+    """The gradient-noise monitor's statistic ("FP4 All the Way", Summary: the
+    threshold relates the gradient norm to the quantization noise norm): the
+    ratio of the two norms, sqrt(sum x^2 / sum (xhat - x)^2), from the FP64 sums
+    `quantize(..., noise=True)` returns. No noise gives +inf (0 when the
+    tensor is 0 too)."""
+    g, e = float(sums[0]), float(sums[1])
+    if e > 0.0:
+        return (g / e) ** 0.5
+    return float("inf") if g > 0.0 else 0.0
+
+
 def quantize_2d(x: np.ndarray, fmt: int = FMT_NVFP4, rnd: int = RTN, seed: int = 0,
                 index_offset: int = 0, amax: float | None = None):
     """Two-dimensional B x B block quantization. Returns (q, q_t): the [R, C]

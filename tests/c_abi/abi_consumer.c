@@ -4,7 +4,12 @@
  * oracle (test infrastructure). Quantizes X (64 x 256) and W (48 x 256) to
  * NVFP4 with round-to-nearest, multiplies them (Y = X W^T, FP32 out), and
  * compares the codes, scale bytes and tensor scales bit for bit and Y within
- * 1e-5 * sum |a_k b_k| per element. Exit status 0 and "abi consumer ok" on
+ * 1e-5 * sum |a_k b_k| per element. Then the GEMM with raw operands, which
+ * the library quantizes into the caller's workspace: for both formats, both
+ * roundings, with and without the rotation, and each operand stored K-major
+ * (layout N) or transposed (layout T), the product and the workspace's codes
+ * and scale bytes must equal those of fp4_quantize followed by a GEMM of the
+ * quantized operands, bit for bit. Exit status 0 and "abi consumer ok" on
  * success.
  */
 #include <math.h>
@@ -96,6 +101,161 @@ static int compare_quant(const fp4_tensor* t, int rows, const float* host, const
     return 0;
 }
 
+/* One raw-operand case: the stored matrix of an operand (rows x K for
+ * layout N, K x rows for layout T) on the device. */
+typedef struct {
+    float* dev;
+    int rows, layout;
+} raw_src;
+
+static int upload_raw(const float* logical, int rows, int layout, raw_src* r)
+{
+    float* h = malloc(sizeof(float) * rows * K);
+    for (int i = 0; i < rows; ++i)
+        for (int k = 0; k < K; ++k) {
+            if (layout == FP4_LAYOUT_N) h[i * K + k] = logical[i * K + k];
+            else h[k * rows + i] = logical[i * K + k];
+        }
+    CHECK_HIP(hipMalloc((void**)&r->dev, sizeof(float) * rows * K));
+    CHECK_HIP(hipMemcpy(r->dev, h, sizeof(float) * rows * K, hipMemcpyHostToDevice));
+    free(h);
+    r->rows = rows;
+    r->layout = layout;
+    return 0;
+}
+
+static void fill_raw(fp4_operand* o, const raw_src* r, int fmt, int rnd, uint64_t seed, int had,
+                     uint32_t signs)
+{
+    memset(o, 0, sizeof(*o));
+    o->kind = FP4_OPERAND_RAW;
+    o->dtype = FP4_DTYPE_F32;
+    o->data = r->dev;
+    o->rows = r->rows;
+    o->k = K;
+    o->ld = r->layout == FP4_LAYOUT_N ? K : r->rows;
+    o->layout = r->layout;
+    o->fmt = fmt;
+    o->rnd = rnd;
+    o->seed = seed;
+    o->index_offset = rnd == FP4_SR ? 64 : 0;
+    o->had_on = had;
+    o->had_signs = signs;
+}
+
+/* fp4_quantize of a raw operand into its own buffers, as the reference path. */
+static int quantize_raw(const fp4_operand* o, fp4_tensor* t)
+{
+    int B = o->fmt == FP4_NVFP4 ? 16 : 32;
+    memset(t, 0, sizeof(*t));
+    CHECK_HIP(hipMalloc((void**)&t->codes, (size_t)o->rows * K / 2));
+    CHECK_HIP(hipMalloc((void**)&t->scales, (size_t)o->rows * K / B));
+    if (o->fmt == FP4_NVFP4) {
+        CHECK_HIP(hipMalloc((void**)&t->amax, 4));
+        CHECK_HIP(hipMalloc((void**)&t->tscale, 4));
+    }
+    t->fmt = o->fmt;
+    t->had_on = o->had_on;
+    t->had_signs = o->had_signs;
+    int64_t R = o->layout == FP4_LAYOUT_N ? o->rows : K;
+    int64_t C = o->layout == FP4_LAYOUT_N ? K : o->rows;
+    CHECK_FP4(fp4_quantize(o->data, FP4_DTYPE_F32, R, C, o->ld,
+                           o->layout == FP4_LAYOUT_N ? FP4_AXIS_COLS : FP4_AXIS_ROWS, (fp4_rounding)o->rnd,
+                           o->seed, o->index_offset, 0, t, NULL));
+    return 0;
+}
+
+static void free_q(fp4_tensor* t)
+{
+    hipFree(t->codes); hipFree(t->scales);
+    if (t->amax) hipFree(t->amax);
+    if (t->tscale) hipFree(t->tscale);
+}
+
+static int same_device_bytes(const void* a, const void* b, size_t n)
+{
+    uint8_t* ha = malloc(n);
+    uint8_t* hb = malloc(n);
+    int same = hipMemcpy(ha, a, n, hipMemcpyDeviceToHost) == hipSuccess &&
+               hipMemcpy(hb, b, n, hipMemcpyDeviceToHost) == hipSuccess && memcmp(ha, hb, n) == 0;
+    free(ha); free(hb);
+    return same;
+}
+
+static int raw_operand_cases(const float* x, const float* w)
+{
+    int cases = 0;
+    float* y_raw;
+    float* y_ref;
+    CHECK_HIP(hipMalloc((void**)&y_raw, sizeof(float) * M * N));
+    CHECK_HIP(hipMalloc((void**)&y_ref, sizeof(float) * M * N));
+    for (int la = 0; la < 2; ++la)
+        for (int lb = 0; lb < 2; ++lb) {
+            raw_src ra, rb;
+            if (upload_raw(x, M, la, &ra) || upload_raw(w, N, lb, &rb)) return 10;
+            for (int fmt = 0; fmt < 2; ++fmt)
+                for (int rnd = 0; rnd < 2; ++rnd)
+                    for (int had = 0; had < 2; ++had) {
+                        uint32_t signs = fp4_hadamard_signs(5);
+                        fp4_operand a, b;
+                        fill_raw(&a, &ra, fmt, rnd, 11, had, signs);
+                        fill_raw(&b, &rb, fmt, rnd, 12, had, signs);
+                        size_t need = fp4_gemm_workspace_bytes(&a, &b);
+                        if (need == 0) {
+                            fprintf(stderr, "raw operands reported no workspace\n");
+                            return 11;
+                        }
+                        uint8_t* ws;
+                        CHECK_HIP(hipMalloc((void**)&ws, need));
+                        if (fp4_gemm(&a, &b, FP4_DTYPE_F32, y_raw, N, ws, need - 1, NULL) != FP4_ERR_WORKSPACE) {
+                            fprintf(stderr, "a workspace one byte short was accepted\n");
+                            return 12;
+                        }
+                        CHECK_FP4(fp4_gemm(&a, &b, FP4_DTYPE_F32, y_raw, N, ws, need, NULL));
+                        fp4_tensor qa, qb;
+                        if (quantize_raw(&a, &qa) || quantize_raw(&b, &qb)) return 13;
+                        fp4_operand oa, ob;
+                        memset(&oa, 0, sizeof(oa));
+                        memset(&ob, 0, sizeof(ob));
+                        oa.kind = ob.kind = FP4_OPERAND_QUANTIZED;
+                        oa.q = &qa;
+                        ob.q = &qb;
+                        CHECK_FP4(fp4_gemm(&oa, &ob, FP4_DTYPE_F32, y_ref, N, NULL, 0, NULL));
+                        CHECK_HIP(hipDeviceSynchronize());
+                        /* workspace layout: A codes, A scales, (NVFP4: A amax, tscale), then B's */
+                        int B = fmt == FP4_NVFP4 ? 16 : 32;
+                        size_t up = 256;
+                        size_t ca = ((size_t)M * K / 2 + up - 1) / up * up;
+                        size_t sa = ((size_t)M * K / B + up - 1) / up * up;
+                        size_t a_bytes = ca + sa + (fmt == FP4_NVFP4 ? up : 0);
+                        size_t cb = ((size_t)N * K / 2 + up - 1) / up * up;
+                        size_t sb = ((size_t)N * K / B + up - 1) / up * up;
+                        int ok = same_device_bytes(y_raw, y_ref, sizeof(float) * M * N) &&
+                                 same_device_bytes(ws, qa.codes, (size_t)M * K / 2) &&
+                                 same_device_bytes(ws + ca, qa.scales, (size_t)M * K / B) &&
+                                 same_device_bytes(ws + a_bytes, qb.codes, (size_t)N * K / 2) &&
+                                 same_device_bytes(ws + a_bytes + cb, qb.scales, (size_t)N * K / B);
+                        if (ok && fmt == FP4_NVFP4)
+                            ok = same_device_bytes(ws + ca + sa + 4, qa.tscale, 4) &&
+                                 same_device_bytes(ws + a_bytes + cb + sb + 4, qb.tscale, 4);
+                        if (!ok) {
+                            fprintf(stderr, "raw-operand GEMM differs from quantize-then-GEMM: layouts %d %d, "
+                                            "fmt %d, rnd %d, rotation %d\n", la, lb, fmt, rnd, had);
+                            return 14;
+                        }
+                        free_q(&qa);
+                        free_q(&qb);
+                        hipFree(ws);
+                        ++cases;
+                    }
+            hipFree(ra.dev);
+            hipFree(rb.dev);
+        }
+    hipFree(y_raw);
+    hipFree(y_ref);
+    return cases == 32 ? 0 : 15;
+}
+
 int main(void)
 {
     static float x[M * K], w[N * K];
@@ -110,7 +270,17 @@ int main(void)
     if ((rc = quantize_one(x, M, &tx, &dx, &sx))) return rc;
     if ((rc = quantize_one(w, N, &tw, &dw, &sw))) return rc;
     CHECK_HIP(hipMalloc((void**)&dy, sizeof(float) * M * N));
-    CHECK_FP4(fp4_gemm(&tx, &tw, FP4_DTYPE_F32, dy, N, NULL));
+    fp4_operand ox, ow;
+    memset(&ox, 0, sizeof(ox));
+    memset(&ow, 0, sizeof(ow));
+    ox.kind = ow.kind = FP4_OPERAND_QUANTIZED;
+    ox.q = &tx;
+    ow.q = &tw;
+    if (fp4_gemm_workspace_bytes(&ox, &ow) != 0) {
+        fprintf(stderr, "quantized operands need no workspace\n");
+        return 7;
+    }
+    CHECK_FP4(fp4_gemm(&ox, &ow, FP4_DTYPE_F32, dy, N, NULL, 0, NULL));
     static float y[M * N];
     CHECK_HIP(hipMemcpy(y, dy, sizeof(y), hipMemcpyDeviceToHost)); /* synchronizes the null stream */
 
@@ -141,9 +311,11 @@ int main(void)
         fprintf(stderr, "GEMM error %.3g of the 1e-5 sum|ab| bound\n", worst);
         return 6;
     }
+    if ((rc = raw_operand_cases(x, w))) return rc;
     hipFree(sx); hipFree(sw); hipFree(dy);
     hipFree(dx.codes); hipFree(dx.scales); hipFree(dx.amax); hipFree(dx.tscale);
     hipFree(dw.codes); hipFree(dw.scales); hipFree(dw.amax); hipFree(dw.tscale);
-    printf("abi consumer ok (GEMM worst error %.3g of the bound)\n", worst);
+    printf("abi consumer ok (GEMM worst error %.3g of the bound; 32 raw-operand GEMMs equal to "
+           "quantize-then-GEMM)\n", worst);
     return 0;
 }

@@ -57,8 +57,9 @@ def test_hadamard_mask_matches_oracle(fp4, orc):
 
 
 def test_status_strings(fp4):
-    for s in range(7):
-        assert fp4.fp4_status_str(s)
+    for s in range(8):
+        assert fp4.fp4_status_str(s) != "unknown status"
+    assert fp4.fp4_status_str(8) == "unknown status"
 
 
 def _t(fp4, **kw):
@@ -204,6 +205,27 @@ def test_amax_hadamard16_rejects_bad_arguments(fp4, case):
     assert fp4.lib().fp4_tensor_amax_hadamard16(src, dt, R, C, ld, axis, 5, amax, None) == want
 
 
+def _q_op(fp4, t):
+    o = fp4.fp4_operand()
+    o.kind = fp4.FP4_OPERAND_QUANTIZED
+    o.q = ctypes.pointer(t)
+    return o
+
+
+def _raw_op(fp4, **kw):
+    o = fp4.fp4_operand()
+    o.kind = kw.get("kind", fp4.FP4_OPERAND_RAW)
+    o.dtype = kw.get("dtype", 1)
+    o.data = kw.get("data", 0x70000)
+    o.rows, o.k = kw.get("rows", 64), kw.get("k", 128)
+    o.ld = kw.get("ld", o.rows if kw.get("layout", 0) == 1 else o.k)
+    o.layout = kw.get("layout", 0)
+    o.fmt, o.rnd = kw.get("fmt", 0), kw.get("rnd", 0)
+    o.seed, o.index_offset = kw.get("seed", 0), kw.get("index_offset", 0)
+    o.had_on, o.had_signs = kw.get("had_on", 0), kw.get("had_signs", 0)
+    return o
+
+
 GEMM_BAD = [
     ({}, {"fmt": 1}, 1, 128, 4),                      # mixed formats
     ({"fmt": 1, "had_on": 1, "had_signs": 5}, {"fmt": 1, "had_on": 1, "had_signs": 6}, 1, 128, 4),
@@ -215,6 +237,7 @@ GEMM_BAD = [
     ({"tscale": 0}, {}, 1, 128, 1),
     ({"codes": 0x10008}, {}, 1, 128, 3),
     ({}, {}, 3, 128, 5),
+    ({"fmt": 4}, {}, 1, 128, 5),
     ({"rows": 2 ** 20, "cols": 4096}, {"cols": 4096}, 1, 128, 2),   # A codes reach 2^31 bytes
     ({"cols": 4096}, {"rows": 2 ** 20, "cols": 4096}, 1, 2 ** 20, 2),  # B codes reach 2^31 bytes
 ]
@@ -224,11 +247,96 @@ GEMM_BAD = [
 def test_gemm_rejects_bad_arguments(fp4, case):
     a_over, b_over, out_t, ldc, want = case
     A, B = _t(fp4, **a_over), _t(fp4, **b_over)
-    st = fp4.lib().fp4_gemm(ctypes.byref(A), ctypes.byref(B), out_t, 0x50000, ldc, None)
+    st = fp4.lib().fp4_gemm(ctypes.byref(_q_op(fp4, A)), ctypes.byref(_q_op(fp4, B)), out_t, 0x50000, ldc,
+                            None, 0, None)
     assert st == want
     A, B = _t(fp4), _t(fp4)
-    assert fp4.lib().fp4_gemm(ctypes.byref(A), ctypes.byref(B), 0, 0x50002, 128, None) == 3
-    assert fp4.lib().fp4_gemm(None, ctypes.byref(B), 1, 0x50000, 128, None) == 1
+    oa, ob = _q_op(fp4, A), _q_op(fp4, B)
+    assert fp4.lib().fp4_gemm(ctypes.byref(oa), ctypes.byref(ob), 0, 0x50002, 128, None, 0, None) == 3
+    assert fp4.lib().fp4_gemm(None, ctypes.byref(ob), 1, 0x50000, 128, None, 0, None) == 1
+    assert fp4.lib().fp4_gemm(ctypes.byref(oa), ctypes.byref(ob), 1, None, 128, None, 0, None) == 1
+    nullq = fp4.fp4_operand()
+    nullq.kind = fp4.FP4_OPERAND_QUANTIZED
+    assert fp4.lib().fp4_gemm(ctypes.byref(nullq), ctypes.byref(ob), 1, 0x50000, 128, None, 0, None) == 1
+
+
+def _ws_bytes(rows, k, fmt):
+    up = lambda n: (n + 255) // 256 * 256
+    return up(rows * k // 2) + up(rows * k // (16 if fmt == 0 else 32)) + (256 if fmt == 0 else 0)
+
+
+def test_gemm_workspace_bytes(fp4):
+    L = fp4.lib()
+    A, B = _t(fp4), _t(fp4)
+    qa, qb = _q_op(fp4, A), _q_op(fp4, B)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(qa), ctypes.byref(qb)) == 0
+    ra = _raw_op(fp4, rows=100, k=256)
+    rb = _raw_op(fp4, rows=48, k=256, layout=1, fmt=0)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(ra), ctypes.byref(qb)) == _ws_bytes(100, 256, 0)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(qa), ctypes.byref(rb)) == _ws_bytes(48, 256, 0)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(ra), ctypes.byref(rb)) == \
+        _ws_bytes(100, 256, 0) + _ws_bytes(48, 256, 0)
+    mx = _raw_op(fp4, rows=4096, k=4096, fmt=1)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(mx), ctypes.byref(mx)) == 2 * _ws_bytes(4096, 4096, 1)
+    # the Llama-7B forward with both operands raw: X 32768 x 4096 and W 11008 x 4096 in NVFP4
+    x = _raw_op(fp4, rows=32768, k=4096)
+    w = _raw_op(fp4, rows=11008, k=4096)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(x), ctypes.byref(w)) == \
+        32768 * 2048 + 32768 * 256 + 256 + 11008 * 2048 + 11008 * 256 + 256
+    for bad in (_raw_op(fp4, rows=0), _raw_op(fp4, k=120), _raw_op(fp4, fmt=2), _raw_op(fp4, kind=7)):
+        assert L.fp4_gemm_workspace_bytes(ctypes.byref(bad), ctypes.byref(qb)) == 0
+    assert L.fp4_gemm_workspace_bytes(None, ctypes.byref(qb)) == 0
+
+
+RAW_BAD = [
+    # (A overrides (raw), ws, ws_bytes, expected): B is a valid quantized NVFP4 64 x 128 operand
+    ({}, None, 0, 7),                                   # no workspace
+    ({}, 0x800000, _ws_bytes(64, 128, 0) - 1, 7),       # workspace too small
+    ({}, 0x800010, 1 << 20, 7),                         # workspace not 256-byte aligned
+    ({"data": 0}, 0x800000, 1 << 20, 1),
+    ({"data": 0x70008}, 0x800000, 1 << 20, 3),          # source misaligned
+    ({"ld": 132}, 0x800000, 1 << 20, 3),                # ld % 8
+    ({"ld": 64}, 0x800000, 1 << 20, 2),                 # ld < K (layout N)
+    ({"layout": 1, "ld": 32}, 0x800000, 1 << 20, 2),    # ld < rows (layout T)
+    ({"layout": 2}, 0x800000, 1 << 20, 5),
+    ({"rnd": 3}, 0x800000, 1 << 20, 5),
+    ({"dtype": 4}, 0x800000, 1 << 20, 5),
+    ({"rnd": 1, "index_offset": 12}, 0x800000, 1 << 20, 3),   # SR offset % 8
+    ({"fmt": 1}, 0x800000, 1 << 20, 4),                 # formats differ
+    ({"had_on": 1, "had_signs": 3}, 0x800000, 1 << 20, 4),  # rotation on one side only
+    ({"k": 256}, 0x800000, 1 << 20, 2),                 # K differs from B's
+    ({"rows": 60, "layout": 1, "ld": 64}, 0x800000, 1 << 20, 2),  # layout T: rows are the contiguous axis, % 8
+]
+
+
+@pytest.mark.parametrize("case", RAW_BAD)
+def test_gemm_rejects_bad_raw_operands(fp4, case):
+    over, ws, ws_bytes, want = case
+    A = _raw_op(fp4, **over)
+    B = _t(fp4)
+    st = fp4.lib().fp4_gemm(ctypes.byref(A), ctypes.byref(_q_op(fp4, B)), 1, 0x50000, 128, ws, ws_bytes, None)
+    assert st == want
+
+
+def test_gemm_rejects_bad_raw_b(fp4):
+    # The same checks apply to B; a too-small workspace counts both operands.
+    A = _raw_op(fp4, rows=64, k=128)
+    B = _raw_op(fp4, rows=48, k=128, layout=1, ld=48)
+    need = _ws_bytes(64, 128, 0) + _ws_bytes(48, 128, 0)
+    L = fp4.lib()
+    assert L.fp4_gemm(ctypes.byref(A), ctypes.byref(B), 1, 0x50000, 48, 0x800000, need - 256, None) == 7
+    Bbad = _raw_op(fp4, rows=48, k=128, layout=1, ld=40)
+    assert L.fp4_gemm(ctypes.byref(A), ctypes.byref(Bbad), 1, 0x50000, 48, 0x800000, need, None) == 2
+    Bsr = _raw_op(fp4, rows=48, k=128, layout=1, ld=48, rnd=1, index_offset=4)
+    assert L.fp4_gemm(ctypes.byref(A), ctypes.byref(Bsr), 1, 0x50000, 48, 0x800000, need, None) == 3
+
+
+def test_noise_ratio_rejects_bad_arguments(fp4):
+    L = fp4.lib()
+    assert L.fp4_noise_ratio(None, 0x60000, None) == 1
+    assert L.fp4_noise_ratio(0x60000, None, None) == 1
+    assert L.fp4_noise_ratio(0x60004, 0x60010, None) == 3
+    assert L.fp4_noise_ratio(0x60000, 0x60014, None) == 3
 
 
 DEQ_BAD = [
@@ -261,3 +369,91 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "_lib", None)
     with pytest.raises(RuntimeError):
         m.lib()
+
+
+# ---------------------------------------------------------------- the binding's own checks
+# The Python binding refuses tensors the library cannot see through raw
+# pointers (host memory, wrong dtype or shape, transposed views, buffers too
+# small) before calling it. These run on CPU and meta tensors: nothing here
+# reaches the library's compute calls.
+def test_binding_rejects_host_and_meta_tensors(fp4):
+    import torch
+    x = torch.zeros((64, 128), dtype=torch.float32)
+    q = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.fp4_quantize(x, 0, 0, 0, 0, False, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.fp4_tensor_amax(x, torch.zeros(1))
+    m = torch.empty((64, 128), dtype=torch.float32, device="meta")
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.fp4_quantize(m, 0, 0, 0, 0, False, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.RawOperand(x)
+
+
+def test_binding_checks_shapes_and_buffers(fp4, monkeypatch):
+    import torch
+    # Pretend CPU tensors are device tensors to reach the shape and size checks
+    # (the library is never called: every case raises first).
+    monkeypatch.setattr(fp4, "_check_device", lambda t, name, device=None: None)
+    calls = []
+    real = fp4.lib()
+
+    class OnlySizeHelpers:
+        # the host-only size helpers answer; any other entry point is recorded
+        def __getattr__(self, name):
+            if name in ("fp4_codes_bytes", "fp4_scales_bytes", "fp4_status_str"):
+                return getattr(real, name)
+            calls.append(name)
+            return lambda *a: 0
+
+    monkeypatch.setattr(fp4, "_lib", OnlySizeHelpers())
+    x = torch.zeros((64, 128), dtype=torch.float32)
+    q = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    with pytest.raises(ValueError, match="needs 128 x 64"):
+        fp4.fp4_quantize(x, fp4.FP4_AXIS_ROWS, 0, 0, 0, False, q)      # output not transposed
+    with pytest.raises(ValueError, match="unit column stride"):
+        fp4.fp4_quantize(torch.zeros((128, 64)).t(), 0, 0, 0, 0, False, q)
+    with pytest.raises(TypeError):
+        fp4.fp4_quantize(x.to(torch.float16), 0, 0, 0, 0, False, q)
+    small = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    small.codes = small.codes[:10]
+    with pytest.raises(ValueError, match="codes holds"):
+        fp4.fp4_quantize(x, 0, 0, 0, 0, False, small)
+    small = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    small.scales = small.scales.flatten()[:100]
+    with pytest.raises(ValueError, match="scales holds"):
+        fp4.fp4_quantize(x, 0, 0, 0, 0, False, small)
+    noamax = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    noamax.amax = torch.zeros(1, dtype=torch.float64)
+    with pytest.raises(ValueError, match="amax"):
+        fp4.fp4_quantize(x, 0, 0, 0, 0, False, noamax)
+    # GEMM: output shape, output layout, K of the operands
+    qa = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    qb = fp4.QTensor(48, 128, fp4.FP4_NVFP4, device="cpu")
+    with pytest.raises(ValueError, match="the product is 64 x 48"):
+        fp4.fp4_gemm(qa, qb, torch.zeros((48, 64)))
+    with pytest.raises(ValueError, match="unit column stride"):
+        fp4.fp4_gemm(qa, qb, torch.zeros((48, 64)).t())
+    # dequantize: destination shape
+    with pytest.raises(ValueError, match="dst is"):
+        fp4.fp4_dequantize(qa, torch.zeros((128, 64)))
+    # dual: each output in its own orientation
+    qr_bad = fp4.QTensor(64, 128, fp4.FP4_NVFP4, device="cpu")
+    with pytest.raises(ValueError, match="out_rows"):
+        fp4.fp4_quantize_dual(x, 0, 0, 0, 1, 0, 0, False, q, qr_bad)
+    # noise buffers
+    with pytest.raises(ValueError, match="noise"):
+        fp4.fp4_quantize_noise(x, 0, 0, 0, 0, False, q, torch.zeros(2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="ratio"):
+        fp4.fp4_noise_ratio(torch.zeros(2, dtype=torch.float64), torch.zeros(1, dtype=torch.float32))
+    # raw operands: layout, and a workspace of the wrong type
+    with pytest.raises(ValueError, match="layout"):
+        fp4.RawOperand(x, layout=3)
+    ra = fp4.RawOperand(x)
+    assert (ra.rows, ra.k) == (64, 128)
+    rt = fp4.RawOperand(x, layout=fp4.FP4_LAYOUT_T)
+    assert (rt.rows, rt.k) == (128, 64)
+    with pytest.raises(ValueError, match="ws"):
+        fp4.fp4_gemm(ra, qb, torch.zeros((64, 48)), ws=torch.zeros(10, dtype=torch.float32))
+    assert calls == []

@@ -129,11 +129,21 @@ def _rows_of(q, rows):
     return d
 
 
-def _sample_rows(M, seed, n=64):
-    """The first and last n rows (first and last row tiles) and n random rows."""
+def _sample_rows(M, seed, n=64, tile=256):
+    """The first and last n rows and one random row of every `tile`-row band,
+    so that every output tile of the kernel (256 x 256) has a checked row, in
+    every column."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(n), np.arange(M - n, M),
-                                     rng.integers(0, M, n)]))
+    starts = np.arange(0, M, tile)
+    per_tile = starts + rng.integers(0, tile, len(starts))
+    per_tile = np.minimum(per_tile, M - 1)
+    return np.unique(np.concatenate([np.arange(n), np.arange(M - n, M), per_tile]))
+
+
+def test_sampled_rows_reach_every_row_tile():
+    for M in (32768, 16384, 11008, 28672, 300):
+        rows = _sample_rows(M, 17)
+        assert set(rows // 256) == set(range((M + 255) // 256)), M
 
 
 # Full-size GEMMs. Llama-7B-shaped layer (32768 tokens, 4096 in, 11008 out):
@@ -181,6 +191,7 @@ def test_full_size_gemm_sampled_rows(fp4, orc, wl, which, out):
     B = q_from_oracle(qb, had_signs=signs if had else None)
     y = fp4.gemm(A, B, dtype=torch.bfloat16 if out == "bf16" else torch.float32)
     rows = _sample_rows(qa["rows"], 17, 64 if wl == "llama7b" else 16)
+    say("checked rows", len(rows), "of", qa["rows"], "covering", len(set(rows // 256)), "row tiles")
     yh = to_host(y[torch.from_numpy(rows).cuda()])
     if out == "bf16":
         yh = orc.bf16_bits_to_f32(yh)
@@ -259,4 +270,58 @@ def test_mxfp4_rotated_wgrad_end_to_end(fp4, orc):
     qb = orc.quantize(xh, axis=1, fmt=1, rnd=1, seed=3, had_on=True, had_signs=signs)
     ref, S = orc.gemm_ref(qa, qb)
     ok, worst = orc.gemm_check(y, ref, S, "fp32")
+    assert ok, worst
+
+
+# ------------------------------------------------------------ raw operands
+RAW = [(fmt, rnd, la, lb, had) for fmt in (0, 1) for rnd in (0, 1) for la in (0, 1) for lb in (0, 1)
+       for had in (False, True) if not (had and la != lb)]
+
+
+@pytest.mark.parametrize("fmt,rnd,la,lb,had", RAW)
+def test_raw_operand_gemm(fp4, orc, fmt, rnd, la, lb, had):
+    """fp4_gemm with raw operands (quantized by the library into the
+    workspace, each stored K-major (layout N) or transposed (layout T)):
+    bit-equal to fp4_quantize of each operand followed by the quantized GEMM,
+    and within the tolerance of the oracle's GEMM of the oracle's
+    quantizations."""
+    import torch
+    M, N, K = 200, 136, 256
+    say("raw-operand gemm fmt", fmt, "rnd", rnd, "layouts", la, lb, "had", had)
+    xh = _data((M, K), 31, outliers=True)
+    wh = _data((N, K), 32, std=0.02)
+    stored = lambda h, lay: np.ascontiguousarray(h.T) if lay == 1 else h
+    xs, ws_ = stored(xh, la), stored(wh, lb)
+    signs = orc.hadamard_signs(17) if had else None
+    A = fp4.RawOperand(to_device(xs), layout=la, fmt=fmt, rnd=rnd, seed=41, index_offset=8 * rnd,
+                       had_signs=signs)
+    B = fp4.RawOperand(to_device(ws_), layout=lb, fmt=fmt, rnd=rnd, seed=42, had_signs=signs)
+    assert (A.rows, A.k, B.rows, B.k) == (M, K, N, K)
+    y = fp4.gemm(A, B, dtype=torch.float32)
+    qa = fp4.quantize(A.data, axis=la, fmt=fmt, rnd=rnd, seed=41, index_offset=8 * rnd, had_signs=signs)
+    qb = fp4.quantize(B.data, axis=lb, fmt=fmt, rnd=rnd, seed=42, had_signs=signs)
+    y_ref = fp4.gemm(qa, qb, dtype=torch.float32)
+    assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+    oa = orc.quantize(xs, axis=la, fmt=fmt, rnd=rnd, seed=41, index_offset=8 * rnd, had_on=had,
+                      had_signs=signs or 0)
+    ob = orc.quantize(ws_, axis=lb, fmt=fmt, rnd=rnd, seed=42, had_on=had, had_signs=signs or 0)
+    ref, S = orc.gemm_ref(oa, ob)
+    ok, worst = orc.gemm_check(to_host(y), ref, S, "fp32")
+    assert ok, worst
+
+
+def test_raw_and_quantized_operands_mixed(fp4, orc):
+    """dgrad with dY already quantized and W raw (layout T, quantized along
+    its rows by the call), bf16 output."""
+    import torch
+    T, N, K = 256, 128, 384
+    dyh, wh = _data((T, N), 33), _data((N, K), 34, std=0.02)
+    say("mixed raw / quantized operands")
+    qdy = fp4.quantize(to_device(dyh), rnd=1, seed=5)
+    Wt = fp4.RawOperand(to_device(wh), layout=fp4.FP4_LAYOUT_T, rnd=1, seed=6)
+    ws = torch.empty(fp4.fp4_gemm_workspace_bytes(qdy, Wt), dtype=torch.uint8, device="cuda")
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    fp4.fp4_gemm(qdy, Wt, dx, ws=ws)
+    ref, S = orc.gemm_ref(orc.quantize(dyh, rnd=1, seed=5), orc.quantize(wh, axis=1, rnd=1, seed=6))
+    ok, worst = orc.gemm_check(orc.bf16_bits_to_f32(to_host(dx)), ref, S, "bf16")
     assert ok, worst

@@ -298,6 +298,24 @@ def _assert_noise(got, want, what):
         assert abs(got[k] - want[k]) <= NOISE_RTOL * want[k], (what, name, got[k], want[k])
 
 
+def _assert_ratio(got, want, what):
+    # sqrt of a quotient of two sums each within NOISE_RTOL: within NOISE_RTOL.
+    got = float(got.cpu()[0])
+    assert abs(got - want) <= NOISE_RTOL * want, (what, got, want)
+
+
+def test_noise_ratio_special_values(fp4, orc):
+    """The library's ratio on the device: ordinary sums, no noise (+inf), an
+    all-zero tensor (0)."""
+    import torch
+    say("noise ratio special values")
+    for sums in ([9.0, 0.25], [1e-30, 4e-34], [2.0, 0.0], [0.0, 0.0]):
+        noise = torch.tensor(sums, dtype=torch.float64, device="cuda")
+        got = float(fp4.noise_ratio(noise).cpu()[0])
+        want = orc.noise_ratio(sums)
+        assert got == want or abs(got - want) <= 1e-15 * want, (sums, got, want)
+
+
 NOISE = [(fmt, rnd, axis, had) for fmt in (0, 1) for rnd in (0, 1) for axis in (0, 1) for had in (False, True)]
 
 
@@ -314,6 +332,7 @@ def test_quantize_noise_matches_oracle(fp4, orc, fmt, rnd, axis, had, shape, bf1
     q = fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=13, had_signs=signs if had else None, noise=noise)
     assert_same_quant(q_to_host(q), want, "quantize with the noise monitor")
     _assert_noise(noise, want["noise"], "one call")
+    _assert_ratio(fp4.noise_ratio(noise), orc.noise_ratio(want["noise"]), "one call")
     fp4.quantize(x, axis=axis, fmt=fmt, rnd=rnd, seed=13, had_signs=signs if had else None, noise=noise)
     _assert_noise(noise, 2 * want["noise"], "accumulated over two calls")
 
@@ -365,7 +384,10 @@ def test_noise_monitor_full_size_gradient(fp4, orc):
     _assert_noise(nc, want_c["noise"], "dY cols")
     want_r = orc.quantize(xh, axis=1, rnd=1, seed=(2 << 8) | 2, noise=True)
     _assert_noise(nr, want_r["noise"], "dY rows")
-    say("gradient / noise norm ratio", fp4.noise_ratio(nc), fp4.noise_ratio(nr))
+    rc, rr = fp4.noise_ratio(nc), fp4.noise_ratio(nr)
+    _assert_ratio(rc, orc.noise_ratio(want_c["noise"]), "dY cols ratio")
+    _assert_ratio(rr, orc.noise_ratio(want_r["noise"]), "dY rows ratio")
+    say("gradient / noise norm ratio", float(rc.cpu()[0]), float(rr.cpu()[0]))
 
 
 # ------------------------------------------------------ 2-D block quantization

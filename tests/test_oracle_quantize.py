@@ -418,3 +418,22 @@ def test_2d_error_bound(orc):
     sdec = np.array([[orc.e4m3_value(int(b)) for b in row] for row in q["scales"]])
     bound = np.repeat(sdec, 16, axis=1) * q["sg"] * 1.0 * (1 + 2.0 ** -20)
     assert (np.abs(xhat - x.astype(np.float64)) <= bound).all()
+
+
+def test_noise_ratio_from_the_sums(orc):
+    # The statistic is a ratio of norms: |g| = 3 and |Q(g) - g| = 0.5 give 6.
+    assert orc.noise_ratio([9.0, 0.25]) == 6.0
+    assert orc.noise_ratio([2.0, 0.0]) == float("inf")
+    assert orc.noise_ratio([0.0, 0.0]) == 0.0
+    # A tensor on the E2M1 grid quantizes without noise (MXFP4, one block whose
+    # amax is 6 so the scale is 1): infinite ratio.
+    x = np.array([[0.5, 1, 1.5, 2, 3, 4, 6, -6] * 4], dtype=np.float32)
+    q = orc.quantize(x, fmt=orc.FMT_MXFP4, noise=True)
+    assert q["noise"][1] == 0.0 and orc.noise_ratio(q["noise"]) == float("inf")
+    # Halving the quantization step (all values scaled by 2^k change nothing):
+    # the ratio is scale invariant.
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((64, 64)).astype(np.float32)
+    r1 = orc.noise_ratio(orc.quantize(y, noise=True)["noise"])
+    r2 = orc.noise_ratio(orc.quantize(y * np.float32(8), noise=True)["noise"])
+    assert abs(r1 - r2) <= 1e-12 * r1
