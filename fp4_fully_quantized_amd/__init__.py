@@ -27,7 +27,9 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
            "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_noise_ratio", "fp4_quantize_2d",
-           "fp4_dequantize", "fp4_gemm_workspace_bytes", "fp4_gemm"]
+           "fp4_dequantize", "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_gemm_noalloc"]
+# The allocation-free GEMM's workspace limit (FP4_GEMM_NOALLOC_MAX_BYTES).
+FP4_GEMM_NOALLOC_MAX_BYTES = 128 << 20
 
 
 class Fp4Error(RuntimeError):
@@ -104,6 +106,9 @@ def lib() -> ctypes.CDLL:
         L.fp4_gemm.restype = c.c_int
         L.fp4_gemm.argtypes = [c.POINTER(fp4_operand), c.POINTER(fp4_operand), c.c_int, c.c_void_p,
                                c.c_int64, c.c_void_p, c.c_size_t, c.c_void_p]
+        L.fp4_gemm_noalloc.restype = c.c_int
+        L.fp4_gemm_noalloc.argtypes = [c.POINTER(fp4_operand), c.POINTER(fp4_operand), c.c_int, c.c_void_p,
+                                       c.c_int64, c.c_void_p]
         _lib = L
     return _lib
 
@@ -464,6 +469,22 @@ def fp4_gemm(A, B, C, ws=None, stream=None) -> None:
         ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     _check(lib().fp4_gemm(ctypes.byref(oa), ctypes.byref(ob), _dtype_code(C), C.data_ptr(), C.stride(0),
                           ws_ptr, ws_bytes, _stream(stream)), "fp4_gemm")
+
+
+def fp4_gemm_noalloc(A, B, C, stream=None) -> None:
+    """fp4_gemm with the library's own static workspace (for callers that
+    cannot allocate): RAW operands are quantized there. Calls with RAW
+    operands that overlap on one GPU race on that workspace."""
+    dev = _operand_device(A)
+    if _operand_device(B) != dev:
+        raise ValueError(f"A is on {dev}, B on {_operand_device(B)}")
+    oa, ka = _operand(A, "A")
+    ob, kb = _operand(B, "B")
+    _check_matrix(C, "C", dev)
+    if tuple(C.shape) != (A.rows, B.rows):
+        raise ValueError(f"C is {tuple(C.shape)}, the product is {A.rows} x {B.rows}")
+    _check(lib().fp4_gemm_noalloc(ctypes.byref(oa), ctypes.byref(ob), _dtype_code(C), C.data_ptr(),
+                                  C.stride(0), _stream(stream)), "fp4_gemm_noalloc")
 
 
 # ---------------------------------------------------------------- conveniences

@@ -5,7 +5,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "fp4_internal.hpp"
+
+// Workspace of fp4_gemm_noalloc: a device array each GPU holds from the
+// library's load until the process ends. Host code never uses this name as a
+// device address (on the host it is a stand-in); it uses the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[FP4_GEMM_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -308,6 +316,66 @@ fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64
   return hip_status();
 }
 
+// The product, with RAW operands quantized into ws first.
+fp4_status gemm_impl(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C, int64_t ldc,
+                     void* ws, size_t ws_bytes, fp4_stream_t stream) {
+  if (!C) return FP4_ERR_NULL;
+  OperandView va, vb;
+  fp4_status st = view_operand(A, &va);
+  if (st != FP4_OK) return st;
+  st = view_operand(B, &vb);
+  if (st != FP4_OK) return st;
+  // Format, rotation and K agreement first: a RAW operand's K must suit the
+  // product before its workspace is sized.
+  if (va.fmt != vb.fmt) return FP4_ERR_UNSUPPORTED;
+  if (va.had_on != vb.had_on || (va.had_on && va.had_signs != vb.had_signs)) return FP4_ERR_UNSUPPORTED;
+  if (va.k != vb.k || va.k <= 0 || va.k % 128 != 0 || va.rows <= 0 || vb.rows <= 0) return FP4_ERR_SHAPE;
+  if (!fp4i_gemm_fits(va.rows, vb.rows, va.k)) return FP4_ERR_SHAPE;
+  const size_t need = va.ws_bytes + vb.ws_bytes;
+  if (need > 0) {
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) % kWsAlign) != 0) return FP4_ERR_WORKSPACE;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    if (va.raw) carve_raw(&va, base);
+    if (vb.raw) carve_raw(&vb, base + va.ws_bytes);
+    if (va.raw && (st = check_raw(A, va)) != FP4_OK) return st;
+    if (vb.raw && (st = check_raw(B, vb)) != FP4_OK) return st;
+  }
+  st = check_gemm_pair(&va.q, &vb.q, out_t, C, ldc);
+  if (st != FP4_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < 2; ++i) {
+    const fp4_operand* op = i == 0 ? A : B;
+    OperandView* v = i == 0 ? &va : &vb;
+    if (!v->raw) continue;
+    const RawSource rs = raw_source(op);
+    st = launch_quant(op->data, (fp4_dtype)op->dtype, rs.R, rs.C, op->ld, rs.axis, (fp4_rounding)op->rnd,
+                      op->seed, op->index_offset, 0, &v->q, nullptr, s);
+    if (st != FP4_OK) return st;
+  }
+  launch_gemm_pair(&va.q, &vb.q, out_t, C, ldc, s);
+  return hip_status();
+}
+
+// The address of `scratch` on each device, looked up once per device with
+// that device current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+fp4_status scratch_on_current_device(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP4_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP4_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+    else (void)hipGetLastError();
+  });
+  if (!g_scratch_ptr[dev]) return FP4_ERR_HIP;
+  *p = g_scratch_ptr[dev];
+  return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -490,41 +558,25 @@ size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B) {
 
 fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
                     int64_t ldc, void* ws, size_t ws_bytes, fp4_stream_t stream) {
+  return gemm_impl(A, B, out_t, C, ldc, ws, ws_bytes, stream);
+}
+
+fp4_status fp4_gemm_noalloc(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
+                            int64_t ldc, fp4_stream_t stream) {
   if (!C) return FP4_ERR_NULL;
   OperandView va, vb;
   fp4_status st = view_operand(A, &va);
   if (st != FP4_OK) return st;
   st = view_operand(B, &vb);
   if (st != FP4_OK) return st;
-  // Format, rotation and K agreement first: a RAW operand's K must suit the
-  // product before its workspace is sized.
-  if (va.fmt != vb.fmt) return FP4_ERR_UNSUPPORTED;
-  if (va.had_on != vb.had_on || (va.had_on && va.had_signs != vb.had_signs)) return FP4_ERR_UNSUPPORTED;
-  if (va.k != vb.k || va.k <= 0 || va.k % 128 != 0 || va.rows <= 0 || vb.rows <= 0) return FP4_ERR_SHAPE;
-  if (!fp4i_gemm_fits(va.rows, vb.rows, va.k)) return FP4_ERR_SHAPE;
   const size_t need = va.ws_bytes + vb.ws_bytes;
+  if (need > FP4_GEMM_NOALLOC_MAX_BYTES) return FP4_ERR_WORKSPACE;
+  void* ws = nullptr;
   if (need > 0) {
-    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) % kWsAlign) != 0) return FP4_ERR_WORKSPACE;
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    if (va.raw) carve_raw(&va, base);
-    if (vb.raw) carve_raw(&vb, base + va.ws_bytes);
-    if (va.raw && (st = check_raw(A, va)) != FP4_OK) return st;
-    if (vb.raw && (st = check_raw(B, vb)) != FP4_OK) return st;
-  }
-  st = check_gemm_pair(&va.q, &vb.q, out_t, C, ldc);
-  if (st != FP4_OK) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  for (int i = 0; i < 2; ++i) {
-    const fp4_operand* op = i == 0 ? A : B;
-    OperandView* v = i == 0 ? &va : &vb;
-    if (!v->raw) continue;
-    const RawSource rs = raw_source(op);
-    st = launch_quant(op->data, (fp4_dtype)op->dtype, rs.R, rs.C, op->ld, rs.axis, (fp4_rounding)op->rnd,
-                      op->seed, op->index_offset, 0, &v->q, nullptr, s);
+    st = scratch_on_current_device(&ws);
     if (st != FP4_OK) return st;
   }
-  launch_gemm_pair(&va.q, &vb.q, out_t, C, ldc, s);
-  return hip_status();
+  return gemm_impl(A, B, out_t, C, ldc, ws, need > 0 ? FP4_GEMM_NOALLOC_MAX_BYTES : 0, stream);
 }
 
 fp4_status fp4_noise_ratio(const double* noise, double* ratio, fp4_stream_t stream) {

@@ -359,6 +359,27 @@ size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B);
 fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
                     int64_t ldc, void* ws, size_t ws_bytes, fp4_stream_t stream);
 
+/* The workspace limit of fp4_gemm_noalloc: 128 MiB (both raw NVFP4 operands
+ * of a 32768 x 4096 by 11008 x 4096 product take 100.9 MB). */
+#define FP4_GEMM_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+
+/* fp4_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same product as fp4_gemm, with RAW operands quantized into a workspace the
+ * library owns instead of a caller buffer: a static device array of
+ * FP4_GEMM_NOALLOC_MAX_BYTES, one copy on each GPU the library runs on, held
+ * until the process ends. Its address on a device is looked up once, on the
+ * first call on that device that has a RAW operand (make that call outside
+ * graph capture). The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller still passes C.
+ * FP4_ERR_WORKSPACE when fp4_gemm_workspace_bytes(A, B) exceeds
+ * FP4_GEMM_NOALLOC_MAX_BYTES (nothing enqueued). Every call on a GPU shares
+ * that GPU's array and leaves its quantized operands there: calls with RAW
+ * operands that overlap on one GPU (other streams, other threads) race on it,
+ * so the caller serializes them. Otherwise as fp4_gemm. */
+fp4_status fp4_gemm_noalloc(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
+                            int64_t ldc, fp4_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

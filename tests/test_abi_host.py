@@ -331,6 +331,25 @@ def test_gemm_rejects_bad_raw_b(fp4):
     assert L.fp4_gemm(ctypes.byref(A), ctypes.byref(Bsr), 1, 0x50000, 48, 0x800000, need, None) == 3
 
 
+def test_gemm_noalloc_rejects_operands_beyond_its_workspace(fp4):
+    # Raw operands whose workspace exceeds the static array are refused before
+    # anything touches a device; so are the checks fp4_gemm makes.
+    L = fp4.lib()
+    assert fp4.FP4_GEMM_NOALLOC_MAX_BYTES == 128 << 20
+    x = _raw_op(fp4, rows=32768, k=4096)
+    w = _raw_op(fp4, rows=11008, k=4096)
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(x), ctypes.byref(w)) <= fp4.FP4_GEMM_NOALLOC_MAX_BYTES
+    big = _raw_op(fp4, rows=65536, k=4096)
+    need = L.fp4_gemm_workspace_bytes(ctypes.byref(big), ctypes.byref(w))
+    assert need > fp4.FP4_GEMM_NOALLOC_MAX_BYTES
+    assert L.fp4_gemm_noalloc(ctypes.byref(big), ctypes.byref(w), 1, 0x50000, 11008, None) == 7
+    assert L.fp4_gemm_noalloc(ctypes.byref(x), ctypes.byref(w), 1, None, 11008, None) == 1
+    assert L.fp4_gemm_noalloc(None, ctypes.byref(w), 1, 0x50000, 11008, None) == 1
+    A, B = _t(fp4), _t(fp4, fmt=1)
+    assert L.fp4_gemm_noalloc(ctypes.byref(_q_op(fp4, A)), ctypes.byref(_q_op(fp4, B)), 1, 0x50000, 128,
+                              None) == 4
+
+
 def test_noise_ratio_rejects_bad_arguments(fp4):
     L = fp4.lib()
     assert L.fp4_noise_ratio(None, 0x60000, None) == 1
