@@ -25,6 +25,12 @@ with the caches evicted before each call.
 `roofline` is for the dominant kernel (the NVFP4 GEMM), timed with HIP events
 on the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded
 sample of the same step and scales it to the same unit.
+`large_step` times the large-layer step the same way (hidden 8192, MLP 28672,
+16384 tokens: NVFP4 fwd + bwd, RTN forward, SR on the backward operands).
+`measured_ceilings` puts what the chip reaches on this machine beside the
+data-sheet peaks: loops of the two MFMA instructions the GEMMs issue, and
+streaming passes (read only, copy, and a quantize-like 4:1 read:write pass)
+at their best grid size.
 """
 from __future__ import annotations
 
@@ -40,6 +46,8 @@ if ROOT not in sys.path:
 
 TOKENS, D_IN, D_OUT = 32768, 4096, 11008
 GEMM_FLOP = 2.0 * TOKENS * D_IN * D_OUT          # each of fwd, dgrad, wgrad
+L_TOKENS, L_IN, L_OUT = 16384, 8192, 28672       # the large layer
+L_GEMM_FLOP = 2.0 * L_TOKENS * L_IN * L_OUT
 PEAK_F16_TFLOPS = 2500.0                         # dense MFMA, MI355X
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
@@ -169,6 +177,186 @@ def make_extras(fp4, X, W, dY, signs16):
     return ops, q
 
 
+def make_large_step(fp4, X, W, dY):
+    """The large layer's NVFP4 step: each tensor's amax pass and one fused
+    pass for both of its orientations (X, W: RTN along K + SR along the other
+    axis; dY: SR along both), then the three GEMMs (fwd bf16 out, dgrad and
+    wgrad fp32 out)."""
+    import torch
+
+    T, I, O = L_TOKENS, L_IN, L_OUT
+    Q = fp4.QTensor
+    NV = fp4.FP4_NVFP4
+    RTN, SR = fp4.FP4_RTN, fp4.FP4_SR
+    seed = lambda role: (4 << 8) | role
+    q = {"X": Q(T, I, NV), "Xt": Q(I, T, NV), "W": Q(O, I, NV), "Wt": Q(I, O, NV),
+         "dY": Q(T, O, NV), "dYt": Q(O, T, NV)}
+    for a, b in (("Xt", "X"), ("Wt", "W"), ("dYt", "dY")):
+        q[a].amax = q[b].amax
+    outs = {"Y": torch.empty((T, O), dtype=torch.bfloat16, device="cuda"),
+            "dX": torch.empty((T, I), dtype=torch.float32, device="cuda"),
+            "dW": torch.empty((O, I), dtype=torch.float32, device="cuda")}
+    dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
+    ops = [
+        ("quant X nv dual (rtn K, sr tokens)", "q", lambda: dual(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
+         algorithmic_bytes(T * I, 2, 16, True, 2)),
+        ("quant W nv dual (rtn K, sr out)", "q", lambda: dual(W, RTN, 0, SR, seed(4), q["W"], q["Wt"]),
+         algorithmic_bytes(O * I, 2, 16, True, 2)),
+        ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"]), L_GEMM_FLOP),
+        ("quant dY nv dual (sr both)", "q", lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
+         algorithmic_bytes(T * O, 2, 16, True, 2)),
+        ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"]), L_GEMM_FLOP),
+        ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), L_GEMM_FLOP),
+    ]
+    return ops, outs, q
+
+
+def run_step(ops, steps, warmup):
+    """Time `steps` passes of the op list after `warmup` untimed ones: the
+    wall-clock step time between two synchronizations, and each op's HIP-event
+    times on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        for _, _, fn, _ in ops:
+            fn()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, (_, _, fn, _) in enumerate(ops):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    per_op = [op_record(name, kind, units, [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)])
+              for i, (name, kind, _, units) in enumerate(ops)]
+    return ms_per_step, per_op
+
+
+def large_step_record(fp4, steps, warmup):
+    """Time the large layer's step (hidden 8192, MLP 28672, 16384 tokens)."""
+    import torch
+
+    from fp4_fully_quantized_amd import workloads
+
+    X = workloads.device_tensor("large", "X")
+    W = workloads.device_tensor("large", "W")
+    dY = workloads.device_tensor("large", "dY")
+    ops, outs, q = make_large_step(fp4, X, W, dY)
+    torch.cuda.synchronize()
+    ms, per_op = run_step(ops, steps, warmup)
+    gemms = [r for r, o in zip(per_op, ops) if o[1] == "g_nv"]
+    quant = [(r, o) for r, o in zip(per_op, ops) if o[1] == "q"]
+    q_ms = sum(r["avg_ms"] for r, _ in quant)
+    q_bytes = sum(o[3] for _, o in quant)
+    del X, W, dY, ops, outs, q
+    torch.cuda.empty_cache()
+    return {
+        "workload": ("large-layer step: hidden 8192, MLP 28672, 16384 tokens; NVFP4 amax + one fused "
+                     "quantize pass per tensor (RTN fwd, SR bwd), fwd (bf16 out), dgrad and wgrad (fp32 out)"),
+        "ms_per_step": round(ms, 3),
+        "TFLOPs": round(3 * L_GEMM_FLOP / (ms * 1e-3) / 1e12, 1),
+        "gemm_avg_ms": round(sum(r["avg_ms"] for r in gemms) / len(gemms), 4),
+        "gemm_frac_f16_peak": round(sum(r["frac_f16_peak"] for r in gemms) / len(gemms), 4),
+        "gemm_frac_fp4_peak": round(sum(r["frac_fp4_peak"] for r in gemms) / len(gemms), 4),
+        "quantize_ms": round(q_ms, 4),
+        "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "quantize_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+        "targets": {
+            "quantize_ms": 1.067,     # 5976.9 MB of separate passes at 70% of 8 TB/s
+            "gemm_nv_ms_at_60pct_f16_peak": 5.097,
+            "gemm_ms_at_60pct_fp4_peak": 1.274,
+        },
+        "per_op": per_op,
+    }
+
+
+def measure_ceilings(steps: int = 10):
+    """What the chip reaches on this machine: the two MFMA instructions in tight
+    loops (every SIMD busy, four changing operand sets, eight independent
+    accumulators per wave) and streaming passes over 2 GiB buffers, each at
+    the best of a few grid sizes."""
+    import ctypes
+
+    import torch
+
+    from fp4_fully_quantized_amd import build as fp4_build
+
+    if not os.path.exists(fp4_build.MEASURE_LIB):
+        raise RuntimeError(f"{fp4_build.MEASURE_LIB} is not built; run python -m fp4_fully_quantized_amd.build")
+    L = ctypes.CDLL(fp4_build.MEASURE_LIB)
+    c = ctypes
+    for fn in ("fp4m_mfma_f16", "fp4m_mfma_fp4"):
+        getattr(L, fn).argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_void_p]
+    L.fp4m_stream_read.argtypes = [c.c_void_p, c.c_uint64, c.c_void_p, c.c_int, c.c_void_p]
+    for fn in ("fp4m_stream_copy", "fp4m_stream_read4_write1"):
+        getattr(L, fn).argtypes = [c.c_void_p, c.c_void_p, c.c_uint64, c.c_int, c.c_void_p]
+    stream = c.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(launch, reps):
+        for _ in range(2):
+            assert launch() == 0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            assert launch() == 0
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]   # median, ms
+
+    out = {}
+    # MFMA loops. f16 operands: decoded NVFP4-like values (e2m1 x E4M3, exact
+    # in f16); FP4 operands: random codes with unit E8M0 scales.
+    g = torch.Generator(device="cuda").manual_seed(5)
+    grid, iters = 1024, 4000
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    grid_vals = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device="cuda")
+    codes = torch.randint(0, 8, (8 * 64 * 8,), generator=g, device="cuda")
+    sign = torch.randint(0, 2, (8 * 64 * 8,), generator=g, device="cuda") * 2 - 1
+    scl = torch.pow(2.0, torch.randint(-3, 4, (8 * 64 * 8,), generator=g, device="cuda").float()) * \
+        (1 + torch.randint(0, 8, (8 * 64 * 8,), generator=g, device="cuda").float() / 8)
+    ops_f16 = (grid_vals[codes] * sign * scl).to(torch.float16).contiguous()
+    ops_fp4 = torch.randint(0, 256, (8 * 64 * 16,), generator=g, dtype=torch.int32, device="cuda").to(torch.uint8)
+    for name, fn, ops, flop in (("mfma_f16", L.fp4m_mfma_f16, ops_f16, 32768),
+                                ("mfma_fp4", L.fp4m_mfma_fp4, ops_fp4, 131072)):
+        ms = timed(lambda: fn(ops.data_ptr(), sink.data_ptr(), grid, iters, stream), steps)
+        out[name + "_TFLOPs"] = round(grid * 4 * iters * 8 * flop / (ms * 1e-3) / 1e12, 1)
+    out["mfma_f16_frac_of_spec"] = round(out["mfma_f16_TFLOPs"] / PEAK_F16_TFLOPS, 3)
+    out["mfma_fp4_frac_of_spec"] = round(out["mfma_fp4_TFLOPs"] / PEAK_FP4_TFLOPS, 3)
+    del sink, ops_f16, ops_fp4
+    # Streaming passes over 2 GiB (beyond the 256 MB memory-side cache).
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    passes = {
+        "hbm_stream_read": (lambda gr: L.fp4m_stream_read(src.data_ptr(), nbytes, word.data_ptr(), gr, stream),
+                            nbytes),
+        "hbm_stream_copy": (lambda gr: L.fp4m_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, gr, stream),
+                            2 * nbytes),
+        "hbm_stream_read4_write1": (lambda gr: L.fp4m_stream_read4_write1(src.data_ptr(), dst.data_ptr(),
+                                                                          nbytes, gr, stream),
+                                    nbytes + nbytes // 4),
+    }
+    for name, (launch, moved) in passes.items():
+        best = None
+        for gr in (1024, 2048, 4096, 8192, 16384):
+            ms = timed(lambda: launch(gr), steps)
+            gbps = moved / (ms * 1e-3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, gr)
+        out[name + "_GBps"] = round(best[0], 1)
+        out[name + "_grid"] = best[1]
+    out["hbm_best_frac_of_spec"] = round(max(out[k + "_GBps"] for k in passes) / PEAK_HBM_GBS, 3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_ops(ops, steps, warmup, flush=None):
     """Per-op records (HIP events around each call on the current stream).
     With `flush` (a device buffer larger than the 256 MB last-level cache),
@@ -240,42 +428,54 @@ def op_record(name, kind, units, times_ms):
     return rec
 
 
-def cpu_baseline():
-    """The oracle on a bounded sample of the step: every quantization pass on a
-    row slab of its tensor and every GEMM reference on a few output rows, each
-    scaled linearly to the full step, reported in the bench's unit."""
+def to_host_bits(t):
+    """A bf16 device tensor as numpy uint16 bit patterns on the host."""
+    import numpy as np
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(host):
+    """The oracle on the host cores: every quantization pass of the step at
+    full size on the step's own tensors (host copies), and every GEMM
+    reference on a bounded sample of output rows scaled linearly to the full
+    step, reported in the bench's unit."""
     import numpy as np
 
-    from fp4_fully_quantized_amd import workloads
     from oracle import oracle as orc
 
     orc.lib()
-    rows_q = 1024         # rows of each quantized tensor in the sample
-    rows_g = 512          # output rows of each GEMM in the sample
+    X, W, dY = host["X"], host["W"], host["dY"]
     t_quant = 0.0
-    t_gemm = 0.0
-    X = workloads.host_tensor("llama7b", "X", shape=(rows_q, D_IN))
-    W = workloads.host_tensor("llama7b", "W", shape=(rows_q, D_IN))
-    dY = workloads.host_tensor("llama7b", "dY", shape=(rows_q, D_OUT))
-    # (tensor slab, full element count of the pass, kwargs)
+    sg = orc.hadamard_signs(3)
     passes = [
-        (X, TOKENS * D_IN, dict(fmt=0)), (W, D_OUT * D_IN, dict(fmt=0)),
-        (dY, TOKENS * D_OUT, dict(fmt=0, rnd=1, seed=1)),
-        (W, D_OUT * D_IN, dict(axis=1, fmt=0, rnd=1, seed=4)),
-        (dY, TOKENS * D_OUT, dict(axis=1, fmt=0, rnd=1, seed=2)),
-        (X, TOKENS * D_IN, dict(axis=1, fmt=0, rnd=1, seed=3)),
-        (X, TOKENS * D_IN, dict(fmt=1, had_on=True, had_signs=orc.hadamard_signs(3))),
-        (W, D_OUT * D_IN, dict(fmt=1, had_on=True, had_signs=orc.hadamard_signs(3))),
+        (X, dict(fmt=0)), (X, dict(axis=1, fmt=0, rnd=1, seed=(2 << 8) | 3)),
+        (W, dict(fmt=0)), (W, dict(axis=1, fmt=0, rnd=1, seed=(2 << 8) | 4)),
+        (dY, dict(fmt=0, rnd=1, seed=(2 << 8) | 1)), (dY, dict(axis=1, fmt=0, rnd=1, seed=(2 << 8) | 2)),
+        (X, dict(fmt=1, had_on=True, had_signs=sg)), (W, dict(fmt=1, had_on=True, had_signs=sg)),
     ]
-    for slab, full, kw in passes:
+    for src, kw in passes:
         t0 = time.perf_counter()
-        orc.quantize(slab, **kw)
-        dt = time.perf_counter() - t0
-        t_quant += dt * full / slab.size
+        orc.quantize(src, **kw)
+        t_quant += time.perf_counter() - t0
     # GEMM references (the oracle's gemm_ref: dequantize both operands exactly
-    # to FP64, then the FP64 products A B^T and |A| |B|^T), timed step by step
-    # so that B's dequantization counts once per GEMM and the products scale
-    # with the full output size.
+    # to FP64, then the FP64 products A B^T and |A| |B|^T), on rows_g output
+    # rows x up to 1024 columns, timed step by step so that B's dequantization
+    # counts once per GEMM and the products scale with the full output size.
+    rows_g = 512
+    t_gemm = 0.0
     rng = np.random.default_rng(0)
     for M, N, K in [(TOKENS, D_OUT, D_IN), (TOKENS, D_IN, D_OUT), (D_OUT, D_IN, TOKENS),
                     (TOKENS, D_OUT, D_IN)]:
@@ -298,10 +498,11 @@ def cpu_baseline():
         "unit": "TFLOP/s",
         "cores": orc.num_threads(),
         "kind": "oracle",
-        "sample": (f"every quantization pass of the step on a {rows_q}-row slab of its tensor "
-                   f"and every GEMM reference on {rows_g} output rows x up to 1024 columns, "
-                   f"each scaled linearly to the full Llama-7B step; extrapolated step "
-                   f"{t_step:.1f} s (quantize {t_quant:.1f} s, FP64 GEMM {t_gemm:.1f} s)"),
+        "cpu_model": cpu_model(),
+        "sample": (f"every quantization pass of the Llama-7B step at full size on the step's own tensors "
+                   f"({t_quant:.1f} s measured), and every GEMM reference on {rows_g} output rows x up to 1024 "
+                   f"columns scaled linearly to the full outputs ({t_gemm:.1f} s extrapolated); step "
+                   f"{t_step:.1f} s"),
     }
 
 
@@ -311,6 +512,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large-step", action="store_true",
+                    help="skip the large layer's step (timed after the Llama-7B step)")
     ap.add_argument("--separate-passes", action="store_true",
                     help="quantize each orientation with its own pass instead of one read per tensor")
     args = ap.parse_args()
@@ -335,30 +538,7 @@ def main():
     ops, outs, q = make_step(fp4, X, W, dY, signs, separate=args.separate_passes)
     torch.cuda.synchronize()
 
-    def step(events=None):
-        for i, (_, _, fn, _) in enumerate(ops):
-            if events is not None:
-                events[i][0].record()
-            fn()
-            if events is not None:
-                events[i][1].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    per_op = [op_record(name, kind, units, [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
-              for i, (name, kind, _, units) in enumerate(ops)]
+    ms_per_step, per_op = run_step(ops, args.steps, args.warmup)
 
     # Adjacent passes, timed after the step's timed region.
     extra_ops, extra_q = make_extras(fp4, X, W, dY, fp4.fp4_hadamard_signs(4))
@@ -411,7 +591,10 @@ def main():
                          "transposed quantization) and MXFP4+Hadamard fwd"),
             "tokens": TOKENS, "in_features": D_IN, "out_features": D_OUT,
             "gemms_per_step": 4, "quantizations_per_step": 8,
-            "quantize_launches": "separate" if args.separate_passes else "one read per NVFP4 tensor",
+            "quantize_launches": ("separate passes: an amax pass and one quantize pass per orientation"
+                                  if args.separate_passes else
+                                  "per NVFP4 tensor: an amax pass, then one pass that quantizes both "
+                                  "orientations (two reads of the tensor)"),
         },
         "quantize_GBps_aggregate": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "hbm_copy_GBps": round(copy_gbps, 1),
@@ -428,10 +611,26 @@ def main():
             "traffic": traffic,
         },
     }
+    # The chip's measured ceilings, then the large layer's step.
+    ceilings = measure_ceilings()
+    ceilings["rocclr_copy_GBps"] = round(copy_gbps, 1)
+    out["measured_ceilings"] = ceilings
+    out["roofline"]["measured_peak"] = ceilings["mfma_f16_TFLOPs"]
+    out["roofline"]["frac_of_measured_peak"] = round(achieved / ceilings["mfma_f16_TFLOPs"], 4)
+    stream_q = ceilings["hbm_stream_read4_write1_GBps"]
+    for recs in (per_op, extras, cold):
+        for r in recs:
+            if "GBps" in r:
+                r["frac_stream"] = round(r["GBps"] / stream_q, 3)
+    host = None
     if not args.no_cpu_baseline:
-        del X, W, dY, ops, outs, q
-        torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline()
+        host = {k: to_host_bits(v) for k, v in (("X", X), ("W", W), ("dY", dY))}
+    del X, W, dY, ops, outs, q
+    torch.cuda.empty_cache()
+    if not args.no_large_step:
+        out["large_step"] = large_step_record(fp4, args.steps, args.warmup)
+    if host is not None:
+        out["cpu_baseline"] = cpu_baseline(host)
     print(json.dumps(out), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Builds libfp4.so (gfx950) in-tree from csrc/ with hipcc.
+"""Builds libfp4.so (gfx950) in-tree from csrc/ with hipcc, and beside it
+libfp4_measure.so (the benchmark's on-box ceiling measurements).
 
     python -m fp4_fully_quantized_amd.build
 
@@ -18,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4.so")
 SOURCES = ["quant.hip", "quant_dual.hip", "quant_2d.hip", "gemm.hip", "abi.cpp"]
+# The chip's measured ceilings (MFMA loops, streaming passes) for the benchmark.
+MEASURE_SOURCES = ["measure.hip"]
+MEASURE_LIB = os.path.join(PKG, "libfp4_measure.so")
 ARCH = os.environ.get("FP4_OFFLOAD_ARCH", "gfx950")
 
 
@@ -33,10 +37,16 @@ def flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
+    _build_lib(SOURCES, LIB, verbose)
+    _build_lib(MEASURE_SOURCES, MEASURE_LIB, verbose)
+    return LIB
+
+
+def _build_lib(sources: list[str], lib: str, verbose: bool) -> None:
     os.makedirs(BUILD, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD, src + ".o")
         cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
@@ -54,10 +64,9 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(f"[fp4 build] {src}:\n{out}\n")
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -11,6 +11,10 @@ same counters read for the library's kernels.
 reads the rocprofv3 CSV output of the profiling commands listed in
 PROFILE_COMMANDS (under the folder OUT) and writes the text summaries and
 profiles/traffic.json that the benchmark's roofline figure reads.
+
+    python -m fp4_fully_quantized_amd.profiling summarize-trace OUT
+
+writes only the kernel-time summaries, from the kernel-trace run ("stats").
 """
 import sys
 
@@ -83,12 +87,15 @@ PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_bench -o bench -- "
              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
-             "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
+             "--no-large-step",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
-             "-d OUT/pmc_write -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "-d OUT/pmc_write -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
+             "--no-large-step",
     "util": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA "
             "GRBM_GUI_ACTIVE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
-            "-d OUT/pmc_util -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+            "-d OUT/pmc_util -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
+            "--no-large-step",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o copy -- "
                   "python3 -m fp4_fully_quantized_amd.profiling copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o copy -- "
@@ -108,6 +115,15 @@ GROUPS = [
     ("both orientations' amaxes, one rotated (one read)", r"^k_amax_pair<"),
     ("2-D block quantize (both orientations)", r"^k_quant_2d<"),
 ]
+# The benchmark's on-box ceiling measurements (libfp4_measure.so), launched
+# between the Llama-7B part of the run and the large layer's step.
+CEILING_KERNELS = [
+    ("f16 MFMA loop (v_mfma_f32_32x32x16_f16)", r"^k_mfma_f16$"),
+    ("scaled FP4 MFMA loop (v_mfma_scale_f32_32x32x64_f8f6f4)", r"^k_mfma_fp4$"),
+    ("streaming read", r"^k_stream_read$"),
+    ("streaming copy", r"^k_stream_copy$"),
+    ("streaming read 16 B / write 4 B per lane", r"^k_stream_read4_write1$"),
+]
 STEPS, WARMUP = 10, 3   # of the stats command
 PMC_STEPS, PMC_WARMUP = 1, 1   # of the counter commands
 CUS, SIMDS_PER_CU, XCDS = 256, 4, 8
@@ -120,6 +136,14 @@ CUS, SIMDS_PER_CU, XCDS = 256, 4, 8
 # the step's quantize calls 2 + K times with the caches evicted before each.
 TOKENS, D_IN, D_OUT = 32768, 4096, 11008
 _NX, _NW, _NY = TOKENS * D_IN, D_OUT * D_IN, TOKENS * D_OUT
+# Algorithmic bytes of each NVFP4 GEMM: both operands' codes (0.5 B) and E4M3
+# scales (1/16 B) per element read once, the output written once.
+_OPND = 0.5 + 1 / 16
+GEMM_ALGO_BYTES = {
+    "fwd": (_NX + _NW) * _OPND + TOKENS * D_OUT * 2,      # Y bf16
+    "dgrad": (_NY + _NW) * _OPND + TOKENS * D_IN * 4,     # dX fp32
+    "wgrad": (_NY + _NX) * _OPND + D_OUT * D_IN * 4,      # dW fp32
+}
 _DUAL = 2 + 2 * (0.5 + 1 / 16)      # bf16 read + two orientations of codes and E4M3 scales
 _MX = 2 + 0.5 + 1 / 32
 _GF = 2.0 * TOKENS * D_IN * D_OUT
@@ -179,17 +203,30 @@ def _per_dispatch(csv_path: str):
     return [tuple(d[k]) for k in sorted(d)]
 
 
-def _trace_groups(trace_csv: str):
-    """{group label: [durations in ns]} from a rocprofv3 kernel_trace.csv."""
+def _trace_parts(trace_csv: str):
+    """The kernel trace's dispatches [(short name, duration ns)] in launch
+    order, split into the Llama-7B part of the run, the ceiling measurements
+    and the large layer's part (after the last measurement kernel)."""
     import csv
     import re
 
-    out = {label: [] for label, _ in GROUPS}
-    for r in csv.DictReader(open(trace_csv)):
-        name = short_name(r["Kernel_Name"])
-        for label, rx in GROUPS:
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    d = [(short_name(r["Kernel_Name"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows]
+    meas = [i for i, (n, _) in enumerate(d) if any(re.search(rx, n) for _, rx in CEILING_KERNELS)]
+    if not meas:
+        return d, [], []
+    return d[:meas[0]], d[meas[0]:meas[-1] + 1], d[meas[-1] + 1:]
+
+
+def _group(dispatches, groups):
+    """{group label: [durations in ns]} of the dispatches whose names match."""
+    import re
+
+    out = {label: [] for label, _ in groups}
+    for name, dur in dispatches:
+        for label, rx in groups:
             if re.search(rx, name):
-                out[label].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                out[label].append(dur)
     return out
 
 
@@ -199,8 +236,94 @@ def _gemm_shape(grid: int, index: int):
     return names[index % 3]
 
 
+def _stats_lines(groups):
+    """Group rows of a part of the run that launches each group the same
+    number of times per step: all launches, and the timed steps' alone."""
+    out = ["| group | launches | avg us | avg us (timed) | min us | max us |", "|---|---|---|---|---|---|"]
+    for label, d in groups.items():
+        if d:
+            per_step = len(d) // (WARMUP + STEPS)
+            timed = d[per_step * WARMUP:]
+            out.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {sum(timed) / len(timed) / 1e3:.1f} | "
+                       f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
+    return out
+
+
+# The large layer's step in launch order (bench.py make_large_step).
+L_TOKENS, L_IN, L_OUT = 16384, 8192, 28672
+LARGE_GROUPS = [
+    ("tensor amax (X, W, dY)", r"^k_amax<"),
+    ("quantize X, both orientations (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,"),
+    ("quantize dY, both orientations (SR)", r"^k_quant_dual<0, 1, 1,"),
+    ("NVFP4 GEMM fwd 16384x28672x8192 (bf16 out)", r"^k_gemm<0, 256, true>"),
+    ("NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)", r"^k_gemm<0, 256, false>"),
+]
+
+
+def _write_large_step(dispatches, command, profiles_dir):
+    import os
+
+    groups = _group(dispatches, LARGE_GROUPS)
+    # The X and W dual passes share a kernel; split dgrad / wgrad by launch order.
+    g = groups.pop("NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)")
+    groups["NVFP4 GEMM dgrad 16384x8192x28672 (fp32 out)"] = g[0::2]
+    groups["NVFP4 GEMM wgrad 28672x8192x16384 (fp32 out)"] = g[1::2]
+    lines = [
+        "# Kernel time of the large layer's step (bench.py `large_step`)",
+        "",
+        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; "
+        "`OUT` = the folder the run writes its CSV files to):",
+        "",
+        "```", command, "```",
+        "",
+        f"The large layer: hidden {L_IN}, MLP {L_OUT}, {L_TOKENS} tokens. One step = for each of X, W and dY "
+        "an amax pass and one pass that quantizes both orientations (NVFP4; X and W: RTN along K, SR along "
+        "the other axis; dY: SR along both), the fwd GEMM (bf16 out), dgrad and wgrad (fp32 out); "
+        f"{WARMUP} warm-up + {STEPS} timed steps, after the rest of the run. `avg us (timed)` leaves out the "
+        "warm-up steps. X's and W's dual passes run the same kernel (the group holds both).",
+        "",
+    ] + _stats_lines(groups) + [""]
+    with open(os.path.join(profiles_dir, "large_layer_step_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
+def _write_ceilings(dispatches, command, profiles_dir):
+    import os
+
+    groups = _group(dispatches, CEILING_KERNELS)
+    lines = [
+        "# Kernel time of the chip-ceiling measurements (bench.py `measured_ceilings`)",
+        "",
+        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; "
+        "`OUT` = the folder the run writes its CSV files to):",
+        "",
+        "```", command, "```",
+        "",
+        "The MFMA loops run 1024 workgroups of 4 waves, each wave 4000 iterations of 8 MFMAs "
+        "(32768 FLOP per f16 instruction, 131072 per FP4 instruction); the streaming passes cover 2 GiB "
+        "at five grid sizes each (2 warm-up + 10 timed launches per size, so the averages mix grid sizes; "
+        "the benchmark reports the best size's median).",
+        "",
+        "| kernel | launches | avg us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for label, d in groups.items():
+        if d:
+            lines.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
+                         f"{max(d) / 1e3:.1f} |")
+    lines.append("")
+    with open(os.path.join(profiles_dir, "chip_ceilings_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def summarize(out_dir: str, profiles_dir: str) -> None:
-    import json
+    summarize_trace(out_dir, profiles_dir)
+    summarize_counters(out_dir, profiles_dir)
+
+
+def summarize_trace(out_dir: str, profiles_dir: str) -> None:
+    """Kernel-time summaries of the kernel-trace run: the Llama-7B part of the
+    benchmark, the large layer's step and the chip-ceiling measurements."""
     import os
 
     stats_csv = os.path.join(out_dir, "prof_bench", "bench_kernel_stats.csv")
@@ -208,7 +331,8 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
     cmd = lambda k: PROFILE_COMMANDS[k]   # OUT: the folder the runs write their CSV files to
 
     # ---- kernel time of the step
-    groups = _trace_groups(trace_csv)
+    llama, ceil, large = _trace_parts(trace_csv)
+    groups = _group(llama, GROUPS)
     lines = [
         "# Kernel time of the Llama-7B layer step (bench.py)",
         "",
@@ -225,7 +349,9 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
         "dY pass, the 2-D quantization of W), 2 warm-up + 10 timed calls each, then the step's quantize "
         "calls again with the caches evicted before each call (torch's reduction over a 1 GiB buffer), "
         "2 + 10 calls each, and a 1 GiB device copy (`__amd_rocclr_copyBuffer`, 13 launches) that measures "
-        "the copy bandwidth; the other torch kernels are the one-time input generation.",
+        "the copy bandwidth; the other torch kernels are the one-time input generation. The same run then "
+        "measures the chip's ceilings (`chip_ceilings_kernel_stats.md`) and times the large layer's step "
+        "(`large_layer_step_kernel_stats.md`); this table covers the dispatches before those.",
         "",
         "`avg us (timed)` (GEMMs, which only the step launches) leaves out the warm-up steps' launches (the "
         "first launches of a run are slower while the clock settles); that is the figure to set against the "
@@ -250,9 +376,21 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
                 timed = f"{sum(t) / len(t) / 1e3:.1f}"
             lines.append(f"| {label} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {timed} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
-    lines += ["", "## Per kernel (`--stats` summary)", "", kernel_stats_table(stats_csv), ""]
+    lines += ["", "## Per kernel over the whole run (`--stats` summary)", "", kernel_stats_table(stats_csv), ""]
     with open(os.path.join(profiles_dir, "llama7b_step_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines))
+    if large:
+        _write_large_step(large, cmd("stats"), profiles_dir)
+    if ceil:
+        _write_ceilings(ceil, cmd("stats"), profiles_dir)
+
+
+def summarize_counters(out_dir: str, profiles_dir: str) -> None:
+    """HBM traffic and MFMA / VALU utilisation from the counter runs."""
+    import json
+    import os
+
+    cmd = lambda k: PROFILE_COMMANDS[k]   # OUT: the folder the runs write their CSV files to
 
     # ---- HBM traffic of the NVFP4 GEMM
     # Only the copy dispatches (the fill that creates the source is left out).
@@ -272,7 +410,8 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
     assert len(fe) == len(wr) and len(fe) % 3 == 0, (len(fe), len(wr))
     rows = []
     for i, ((_, grid, fk), (_, _, wk)) in enumerate(zip(fe, wr)):
-        rows.append((_gemm_shape(grid, i), grid // 256, fk, wk, (fk * f_fac + wk * w_fac) * 1024))
+        rows.append((_gemm_shape(grid, i), grid // 256, fk, wk, (fk * f_fac + wk * w_fac) * 1024,
+                     list(GEMM_ALGO_BYTES.values())[i % 3]))
     avg = sum(r[4] for r in rows) / len(rows)
     lines = [
         "# HBM traffic of the NVFP4 GEMM (Llama-7B layer: fwd, dgrad, wgrad)",
@@ -289,16 +428,22 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
         "",
         "## Per dispatch (KiB as read, then bytes after calibration)",
         "",
-        "| GEMM | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) |",
-        "|---|---|---|---|---|",
+        "| GEMM | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | algorithmic | ratio |",
+        "|---|---|---|---|---|---|---|",
     ]
-    for name, wgs, fk, wk, b in rows:
-        lines.append(f"| {name} | {wgs} WGs | {fk:.0f} | {wk:.0f} | {b / 1e6:.1f} MB |")
+    for name, wgs, fk, wk, b, algo in rows:
+        lines.append(f"| {name} | {wgs} WGs | {fk:.0f} | {wk:.0f} | {b / 1e6:.1f} MB | {algo / 1e6:.1f} MB | "
+                     f"{b / algo:.2f} |")
+    algo_avg = sum(GEMM_ALGO_BYTES.values()) / 3
     lines += [
         "",
-        f"Average over the NVFP4 GEMM launches: {avg / 1e6:.1f} MB per launch (this is `roofline.traffic`).",
-        "Algorithmic bytes per launch are 100.7 MB of operands (codes + scales of both operands) plus the "
-        "output (721 MB bf16 fwd, 537 MB fp32 dgrad, 180 MB fp32 wgrad).",
+        f"Average over the NVFP4 GEMM launches: {avg / 1e6:.1f} MB per launch (this is `roofline.traffic`), "
+        f"against {algo_avg / 1e6:.1f} MB of algorithmic bytes on average ({avg / algo_avg:.2f}x).",
+        "Algorithmic bytes per launch: both operands' codes (0.5 B) and E4M3 scales (1/16 B) per element, read "
+        "once, plus the output written once: fwd X + W (75.5 + 25.4 MB) + Y bf16 (721.4 MB) = "
+        f"{GEMM_ALGO_BYTES['fwd'] / 1e6:.1f} MB; dgrad dY + W^T (202.9 + 25.4 MB) + dX fp32 (536.9 MB) = "
+        f"{GEMM_ALGO_BYTES['dgrad'] / 1e6:.1f} MB; wgrad dY^T + X^T (202.9 + 75.5 MB) + dW fp32 (180.4 MB) = "
+        f"{GEMM_ALGO_BYTES['wgrad'] / 1e6:.1f} MB.",
         "",
         f"GEMM source digest: `{source_digest()}`.",
         "",
@@ -396,10 +541,10 @@ def summarize(out_dir: str, profiles_dir: str) -> None:
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "copy":
         copy()
-    elif len(sys.argv) > 2 and sys.argv[1] == "summarize":
+    elif len(sys.argv) > 2 and sys.argv[1] in ("summarize", "summarize-trace"):
         import os
 
-        summarize(sys.argv[2], os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                                            "profiles"))
+        prof = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+        (summarize if sys.argv[1] == "summarize" else summarize_trace)(sys.argv[2], prof)
     else:
         print(__doc__)

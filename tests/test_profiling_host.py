@@ -112,3 +112,47 @@ def test_summarize_on_synthetic_counters(tmp_path):
     t = json.loads((prof / "traffic.json").read_text())
     assert t["fetch_factor"] == 2.0 and t["write_factor"] == 1.0
     assert t["nv_gemm_bytes_per_launch"] == round(p._GF * 1.0)
+
+
+def _large_names(steps, warmup):
+    step = ["k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
+            "k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
+            "k_gemm<0, 256, true>",
+            "k_amax<true, false>", "k_quant_dual<0, 1, 1, true, false, false, false>",
+            "k_gemm<0, 256, false>", "k_gemm<0, 256, false>"]
+    return step * (warmup + steps)
+
+
+def test_trace_split_into_llama_ceilings_and_large_step(tmp_path):
+    """The kernel trace of a full benchmark run: the Llama-7B part, the ceiling
+    measurements, then the large layer's step, each summarized on its own
+    (durations chosen so each group's timed average is known)."""
+    ceil = ["k_mfma_f16", "k_mfma_fp4"] + ["k_stream_read", "k_stream_copy", "k_stream_read4_write1"]
+    names = _names(p.STEPS, p.WARMUP) + ["__amd_rocclr_copyBuffer"] + ceil + ["fill"] + \
+        _large_names(p.STEPS, p.WARMUP)
+    dur = {"k_gemm<0, 256, true>": 5_000_000, "k_gemm<0, 256, false>": 6_000_000}
+    trace, t = [], 0
+    n_large = len(_large_names(p.STEPS, p.WARMUP))
+    first_large = len(names) - n_large
+    for k, n in enumerate(names):
+        d = dur.get(n, 100_000) if k >= first_large else 1000
+        if k >= first_large and n == "k_gemm<0, 256, false>":
+            d = 6_000_000 if (k - first_large) % 9 == 7 else 7_000_000   # dgrad, then wgrad
+        trace.append([_raw(n), t, t + d])
+        t += d + 10
+    out = tmp_path / "out" / "prof_bench"
+    _write_csv(str(out / "bench_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
+    llama, ce, large = p._trace_parts(str(out / "bench_kernel_trace.csv"))
+    assert [n for n, _ in ce] == ceil
+    # the large part also holds the generation of its inputs ("fill")
+    assert len(large) == n_large + 1 and len(llama) == len(_names(p.STEPS, p.WARMUP)) + 1
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    p._write_large_step(large, "CMD", str(prof))
+    text = (prof / "large_layer_step_kernel_stats.md").read_text()
+    assert "| NVFP4 GEMM fwd 16384x28672x8192 (bf16 out) | 13 | 5000.0 | 5000.0 |" in text
+    assert "| NVFP4 GEMM dgrad 16384x8192x28672 (fp32 out) | 13 | 6000.0 | 6000.0 |" in text
+    assert "| NVFP4 GEMM wgrad 28672x8192x16384 (fp32 out) | 13 | 7000.0 | 7000.0 |" in text
+    assert "| tensor amax (X, W, dY) | 39 | 100.0 |" in text
+    p._write_ceilings(ce, "CMD", str(prof))
+    assert "| f16 MFMA loop" in (prof / "chip_ceilings_kernel_stats.md").read_text()
