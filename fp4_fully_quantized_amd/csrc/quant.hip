@@ -20,12 +20,11 @@
 //                  of lanes hold a block: one DPP butterfly stage).
 //  * k_amax_rot_rows  the same for the rotation down columns: each lane reads
 //                  16 rows x 8 columns and rotates each column in registers.
-//  * k_quant_cols  blocks along the contiguous axis: each lane owns 8
-//                  consecutive elements (one 16-byte bf16 load), a block spans
-//                  2 (NVFP4) or 4 (MXFP4) lanes; the block amax and the
-//                  Hadamard's cross-lane stages use DPP quad permutes; each
-//                  lane stores one dword of 8 codes (256 contiguous bytes per
-//                  wave).
+//  * k_quant_cols  blocks along the contiguous axis: each lane owns one whole
+//                  block (16 or 32 consecutive elements, 2-8 16-byte loads),
+//                  so the rotation's stages, the block amax and the block
+//                  scale run in registers without cross-lane traffic; each
+//                  lane stores its block's codes (8 or 16 bytes) and scale.
 //  * k_quant_rows  blocks along rows (the transposed orientation used by dgrad
 //                  and wgrad operands): a 256 x 64 tile is loaded with
 //                  coalesced 16-byte row loads into LDS (input format), each
@@ -163,6 +162,13 @@ __global__ __launch_bounds__(256) void k_amax_rot_rows(const void* __restrict__ 
 }
 
 
+// Blocks along the contiguous axis: every lane owns one whole block (16 or 32
+// consecutive elements of a row), a wave 64 consecutive blocks of one row (a
+// task). The lane loads its block with 16-byte loads (a wave reads one
+// contiguous 2 or 4 KiB run of bf16), applies the rotation's signs while the
+// values are still packed (one XOR flips two bf16 elements), runs every
+// butterfly stage and the block amax in registers, derives the block scale
+// once per block, and stores its codes (8 or 16 bytes) and its scale byte.
 template <int FMT, int RND, bool BF16, bool HAD, bool MON>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t C, int64_t ld,
                                                      uint32_t spr, uint32_t ntasks,
@@ -173,6 +179,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
                                                      double* noise) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
+  constexpr int LOADS = B * ES / 16;   // 16-byte loads per block
   const int lane = threadIdx.x & 63;
   double ng = 0.0, ne = 0.0;
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
@@ -182,62 +189,66 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
     sg = nv_tensor_scale(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
   }
-  const int sub = lane & (B / 8 - 1);  // position of this lane's 8 elements inside its block
   for (uint32_t t = wave; t < ntasks; t += nwaves) {
     const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
     const uint32_t r = tu / spr;
     const uint32_t seg = tu - r * spr;
-    const int64_t col = (int64_t)seg * 512 + lane * 8;
-    const bool active = col < C;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active) load8<BF16>(static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES, x);
-    if constexpr (HAD && FMT == NV) {
-      hadamard16_lane_pair(x, signs, sub);
-    } else if constexpr (HAD) {
-      // 32-wide: stages 1, 2, 4 in registers, 8 and 16 across the lane quad.
+    const int64_t col = ((int64_t)seg * 64 + lane) * B;   // first element of this lane's block
+    if (col >= C) continue;
+    const char* p = static_cast<const char*>(src) + ((int64_t)r * ld + col) * ES;
+    float x[B];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((signs >> (8 * sub + i)) & 1u) x[i] = -x[i];
-      fwht8_local(x);
+    for (int k = 0; k < LOADS; ++k) {
+      uint4 w = reinterpret_cast<const uint4*>(p)[k];
+      if constexpr (BF16) {
+        uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float p = dpp_xor1(x[i]);
-        x[i] = (sub & 1) ? p - x[i] : x[i] + p;
+        for (int j = 0; j < 4; ++j) {
+          const int e = 8 * k + 2 * j;   // element of u[j]'s low half
+          if constexpr (HAD)             // negate x_e, x_e+1 where the mask says so
+            u[j] ^= (((signs >> e) & 1u) << 15) | (((signs >> (e + 1)) & 1u) << 31);
+          x[e] = bf16_lo(u[j]);
+          x[e + 1] = bf16_hi(u[j]);
+        }
+      } else {
+        uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * k + j;
+          if constexpr (HAD) u[j] ^= ((signs >> e) & 1u) << 31;
+          x[e] = __uint_as_float(u[j]);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float p = dpp_xor2(x[i]);
-        x[i] = (sub & 2) ? p - x[i] : x[i] + p;
-      }
-      const float c = hadamard_norm();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = x[i] * c;
     }
+    if constexpr (HAD) fwht_block<B>(x);
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
-    m = fmaxf(m, dpp_xor1(m));
-    if constexpr (FMT == MX) m = fmaxf(m, dpp_xor2(m));
+    for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
     float rcp;
     const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
-    float v[8];
+    uint32_t w[B / 8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = x[i] * rcp;
-    uint32_t w;
-    if constexpr (RND == 0) {
-      w = e2m1_rtn_pack8(v);
-    } else {
-      uint32_t h[4];
-      sr_draws8(seed, (offset + (uint64_t)r * (uint64_t)C + (uint64_t)col) >> 3, h);
-      w = e2m1_sr_pack8(v, h);
+    for (int g = 0; g < B / 8; ++g) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * rcp;
+      if constexpr (RND == 0) {
+        w[g] = e2m1_rtn_pack8(v);
+      } else {
+        uint32_t h[4];
+        sr_draws8(seed, (offset + (uint64_t)r * (uint64_t)C + (uint64_t)col) / 8 + g, h);
+        w[g] = e2m1_sr_pack8(v, h);
+      }
     }
-    if (active) {
-      *reinterpret_cast<uint32_t*>(codes + (int64_t)r * (C / 2) + col / 2) = w;
-      if ((lane & (B / 8 - 1)) == 0) scales[(int64_t)r * (C / B) + col / B] = (uint8_t)sbyte;
-    }
+    uint8_t* dst = codes + (int64_t)r * (C / 2) + col / 2;
+    if constexpr (B == 16) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    scales[(int64_t)r * (C / B) + col / B] = (uint8_t)sbyte;
     if constexpr (MON) {
       float g = 0.0f, e = 0.0f;
-      noise8<FMT>(x, w, scale_value<FMT>(sbyte), sg, g, e);
+      const float bs = scale_value<FMT>(sbyte);
+#pragma unroll
+      for (int k = 0; k < B / 8; ++k) noise8<FMT>(x + 8 * k, w[k], bs, sg, g, e);
       ng += (double)g;
       ne += (double)e;
     }
@@ -538,7 +549,9 @@ uint32_t strided_grid(uint64_t ntasks) {
 
 template <int FMT, int RND, bool BF16, bool HAD>
 void launch_cols(const QuantArgs& a, hipStream_t s) {
-  const uint32_t spr = (uint32_t)((a.C + 511) / 512);
+  // A task is 64 blocks of one row (one block per lane).
+  const int64_t per_task = 64 * (FMT == NV ? 16 : 32);
+  const uint32_t spr = (uint32_t)((a.C + per_task - 1) / per_task);
   const uint32_t ntasks = (uint32_t)(a.R * spr);
   uint32_t grid = strided_grid(ntasks);
   if (a.noise) grid = noise_grid(k_quant_cols<FMT, RND, BF16, HAD, true>, grid);

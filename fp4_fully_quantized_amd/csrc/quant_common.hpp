@@ -51,6 +51,26 @@ __device__ __forceinline__ float hadamard_scale() {
   else return 0.25f;
 }
 
+// All butterfly stages and the normalisation on one B-block held by one
+// thread whose signs are already applied.
+template <int B>
+__device__ __forceinline__ void fwht_block(float x[B]) {
+#pragma unroll
+  for (int h = 1; h < B; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if ((i & h) == 0) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  const float c = hadamard_scale<B>();
+#pragma unroll
+  for (int i = 0; i < B; ++i) x[i] = x[i] * c;
+}
+
 // Signs, all butterfly stages and the normalisation on one B-block held by
 // one thread.
 template <int B>
