@@ -185,9 +185,12 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
   const uint32_t nwaves = gridDim.x * 4u;
   float sg = 1.0f;
+  __shared__ float rtab[128];   // NVFP4 element multipliers per scale byte
   if constexpr (FMT == NV) {
     sg = nv_tensor_scale(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
+    nv_rcp_table(rtab, sg);
+    __syncthreads();
   }
   for (uint32_t t = wave; t < ntasks; t += nwaves) {
     const uint32_t tu = __builtin_amdgcn_readfirstlane(t);
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
 #pragma unroll
     for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
     float rcp;
-    const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+    const uint32_t sbyte = block_scale_tab<FMT>(m, sg, rtab, rcp);
     uint32_t w[B / 8];
 #pragma unroll
     for (int g = 0; g < B / 8; ++g) {
@@ -292,9 +295,11 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
   __shared__ __attribute__((aligned(16))) uint8_t stage_s[TC * NB];
 
   float sg = 1.0f;
+  __shared__ float rtab[128];   // NVFP4 element multipliers (published by the tile load's barrier)
   if constexpr (FMT == NV) {
     sg = nv_tensor_scale(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = sg;
+    nv_rcp_table(rtab, sg);
   }
   double ng = 0.0, ne = 0.0;  // quantization noise, when asked for
   // One tile per workgroup; with the noise monitor (MON) a capped grid loops
@@ -308,19 +313,33 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
     const int64_t c0 = (int64_t)tc * TC;
     const int tid = threadIdx.x;
 
-    // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load.
+    // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load; only edge
+    //    tiles check bounds.
     constexpr int CPR = TC * ES / 16;
+    if (r0 + TR <= R && c0 + TC <= C) {
 #pragma unroll
-    for (int k = 0; k < TR * CPR / 256; ++k) {
-      const int idx = k * 256 + tid;
-      const int rr = idx / CPR;
-      const int cc = idx % CPR;
-      const int64_t col = c0 + cc * (16 / ES);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r0 + rr < R && col < C)
-        v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-      uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      for (int k = 0; k < TR * CPR / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int rr = idx / CPR;
+        const int cc = idx % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                                                        ((r0 + rr) * ld + c0 + cc * (16 / ES)) * ES);
+        uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < TR * CPR / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int rr = idx / CPR;
+        const int cc = idx % CPR;
+        const int64_t col = c0 + cc * (16 / ES);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r0 + rr < R && col < C)
+          v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
+        uint32_t* d = reinterpret_cast<uint32_t*>(&tile[rr * PITCH + cc * 16]);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      }
     }
     __syncthreads();
 
@@ -360,7 +379,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
 #pragma unroll
       for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
       float rcp;
-      const uint32_t sbyte = block_scale<FMT>(m, sg, rcp);
+      const uint32_t sbyte = block_scale_tab<FMT>(m, sg, rtab, rcp);
       uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
       float bg = 0.0f, be = 0.0f;
       const float bs = MON ? scale_value<FMT>(sbyte) : 0.0f;

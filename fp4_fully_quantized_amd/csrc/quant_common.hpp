@@ -26,6 +26,47 @@ __device__ __forceinline__ float nv_tensor_scale(float amax) {
   return amax < 0x1p-100f ? 1.0f : amax / 2688.0f;
 }
 
+// amax_b / 6 rounded to nearest even in FP32 (m >= 0, finite). From 2^-100
+// up, one multiply by RN(1/6) and one fma correction give exactly the IEEE
+// quotient: the residual m - 6 q0 is exact (an fma) and zero or a normal
+// number there, and the corrected quotient equals the correctly rounded one
+// for every such FP32 m (checked over all of them); below 2^-100 the division
+// itself. About a third of the division's instructions.
+__device__ __forceinline__ float div6(float m) {
+  if (m < 0x1p-100f) return m / 6.0f;
+  const float r6 = 0x1.555556p-3f;   // RN(1/6)
+  const float q0 = m * r6;
+  return __builtin_fmaf(__builtin_fmaf(-6.0f, q0, m), r6, q0);
+}
+
+// The element multipliers an NVFP4 tensor can use, r(b) = 1 / (E4M3(b) * s_g)
+// (0 when the product is 0), for the scale bytes b = 0 .. 127 (127, E4M3's
+// NaN, never occurs: the encoder saturates at 448), one IEEE division each,
+// written to an LDS table by the first 128 threads. The caller synchronizes
+// the workgroup before the table is read.
+__device__ __forceinline__ void nv_rcp_table(float* tab, float sg) {
+  const int t = threadIdx.x;
+  if (t < 128) {
+    const float d = e4m3_decode((uint32_t)t) * sg;
+    tab[t] = (d == 0.0f) ? 0.0f : 1.0f / d;
+  }
+}
+
+// Block scale of one block with amax m, the NVFP4 multiplier read from the
+// table above (MXFP4 ignores it). Equal to block_scale below.
+template <int FMT>
+__device__ __forceinline__ uint32_t block_scale_tab(float m, float sg, const float* tab, float& r) {
+  if constexpr (FMT == NV) {
+    const uint32_t byte = e4m3_encode(div6(m) / sg);
+    r = tab[byte];
+    return byte;
+  } else {
+    const int e = e8m0_exponent(m);
+    r = pow2_neg(e);
+    return (uint32_t)(e + 127);
+  }
+}
+
 // Block scale of one block with amax m. Returns the scale byte, sets the
 // element multiplier r.
 template <int FMT>

@@ -45,6 +45,9 @@ __device__ __forceinline__ void quant_dual_body(
   static_assert(T * SP + T * NB <= T * PITCH && (T * SP) % 16 == 0, "staging fits in the tile");
   uint8_t* const stage_c = tile;
   uint8_t* const stage_s = tile + T * SP;
+  // NVFP4 element multipliers of each orientation (the tile load's barrier
+  // publishes them).
+  __shared__ float rtab[FMT == NV ? 2 : 1][128];
 
   float sg_c = 1.0f, sg_r = 1.0f;
   if constexpr (FMT == NV) {
@@ -57,6 +60,8 @@ __device__ __forceinline__ void quant_dual_body(
       *tscale_r = sg_r;
       if (amax_copy) *amax_copy = ac;
     }
+    nv_rcp_table(rtab[0], sg_c);
+    nv_rcp_table(rtab[FMT == NV ? 1 : 0], sg_r);
   }
   double ngc = 0.0, nec = 0.0, ngr = 0.0, ner = 0.0;  // quantization noise, when asked for
   // One tile per workgroup; with the noise monitor (MON) a capped grid loops
@@ -70,20 +75,34 @@ __device__ __forceinline__ void quant_dual_body(
     const int64_t c0 = (int64_t)tc * T;
     const int tid = threadIdx.x;
 
-    // 1. tile load, 16 bytes per load.
+    // 1. tile load, 16 bytes per load; only edge tiles check bounds.
     constexpr int CPR = T * ES / 16;
+    if (r0 + T <= R && c0 + T <= C) {
 #pragma unroll
-    for (int k = 0; k < T * CPR / 256; ++k) {
-      const int idx = k * 256 + tid;
-      const int rr = idx / CPR;
-      const int cc = idx % CPR;
-      const int64_t col = c0 + cc * (16 / ES);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r0 + rr < R && col < C)
-        v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-      uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
-      d[0] = make_uint2(v.x, v.y);
-      d[1] = make_uint2(v.z, v.w);
+      for (int k = 0; k < T * CPR / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int rr = idx / CPR;
+        const int cc = idx % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                                                        ((r0 + rr) * ld + c0 + cc * (16 / ES)) * ES);
+        uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
+        d[0] = make_uint2(v.x, v.y);
+        d[1] = make_uint2(v.z, v.w);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < T * CPR / 256; ++k) {
+        const int idx = k * 256 + tid;
+        const int rr = idx / CPR;
+        const int cc = idx % CPR;
+        const int64_t col = c0 + cc * (16 / ES);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r0 + rr < R && col < C)
+          v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
+        uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
+        d[0] = make_uint2(v.x, v.y);
+        d[1] = make_uint2(v.z, v.w);
+      }
     }
     __syncthreads();
 
@@ -119,7 +138,7 @@ __device__ __forceinline__ void quant_dual_body(
 #pragma unroll
         for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(x[i]));
         float rcp;
-        sb[bb] = block_scale<FMT>(m, sg_c, rcp);
+        sb[bb] = block_scale_tab<FMT>(m, sg_c, rtab[0], rcp);
         const int64_t col0 = c0 + half * 64 + bb * B;
         float bg = 0.0f, be = 0.0f;
         const float bs = (MON && noise_c) ? scale_value<FMT>(sb[bb]) : 0.0f;
@@ -196,7 +215,7 @@ __device__ __forceinline__ void quant_dual_body(
 #pragma unroll
         for (int i = 0; i < B; ++i) m = fmaxf(m, fabsf(xk[i]));
         float rcp;
-        const uint32_t sbyte = block_scale<FMT>(m, sg_r, rcp);
+        const uint32_t sbyte = block_scale_tab<FMT>(m, sg_r, rtab[FMT == NV ? 1 : 0], rcp);
         uint32_t* sc = reinterpret_cast<uint32_t*>(&stage_c[cl * SP + b * (B / 2)]);
         float bg = 0.0f, be = 0.0f;
         const float bs = (MON && noise_r) ? scale_value<FMT>(sbyte) : 0.0f;
