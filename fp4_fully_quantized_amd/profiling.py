@@ -110,7 +110,7 @@ GROUPS = [
     ("quantize, both orientations from one read", r"^k_quant_dual(_w3)?<"),
     ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
     ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
-    ("tensor amax", r"^k_amax<"),
+    ("tensor amax", r"^k_amax(_flat)?<"),
     ("tensor amax of the values rotated down the columns", r"^k_amax_rot_rows<"),
     ("both orientations' amaxes, one rotated (one read)", r"^k_amax_pair<"),
     ("2-D block quantize (both orientations)", r"^k_quant_2d<"),
@@ -148,12 +148,12 @@ _DUAL = 2 + 2 * (0.5 + 1 / 16)      # bf16 read + two orientations of codes and 
 _MX = 2 + 0.5 + 1 / 32
 _GF = 2.0 * TOKENS * D_IN * D_OUT
 STEP_DISPATCHES = [
-    ("amax X", r"^k_amax<", 2 * _NX, _NX),
+    ("amax X", r"^k_amax(_flat)?<", 2 * _NX, _NX),
     ("dual X (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NX, 2 * _NX),
-    ("amax W", r"^k_amax<", 2 * _NW, _NW),
+    ("amax W", r"^k_amax(_flat)?<", 2 * _NW, _NW),
     ("dual W (RTN along K, SR along out)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NW, 2 * _NW),
     ("NVFP4 GEMM fwd (bf16 out)", r"^k_gemm<0, 256, true>", _GF, 0),
-    ("amax dY", r"^k_amax<", 2 * _NY, _NY),
+    ("amax dY", r"^k_amax(_flat)?<", 2 * _NY, _NY),
     ("dual dY (SR both)", r"^k_quant_dual<0, 1, 1,", _DUAL * _NY, 2 * _NY),
     ("NVFP4 GEMM dgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
     ("NVFP4 GEMM wgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
@@ -167,9 +167,9 @@ EXTRA_DISPATCHES = [
     ("dual X, 16-wide rotation along tokens", r"^k_quant_dual<0, 0, 1, true, false, true,", _DUAL * _NX, 2 * _NX),
     ("amax pair dY (plain, rotated along tokens)", r"^k_amax_pair<", 2 * _NY, _NY),
     ("dual dY, 16-wide rotation along tokens", r"^k_quant_dual<0, 1, 1, true, false, true,", _DUAL * _NY, 2 * _NY),
-    ("amax W (2-D)", r"^k_amax<", 2 * _NW, _NW),
+    ("amax W (2-D)", r"^k_amax(_flat)?<", 2 * _NW, _NW),
     ("2-D 16x16 W", r"^k_quant_2d<", _DUAL * _NW, 2 * _NW),
-    ("amax dY (monitored)", r"^k_amax<", 2 * _NY, _NY),
+    ("amax dY (monitored)", r"^k_amax(_flat)?<", 2 * _NY, _NY),
     ("dual dY + noise monitor", r"^k_quant_dual_w3<0, 1, 1, true, false, false, true>", _DUAL * _NY, 2 * _NY),
 ]
 
@@ -252,7 +252,7 @@ def _stats_lines(groups):
 # The large layer's step in launch order (bench.py make_large_step).
 L_TOKENS, L_IN, L_OUT = 16384, 8192, 28672
 LARGE_GROUPS = [
-    ("tensor amax (X, W, dY)", r"^k_amax<"),
+    ("tensor amax (X, W, dY)", r"^k_amax(_flat)?<"),
     ("quantize X, both orientations (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,"),
     ("quantize dY, both orientations (SR)", r"^k_quant_dual<0, 1, 1,"),
     ("NVFP4 GEMM fwd 16384x28672x8192 (bf16 out)", r"^k_gemm<0, 256, true>"),
