@@ -63,6 +63,14 @@ def algorithmic_bytes(n_elem: int, src_bytes: int, block: int, amax_pass: bool, 
     return b
 
 
+def gemm_workspace(fp4, A, B):
+    """The split-K area of this product (allocated once, before the timed
+    steps), or None when the shape never splits."""
+    import torch
+    n = fp4.fp4_gemm_workspace_bytes(A, B) + fp4.fp4_gemm_splitk_bytes(A, B)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+
 def make_step(fp4, X, W, dY, signs, separate=False):
     import torch
 
@@ -86,13 +94,15 @@ def make_step(fp4, X, W, dY, signs, separate=False):
     q["Xt"].amax = q["X"].amax
     COLS, ROWS, RTN, SR = fp4.FP4_AXIS_COLS, fp4.FP4_AXIS_ROWS, fp4.FP4_RTN, fp4.FP4_SR
     seed = lambda role: (2 << 8) | role
+    ws = {"fwd": gemm_workspace(fp4, q["X"], q["W"]), "dgrad": gemm_workspace(fp4, q["dY"], q["Wt"]),
+          "wgrad": gemm_workspace(fp4, q["dYt"], q["Xt"]), "mx": gemm_workspace(fp4, q["mX"], q["mW"])}
 
     mx_ops = [
         ("quant X mx had", "q", lambda: fp4.fp4_quantize(X, COLS, RTN, 0, 0, False, q["mX"]),
          algorithmic_bytes(TOKENS * D_IN, 2, 32, False)),
         ("quant W mx had", "q", lambda: fp4.fp4_quantize(W, COLS, RTN, 0, 0, False, q["mW"]),
          algorithmic_bytes(D_OUT * D_IN, 2, 32, False)),
-        ("gemm fwd mx", "g_mx", lambda: fp4.fp4_gemm(q["mX"], q["mW"], outs["Ymx"]), GEMM_FLOP),
+        ("gemm fwd mx", "g_mx", lambda: fp4.fp4_gemm(q["mX"], q["mW"], outs["Ymx"], ws["mx"]), GEMM_FLOP),
     ]
     if not separate:
         dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
@@ -103,12 +113,12 @@ def make_step(fp4, X, W, dY, signs, separate=False):
             ("quant W nv dual (rtn K, sr out)", "q",
              lambda: dual(W, RTN, 0, SR, seed(4), q["W"], q["Wt"]),
              algorithmic_bytes(D_OUT * D_IN, 2, 16, True, 2)),
-            ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"]), GEMM_FLOP),
+            ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"], ws["fwd"]), GEMM_FLOP),
             ("quant dY nv dual (sr both)", "q",
              lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
              algorithmic_bytes(TOKENS * D_OUT, 2, 16, True, 2)),
-            ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"]), GEMM_FLOP),
-            ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), GEMM_FLOP),
+            ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"], ws["dgrad"]), GEMM_FLOP),
+            ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"], ws["wgrad"]), GEMM_FLOP),
         ] + mx_ops
         return ops, outs, q
 
@@ -118,17 +128,17 @@ def make_step(fp4, X, W, dY, signs, separate=False):
          algorithmic_bytes(TOKENS * D_IN, 2, 16, True)),
         ("quant W nv rtn", "q", lambda: fp4.fp4_quantize(W, COLS, RTN, 0, 0, False, q["W"]),
          algorithmic_bytes(D_OUT * D_IN, 2, 16, True)),
-        ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"]), GEMM_FLOP),
+        ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"], ws["fwd"]), GEMM_FLOP),
         ("quant dY nv sr", "q", lambda: fp4.fp4_quantize(dY, COLS, SR, seed(1), 0, False, q["dY"]),
          algorithmic_bytes(TOKENS * D_OUT, 2, 16, True)),
         ("quant W^T nv sr", "q", lambda: fp4.fp4_quantize(W, ROWS, SR, seed(4), 0, True, q["Wt"]),
          algorithmic_bytes(D_OUT * D_IN, 2, 16, False)),
-        ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"]), GEMM_FLOP),
+        ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"], ws["dgrad"]), GEMM_FLOP),
         ("quant dY^T nv sr", "q", lambda: fp4.fp4_quantize(dY, ROWS, SR, seed(2), 0, True, q["dYt"]),
          algorithmic_bytes(TOKENS * D_OUT, 2, 16, False)),
         ("quant X^T nv sr", "q", lambda: fp4.fp4_quantize(X, ROWS, SR, seed(3), 0, True, q["Xt"]),
          algorithmic_bytes(TOKENS * D_IN, 2, 16, False)),
-        ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), GEMM_FLOP),
+        ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"], ws["wgrad"]), GEMM_FLOP),
     ] + mx_ops
     return ops, outs, q
 

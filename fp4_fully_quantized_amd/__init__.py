@@ -27,7 +27,8 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
            "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_noise_ratio", "fp4_quantize_2d",
-           "fp4_dequantize", "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_gemm_noalloc"]
+           "fp4_dequantize", "fp4_gemm_workspace_bytes", "fp4_gemm_splitk_bytes", "fp4_gemm",
+           "fp4_gemm_noalloc"]
 # The allocation-free GEMM's workspace limit (FP4_GEMM_NOALLOC_MAX_BYTES).
 FP4_GEMM_NOALLOC_MAX_BYTES = 128 << 20
 
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.fp4_noise_ratio.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p]
         L.fp4_gemm_workspace_bytes.restype = c.c_size_t
         L.fp4_gemm_workspace_bytes.argtypes = [c.POINTER(fp4_operand), c.POINTER(fp4_operand)]
+        L.fp4_gemm_splitk_bytes.restype = c.c_size_t
+        L.fp4_gemm_splitk_bytes.argtypes = [c.POINTER(fp4_operand), c.POINTER(fp4_operand)]
         L.fp4_gemm.restype = c.c_int
         L.fp4_gemm.argtypes = [c.POINTER(fp4_operand), c.POINTER(fp4_operand), c.c_int, c.c_void_p,
                                c.c_int64, c.c_void_p, c.c_size_t, c.c_void_p]
@@ -448,10 +451,17 @@ def fp4_gemm_workspace_bytes(A, B) -> int:
     return lib().fp4_gemm_workspace_bytes(ctypes.byref(oa), ctypes.byref(ob))
 
 
+def fp4_gemm_splitk_bytes(A, B) -> int:
+    oa, ka = _operand(A, "A")
+    ob, kb = _operand(B, "B")
+    return lib().fp4_gemm_splitk_bytes(ctypes.byref(oa), ctypes.byref(ob))
+
+
 def fp4_gemm(A, B, C, ws=None, stream=None) -> None:
     """C = A_hat B_hat^T (FP32 accumulation). A and B are QTensors blocked
     along K or RawOperands (quantized into `ws`, a uint8 device tensor of at
-    least fp4_gemm_workspace_bytes(A, B) bytes)."""
+    least fp4_gemm_workspace_bytes(A, B) bytes; with fp4_gemm_splitk_bytes(A, B)
+    more, the last partial wave of output tiles is split along K)."""
     import torch
     dev = _operand_device(A)
     if _operand_device(B) != dev:
@@ -548,14 +558,14 @@ def dequantize(q: QTensor, dtype=None, stream=None):
 
 
 def gemm(A, B, dtype=None, out=None, ws=None, stream=None):
-    """Allocate the output (and, for RawOperands, the workspace when none is
-    given) and run fp4_gemm."""
+    """Allocate the output (and, when none is given, the workspace: the RAW
+    operands' and the split-K area) and run fp4_gemm."""
     import torch
     dev = _operand_device(A)
     if out is None:
         out = torch.empty((A.rows, B.rows), dtype=dtype or torch.float32, device=dev)
     if ws is None:
-        n = fp4_gemm_workspace_bytes(A, B)
+        n = fp4_gemm_workspace_bytes(A, B) + fp4_gemm_splitk_bytes(A, B)
         if n:
             ws = torch.empty(n, dtype=torch.uint8, device=dev)
     fp4_gemm(A, B, out, ws, stream)

@@ -220,7 +220,7 @@ fp4_status check_gemm_pair(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype o
 }
 
 void launch_gemm_pair(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t, void* C, int64_t ldc,
-                      hipStream_t s) {
+                      float* split_ws, hipStream_t s) {
   GemmArgs g;
   g.a_codes = A->codes;
   g.a_scales = A->scales;
@@ -235,6 +235,7 @@ void launch_gemm_pair(const fp4_tensor* A, const fp4_tensor* B, fp4_dtype out_t,
   g.bf16out = out_t == FP4_DTYPE_BF16;
   g.c = C;
   g.ldc = ldc;
+  g.split_ws = split_ws;
   fp4i_launch_gemm(g, s);
 }
 
@@ -316,9 +317,18 @@ fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64
   return hip_status();
 }
 
-// The product, with RAW operands quantized into ws first.
+// Bytes of the optional split-K area (after the RAW pieces) for a valid pair.
+size_t splitk_bytes(const OperandView& va, const OperandView& vb) {
+  if (va.fmt != vb.fmt || va.k != vb.k || va.k <= 0 || va.k % 128 != 0) return 0;
+  if (!fp4i_gemm_fits(va.rows, vb.rows, va.k)) return 0;
+  return round_up(fp4i_gemm_split_bytes(va.rows, vb.rows, va.k));
+}
+
+// The product, with RAW operands quantized into ws first; with allow_split and
+// room in ws after the RAW pieces, the last partial wave of output tiles is
+// split along K.
 fp4_status gemm_impl(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C, int64_t ldc,
-                     void* ws, size_t ws_bytes, fp4_stream_t stream) {
+                     void* ws, size_t ws_bytes, bool allow_split, fp4_stream_t stream) {
   if (!C) return FP4_ERR_NULL;
   OperandView va, vb;
   fp4_status st = view_operand(A, &va);
@@ -352,7 +362,11 @@ fp4_status gemm_impl(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t
                       op->seed, op->index_offset, 0, &v->q, nullptr, s);
     if (st != FP4_OK) return st;
   }
-  launch_gemm_pair(&va.q, &vb.q, out_t, C, ldc, s);
+  float* split_ws = nullptr;
+  const size_t opt = allow_split ? splitk_bytes(va, vb) : 0;
+  if (opt > 0 && ws && (reinterpret_cast<uintptr_t>(ws) % kWsAlign) == 0 && ws_bytes >= need + opt)
+    split_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + need);
+  launch_gemm_pair(&va.q, &vb.q, out_t, C, ldc, split_ws, s);
   return hip_status();
 }
 
@@ -556,9 +570,15 @@ size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B) {
   return va.ws_bytes + vb.ws_bytes;
 }
 
+size_t fp4_gemm_splitk_bytes(const fp4_operand* A, const fp4_operand* B) {
+  OperandView va, vb;
+  if (view_operand(A, &va) != FP4_OK || view_operand(B, &vb) != FP4_OK) return 0;
+  return splitk_bytes(va, vb);
+}
+
 fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
                     int64_t ldc, void* ws, size_t ws_bytes, fp4_stream_t stream) {
-  return gemm_impl(A, B, out_t, C, ldc, ws, ws_bytes, stream);
+  return gemm_impl(A, B, out_t, C, ldc, ws, ws_bytes, true, stream);
 }
 
 fp4_status fp4_gemm_noalloc(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
@@ -576,7 +596,7 @@ fp4_status fp4_gemm_noalloc(const fp4_operand* A, const fp4_operand* B, fp4_dtyp
     st = scratch_on_current_device(&ws);
     if (st != FP4_OK) return st;
   }
-  return gemm_impl(A, B, out_t, C, ldc, ws, need > 0 ? FP4_GEMM_NOALLOC_MAX_BYTES : 0, stream);
+  return gemm_impl(A, B, out_t, C, ldc, ws, need > 0 ? FP4_GEMM_NOALLOC_MAX_BYTES : 0, false, stream);
 }
 
 fp4_status fp4_noise_ratio(const double* noise, double* ratio, fp4_stream_t stream) {

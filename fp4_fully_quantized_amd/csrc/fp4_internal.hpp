@@ -67,6 +67,10 @@ struct GemmArgs {
   bool bf16out;
   void* c;
   int64_t ldc;
+  // Optional FP32 area of at least fp4i_gemm_split_bytes(M, N, K) bytes, or
+  // null: with it, the output tiles of the last partial wave are split along
+  // K and their partial sums added by a second kernel.
+  float* split_ws;
 };
 
 void fp4i_launch_amax(const void* src, bool bf16, int64_t R, int64_t C, int64_t ld, float* amax,
@@ -89,6 +93,8 @@ void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const floa
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);
 bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K);
+// Bytes of the split-K area the GEMM of this shape can use (0: it never splits).
+size_t fp4i_gemm_split_bytes(int64_t M, int64_t N, int64_t K);
 // *ratio = sqrt(noise[0] / noise[1]) on the device (the gradient-noise monitor's statistic).
 void fp4i_launch_noise_ratio(const double* noise, double* ratio, hipStream_t s);
 void fp4i_launch_gemm(const GemmArgs& g, hipStream_t s);

@@ -42,6 +42,9 @@
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 
+#include <algorithm>
+#include <type_traits>
+
 using namespace fp4dev;
 
 namespace {
@@ -82,6 +85,20 @@ __device__ __forceinline__ v16f mfma_mx_sel(int s, const v8i& a, const v8i& b, c
                 : mfma_mx<3>(a, b, c, sa, sb);
 }
 
+// Output tile t (in the grouped order) -> tile row and column: groups of
+// group_m tile rows, column-major inside a group, so that the workgroups one
+// XCD runs at a time share A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(uint32_t t, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
+                                            uint32_t& tm, uint32_t& tn) {
+  const uint32_t per_group = group_m * tiles_n;
+  const uint32_t grp = t / per_group;
+  const uint32_t first_m = grp * group_m;
+  const uint32_t gsize = min(group_m, tiles_m - first_m);
+  const uint32_t in_grp = t - grp * per_group;
+  tm = first_m + in_grp % gsize;
+  tn = in_grp / gsize;
+}
+
 template <int FMT, int BK>
 struct Cfg {
   static constexpr int ROWB = BK / 2;               // code bytes per row per K tile
@@ -116,12 +133,16 @@ __device__ __forceinline__ uint4 permute_scales(uint4 v) {
   }
 }
 
-template <int FMT, int BK, bool BF16OUT>
+// SPLIT = false: whole output tiles 0 .. nfull-1. SPLIT = true: the pieces of
+// the split tiles nfull .. nfull+ntail-1, each a range of K, whose FP32
+// partial tiles go to `part` (added by k_split_reduce).
+template <int FMT, int BK, bool BF16OUT, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                                   const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
                                                   const float* __restrict__ a_ts, const float* __restrict__ b_ts,
                                                   uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_m,
-                                                  uint32_t tiles_n, uint32_t per_xcd, uint32_t group_m,
+                                                  uint32_t tiles_n, uint32_t group_m, uint32_t nfull,
+                                                  uint32_t ntail, uint32_t split, float* __restrict__ part,
                                                   void* __restrict__ cout, int64_t ldc, uint32_t vec_ok) {
   using C = Cfg<FMT, BK>;
   // One LDS array: the double-buffered code and scale tiles of the K loop,
@@ -130,17 +151,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   uint8_t (*lds_c)[C::LDS_CODES] = reinterpret_cast<uint8_t (*)[C::LDS_CODES]>(lds);
   uint8_t (*lds_s)[C::LDS_SCALES] = reinterpret_cast<uint8_t (*)[C::LDS_SCALES]>(lds + 2 * C::LDS_CODES);
 
-  // ---- tile of this workgroup
-  const uint32_t xcd = blockIdx.x % NXCD;
-  const uint32_t t = xcd * per_xcd + blockIdx.x / NXCD;
-  if (t >= tiles_m * tiles_n) return;
-  const uint32_t per_group = group_m * tiles_n;
-  const uint32_t grp = t / per_group;
-  const uint32_t first_m = grp * group_m;
-  const uint32_t gsize = min(group_m, tiles_m - first_m);
-  const uint32_t in_grp = t - grp * per_group;
-  const uint32_t tm = first_m + in_grp % gsize;
-  const uint32_t tn = in_grp / gsize;
+  // ---- work of this workgroup. Dispatch goes round robin over the 8 XCDs
+  // and the grid (of each split piece) is a multiple of 8 workgroups, so each
+  // XCD takes one contiguous range of the tiles.
+  const int nk_all = (int)(K / BK);
+  uint32_t t, tt = 0, sidx = 0;
+  int kb = 0, nk = nk_all;
+  if constexpr (!SPLIT) {
+    const uint32_t gfull = (nfull + NXCD - 1) / NXCD * NXCD;
+    t = (blockIdx.x % NXCD) * (gfull / NXCD) + blockIdx.x / NXCD;
+    if (t >= nfull) return;
+  } else {
+    const uint32_t gtail = (ntail + NXCD - 1) / NXCD * NXCD;
+    const uint32_t u = blockIdx.x;
+    sidx = u / gtail;
+    const uint32_t v = u - sidx * gtail;
+    tt = (v % NXCD) * (gtail / NXCD) + v / NXCD;
+    if (tt >= ntail) return;
+    t = nfull + tt;
+    kb = (int)(sidx * (uint32_t)nk_all / split);
+    nk = (int)((sidx + 1) * (uint32_t)nk_all / split) - kb;
+  }
+  uint32_t tm, tn;
+  tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -149,7 +182,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t kb_row = K / 2;
   const uint32_t ks_row = K / C::SB;
-  const int nk = (int)(K / BK);
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(ac, M * kb_row);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(bc, N * kb_row);
@@ -169,13 +201,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   uint4 creg[C::CODE_LOADS];
   uint4 sreg[2];
   // Staging of one K tile: code load j (16 bytes) and the two scale rows.
+  // kt counts the K tiles of this workgroup's range (from kb).
   auto gload_code = [&](int j, int kt) {
-    const uint32_t kc = (uint32_t)kt * C::ROWB;
+    const uint32_t kc = (uint32_t)(kb + kt) * C::ROWB;
     if (j < JA) creg[j] = bload16(ra, goff_a + (uint32_t)(j * C::RPL) * kb_row + kc);
     else creg[j] = bload16(rb, goff_b + (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
   };
   auto gload_scales = [&](int kt) {
-    const uint32_t ks = (uint32_t)kt * C::SCB;
+    const uint32_t ks = (uint32_t)(kb + kt) * C::SCB;
     if constexpr (C::SCB == 16) {
       sreg[0] = bload16(rsa, soff_a + ks);
       sreg[1] = bload16(rsb, soff_b + ks);
@@ -433,107 +466,247 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
     }
   }
 
-  float alpha = 1.0f;
-  if constexpr (FMT == NV) alpha = (*a_ts) * (*b_ts);
-
   // Epilogue. The MFMAs take the B fragment as their first operand, so the
   // accumulator of fragments (i, j) is the transposed product: lane l holds
   // output row i*32 + l%32 (of the wave's 128 rows) and columns j*32 + 8*(r/4)
   // + 4*(l/32) + r%4, r = 0..15: four consecutive columns of one row per group
-  // of four r. bf16 outputs are rounded to nearest even.
-  constexpr int ES = BF16OUT ? 2 : 4;  // output element bytes
-  const uint32_t row0 = m0 + wm * WM;  // first output row / column of this wave
-  const uint32_t col0 = n0 + wn * WN;
-  auto out_at = [&](uint32_t row, uint32_t col) {
-    return static_cast<uint8_t*>(cout) + ((int64_t)row * ldc + col) * ES;
-  };
-  if (vec_ok && m0 + BM <= M && n0 + BN <= N) {
-    // Interior tile: staged through LDS, 32 rows of the wave at a time, so
-    // that every store instruction writes whole rows in 16-byte pieces
-    // (non-temporal: the output is not read again by this kernel). The row
-    // pitch of 132 outputs (4 of padding) keeps the LDS writes and reads free
-    // of bank conflicts.
-    constexpr int PITCH = 132 * ES;
-    static_assert(4 * 32 * PITCH <= 2 * (C::LDS_CODES + C::LDS_SCALES), "output staging exceeds the LDS tiles");
-    __syncthreads();  // every wave is done with the K loop's LDS tiles
-    uint8_t* stage = lds + wave * 32 * PITCH;
+  // of four r. bf16 outputs are rounded to nearest even. `out` is the output
+  // (or the FP32 partial tile), `rows`/`cols` the bounds of its valid part.
+  auto epilogue = [&](auto bf16_tag, uint8_t* out, int64_t ld, uint32_t r0, uint32_t c0, uint32_t rows,
+                      uint32_t cols, float alpha, bool interior) {
+    constexpr bool OBF = decltype(bf16_tag)::value;
+    constexpr int ES = OBF ? 2 : 4;  // output element bytes
+    const uint32_t row0 = r0 + wm * WM;  // first output row / column of this wave
+    const uint32_t col0 = c0 + wn * WN;
+    auto out_at = [&](uint32_t row, uint32_t col) { return out + ((int64_t)row * ld + col) * ES; };
+    if (interior) {
+      // Interior tile: staged through LDS, 32 rows of the wave at a time, so
+      // that every store instruction writes whole rows in 16-byte pieces
+      // (non-temporal: the output is not read again by this kernel). The row
+      // pitch of 132 outputs (4 of padding) keeps the LDS writes and reads free
+      // of bank conflicts.
+      constexpr int PITCH = 132 * ES;
+      static_assert(4 * 32 * PITCH <= 2 * (C::LDS_CODES + C::LDS_SCALES), "output staging exceeds the LDS tiles");
+      __syncthreads();  // every wave is done with the K loop's LDS tiles
+      uint8_t* stage = lds + wave * 32 * PITCH;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v4f y = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if constexpr (FMT == NV) y = y * alpha;
-          uint8_t* d = stage + lr * PITCH + (j * 32 + 8 * q + 4 * g) * ES;
-          if constexpr (BF16OUT) {
-            const v2bf lo = __builtin_convertvector((v2f){y[0], y[1]}, v2bf);
-            const v2bf hi = __builtin_convertvector((v2f){y[2], y[3]}, v2bf);
-            *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-          } else {
-            *reinterpret_cast<v4f*>(d) = y;
+          for (int q = 0; q < 4; ++q) {
+            v4f y = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (FMT == NV) y = y * alpha;
+            uint8_t* d = stage + lr * PITCH + (j * 32 + 8 * q + 4 * g) * ES;
+            if constexpr (OBF) {
+              const v2bf lo = __builtin_convertvector((v2f){y[0], y[1]}, v2bf);
+              const v2bf hi = __builtin_convertvector((v2f){y[2], y[3]}, v2bf);
+              *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+            } else {
+              *reinterpret_cast<v4f*>(d) = y;
+            }
+          }
+        }
+        // Read back 16 bytes per lane: a row of 128 outputs is 128 * ES / 16 lanes.
+        constexpr int LPR = 128 * ES / 16;  // lanes per row
+        constexpr int RPS = 64 / LPR;       // rows per store instruction
+#pragma unroll
+        for (int k = 0; k < 32 / RPS; ++k) {
+          const int rr = k * RPS + lane / LPR;
+          const int cc = (lane % LPR) * (16 / ES);
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH + cc * ES);
+          __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t row = row0 + i * 32 + lr;
+        if (row >= rows) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t col = col0 + j * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (col >= cols) continue;
+            float y = acc[i][j][r];
+            if constexpr (FMT == NV) y = y * alpha;
+            if constexpr (OBF) {
+              const v2bf b = __builtin_convertvector((v2f){y, y}, v2bf);
+              *reinterpret_cast<uint16_t*>(out_at(row, col)) = __builtin_bit_cast(uint16_t, b[0]);
+            } else {
+              *reinterpret_cast<float*>(out_at(row, col)) = y;
+            }
           }
         }
       }
-      // Read back 16 bytes per lane: a row of 128 outputs is 128 * ES / 16 lanes.
-      constexpr int LPR = 128 * ES / 16;  // lanes per row
-      constexpr int RPS = 64 / LPR;       // rows per store instruction
-#pragma unroll
-      for (int k = 0; k < 32 / RPS; ++k) {
-        const int rr = k * RPS + lane / LPR;
-        const int cc = (lane % LPR) * (16 / ES);
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH + cc * ES);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
-      }
     }
+  };
+  if constexpr (SPLIT) {
+    // FP32 partial tile, row-major 256 x 256, unscaled (the reduction applies alpha).
+    float* P = part + ((size_t)tt * split + sidx) * (BM * BN);
+    epilogue(std::integral_constant<bool, false>{}, reinterpret_cast<uint8_t*>(P), BN, 0, 0, BM, BN, 1.0f, true);
   } else {
+    float alpha = 1.0f;
+    if constexpr (FMT == NV) alpha = (*a_ts) * (*b_ts);
+    epilogue(std::integral_constant<bool, BF16OUT>{}, static_cast<uint8_t*>(cout), ldc, m0, n0, M, N, alpha,
+             vec_ok && m0 + BM <= M && n0 + BN <= N);
+  }
+}
+
+// Sum of the `split` FP32 partial tiles of each split output tile, in split
+// order, times alpha (NVFP4: s_gA * s_gB), converted and stored. Workgroup
+// (tile tt, 32-row slab): lane c of a row holds its columns 4c .. 4c+3, so
+// every load and store instruction covers whole 1 KB partial rows.
+template <int FMT, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, uint32_t nfull,
+                                                      uint32_t split, uint32_t tiles_m, uint32_t tiles_n,
+                                                      uint32_t group_m, const float* __restrict__ a_ts,
+                                                      const float* __restrict__ b_ts, uint32_t M, uint32_t N,
+                                                      void* __restrict__ cout, int64_t ldc, uint32_t vec_ok) {
+  const uint32_t tt = blockIdx.x / (BM / 32);
+  const uint32_t slab = blockIdx.x % (BM / 32);
+  uint32_t tm, tn;
+  tile_coords(nfull + tt, tiles_m, tiles_n, group_m, tm, tn);
+  float alpha = 1.0f;
+  if constexpr (FMT == NV) alpha = (*a_ts) * (*b_ts);
+  const int c4 = threadIdx.x % 64;
+  const uint32_t col = tn * BN + 4 * c4;
+  const float* P = part + (size_t)tt * split * (BM * BN);
+  constexpr int ES = BF16OUT ? 2 : 4;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const uint32_t row = row0 + i * 32 + lr;
-      if (row >= M) continue;
+  for (int k = 0; k < 8; ++k) {
+    const int r = (int)slab * 32 + k * 4 + (int)threadIdx.x / 64;
+    const uint32_t row = tm * BM + r;
+    v4f y = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(P + r * BN + 4 * c4));
+    for (uint32_t sp = 1; sp < split; ++sp)
+      y += __builtin_nontemporal_load(reinterpret_cast<const v4f*>(P + (size_t)sp * (BM * BN) + r * BN + 4 * c4));
+    if constexpr (FMT == NV) y = y * alpha;
+    if (row >= M) continue;
+    uint8_t* d = static_cast<uint8_t*>(cout) + ((int64_t)row * ldc + col) * ES;
+    if (vec_ok && col + 4 <= N) {
+      if constexpr (BF16OUT) {
+        const v2bf lo = __builtin_convertvector((v2f){y[0], y[1]}, v2bf);
+        const v2bf hi = __builtin_convertvector((v2f){y[2], y[3]}, v2bf);
+        *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      } else {
+        *reinterpret_cast<v4f*>(d) = y;
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t col = col0 + j * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (col >= N) continue;
-          float y = acc[i][j][r];
-          if constexpr (FMT == NV) y = y * alpha;
-          if constexpr (BF16OUT) {
-            const v2bf b = __builtin_convertvector((v2f){y, y}, v2bf);
-            *reinterpret_cast<uint16_t*>(out_at(row, col)) = __builtin_bit_cast(uint16_t, b[0]);
-          } else {
-            *reinterpret_cast<float*>(out_at(row, col)) = y;
-          }
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= N) break;
+        if constexpr (BF16OUT) {
+          const v2bf b = __builtin_convertvector((v2f){y[e], y[e]}, v2bf);
+          *reinterpret_cast<uint16_t*>(d + e * ES) = __builtin_bit_cast(uint16_t, b[0]);
+        } else {
+          *reinterpret_cast<float*>(d + e * ES) = y[e];
         }
       }
     }
   }
 }
 
+// How the output tiles are cut: tiles whole, and the tiles of the last,
+// partial wave (one workgroup per CU: the LDS tiles take most of a CU's LDS)
+// split along K when that shortens the wave enough to pay for the partial
+// sums. The chip is power-limited under this load: with all 256 CUs busy it
+// holds about 1.7 GHz, with fewer the clock rises towards 2.4 GHz, so a wave
+// of n tiles takes max(n / 256, 1.7 / 2.4) of a full wave's time (the
+// Llama-7B wgrad's last wave of 176 tiles runs nearly as fast as a split of
+// it would, measured). Splitting in S pieces costs writing and re-reading
+// S + 1 tiles of FP32 per split tile (at about 5 TB/s) and a second launch,
+// against a tile time of about 2 us per 256-deep K tile (the faster, MXFP4,
+// kernel). kPlanCUs is the CU count of the gfx950 parts (MI350X, MI355X).
+constexpr uint32_t kPlanCUs = 256;
+struct SplitPlan {
+  uint32_t tiles_m, tiles_n, nfull, ntail, split;
+};
+double wave_time(uint32_t n) { return std::max((double)n / kPlanCUs, 1.7 / 2.4); }
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p;
+  p.tiles_m = (uint32_t)((M + BM - 1) / BM);
+  p.tiles_n = (uint32_t)((N + BN - 1) / BN);
+  const uint32_t tiles = p.tiles_m * p.tiles_n;
+  p.nfull = tiles;
+  p.ntail = 0;
+  p.split = 1;
+  const int bk = K % 256 == 0 ? 256 : 128;
+  const int64_t nk = K / bk;
+  const uint32_t tail = tiles % kPlanCUs;
+  if (tail == 0) return p;
+  const double tile_us = (double)nk * 2.0 * bk / 256;
+  double best = wave_time(tail);
+  for (uint32_t sp = 2; sp <= 8 && nk / sp >= 8; ++sp) {
+    const uint32_t units = tail * sp;
+    const uint32_t waves = (units + kPlanCUs - 1) / kPlanCUs;
+    const double t = ((waves - 1) + wave_time(units - (waves - 1) * kPlanCUs)) / sp;
+    const double extra_us = (double)(sp + 1) * tail * (BM * BN * 4) / 5e6 + 5.0;
+    const double cost = t + extra_us / tile_us + 0.005 * sp;
+    if (cost < best) {
+      best = cost;
+      p.split = sp;
+    }
+  }
+  if (p.split > 1) {
+    p.ntail = tail;
+    p.nfull = tiles - tail;
+  }
+  return p;
+}
+
 template <int FMT, int BK>
 void launch(const GemmArgs& g, hipStream_t s) {
-  const uint32_t tiles_m = (uint32_t)((g.M + BM - 1) / BM);
-  const uint32_t tiles_n = (uint32_t)((g.N + BN - 1) / BN);
-  const uint32_t tiles = tiles_m * tiles_n;
-  const uint32_t per_xcd = (tiles + NXCD - 1) / NXCD;
+  SplitPlan p = split_plan(g.M, g.N, g.K);
+  if (!g.split_ws) {
+    p.nfull += p.ntail;
+    p.ntail = 0;
+    p.split = 1;
+  }
   const uint32_t group_m = 8;
-  const dim3 grid(per_xcd * NXCD), block(256);
+  const dim3 block(256);
   // Interior tiles store 16-byte pieces of output rows: the base address and
   // every row start must be 16-byte aligned.
   const int64_t es = g.bf16out ? 2 : 4;
   const uint32_t vec_ok = (g.ldc * es) % 16 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
+  float* part = p.ntail ? g.split_ws : nullptr;
+  if (p.nfull) {
+    const dim3 grid((p.nfull + NXCD - 1) / NXCD * NXCD);
+    if (g.bf16out)
+      hipLaunchKernelGGL((k_gemm<FMT, BK, true, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
+                         g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
+                         p.tiles_m, p.tiles_n, group_m, p.nfull, p.ntail, p.split, part, g.c, g.ldc, vec_ok);
+    else
+      hipLaunchKernelGGL((k_gemm<FMT, BK, false, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
+                         g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
+                         p.tiles_m, p.tiles_n, group_m, p.nfull, p.ntail, p.split, part, g.c, g.ldc, vec_ok);
+  }
+  if (p.ntail) {
+    // The split pieces after the whole tiles (a partial wave of whole tiles
+    // is exactly what the split replaces), then their sum.
+    const dim3 grid(p.split * ((p.ntail + NXCD - 1) / NXCD * NXCD));
+    hipLaunchKernelGGL((k_gemm<FMT, BK, false, true>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
+                       g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
+                       p.tiles_m, p.tiles_n, group_m, p.nfull, p.ntail, p.split, part, g.c, g.ldc, vec_ok);
+  }
+  if (!p.ntail) return;
+  const dim3 rgrid(p.ntail * (BM / 32));
   if (g.bf16out)
-    hipLaunchKernelGGL((k_gemm<FMT, BK, true>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
-                       g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
-                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc, vec_ok);
+    hipLaunchKernelGGL((k_split_reduce<FMT, true>), rgrid, block, 0, s, part, p.nfull, p.split, p.tiles_m,
+                       p.tiles_n, group_m, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, g.c, g.ldc,
+                       vec_ok);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, BK, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,
-                       g.b_scales, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K,
-                       tiles_m, tiles_n, per_xcd, group_m, g.c, g.ldc, vec_ok);
+    hipLaunchKernelGGL((k_split_reduce<FMT, false>), rgrid, block, 0, s, part, p.nfull, p.split, p.tiles_m,
+                       p.tiles_n, group_m, g.a_tscale, g.b_tscale, (uint32_t)g.M, (uint32_t)g.N, g.c, g.ldc,
+                       vec_ok);
 }
 
 }  // namespace
+
+size_t fp4i_gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan p = split_plan(M, N, K);
+  return (size_t)p.ntail * p.split * (BM * BN) * sizeof(float);
+}
 
 bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K) {
   // Buffer offsets are 32-bit: each operand's codes must stay below 2^31 bytes.

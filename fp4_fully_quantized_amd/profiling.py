@@ -152,14 +152,14 @@ STEP_DISPATCHES = [
     ("dual X (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NX, 2 * _NX),
     ("amax W", r"^k_amax(_flat)?<", 2 * _NW, _NW),
     ("dual W (RTN along K, SR along out)", r"^k_quant_dual<0, 0, 1,", _DUAL * _NW, 2 * _NW),
-    ("NVFP4 GEMM fwd (bf16 out)", r"^k_gemm<0, 256, true>", _GF, 0),
+    ("NVFP4 GEMM fwd (bf16 out)", r"^k_gemm<0, 256, true, false>", _GF, 0),
     ("amax dY", r"^k_amax(_flat)?<", 2 * _NY, _NY),
     ("dual dY (SR both)", r"^k_quant_dual<0, 1, 1,", _DUAL * _NY, 2 * _NY),
-    ("NVFP4 GEMM dgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
-    ("NVFP4 GEMM wgrad (fp32 out)", r"^k_gemm<0, 256, false>", _GF, 0),
+    ("NVFP4 GEMM dgrad (fp32 out)", r"^k_gemm<0, 256, false, false>", _GF, 0),
+    ("NVFP4 GEMM wgrad (fp32 out)", r"^k_gemm<0, 256, false, false>", _GF, 0),
     ("MXFP4+Hadamard X", r"^k_quant_cols<1,", _MX * _NX, _NX),
     ("MXFP4+Hadamard W", r"^k_quant_cols<1,", _MX * _NW, _NW),
-    ("MXFP4 GEMM fwd (bf16 out)", r"^k_gemm<1, 256, true>", _GF, 0),
+    ("MXFP4 GEMM fwd (bf16 out)", r"^k_gemm<1, 256, true, false>", _GF, 0),
 ]
 EXTRA_DISPATCHES = [
     ("amax dY rotated 16-wide along tokens", r"^k_amax_rot_rows<", 2 * _NY, _NY),
@@ -255,8 +255,8 @@ LARGE_GROUPS = [
     ("tensor amax (X, W, dY)", r"^k_amax(_flat)?<"),
     ("quantize X, both orientations (RTN along K, SR along tokens)", r"^k_quant_dual<0, 0, 1,"),
     ("quantize dY, both orientations (SR)", r"^k_quant_dual<0, 1, 1,"),
-    ("NVFP4 GEMM fwd 16384x28672x8192 (bf16 out)", r"^k_gemm<0, 256, true>"),
-    ("NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)", r"^k_gemm<0, 256, false>"),
+    ("NVFP4 GEMM fwd 16384x28672x8192 (bf16 out)", r"^k_gemm<0, 256, true, false>"),
+    ("NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)", r"^k_gemm<0, 256, false, false>"),
 ]
 
 
@@ -357,8 +357,8 @@ def summarize_trace(out_dir: str, profiles_dir: str) -> None:
         "first launches of a run are slower while the clock settles); that is the figure to set against the "
         "benchmark's HIP-event times.",
         "",
-        "`k_gemm<0, 256, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *>` = MXFP4 GEMM (scaled FP4 MFMA); "
-        "the last template flag = bf16 output.",
+        "`k_gemm<0, 256, *, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *, *>` = MXFP4 GEMM (scaled FP4 MFMA); "
+        "the third template flag = bf16 output, the fourth = a split-K piece (none in this step).",
         "",
         "## Kernel groups (from the kernel trace)",
         "",

@@ -326,6 +326,23 @@ typedef struct fp4_operand {
  * rows or K is invalid (fp4_gemm reports which). Host-only. */
 size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B);
 
+/* Optional workspace beyond fp4_gemm_workspace_bytes(A, B): given at least
+ * fp4_gemm_workspace_bytes(A, B) + fp4_gemm_splitk_bytes(A, B) bytes,
+ * fp4_gemm splits the output tiles of the last, partial wave of workgroups
+ * (one 256 x 256 tile per CU) along K, writes their FP32 partial tiles to
+ * this area (placed after the RAW operands' pieces, on a 256-byte boundary)
+ * and adds them, in split order, in a second kernel on the stream. This pays
+ * when few tiles would keep few CUs busy for a long K: the plan weighs the
+ * shorter wave against the partial tiles' traffic, and takes into account
+ * that a wave on fewer CUs runs at a higher clock (the chip is power-limited
+ * under this load). E.g. 6 tiles of a 520 x 300 x 8192 product split in 4,
+ * a 2048 x 2048 x 32768 weight gradient's 64 tiles in 3; the Llama-7B
+ * layer's GEMMs do not split. A split product differs from the unsplit one
+ * only in the order of its FP32 additions, and is the same on every call
+ * for a given shape. 0 when the shape never splits or the operands are
+ * invalid. Host-only. */
+size_t fp4_gemm_splitk_bytes(const fp4_operand* A, const fp4_operand* B);
+
 /* C[i][j] = alpha * sum_k A_hat[i][k] * B_hat[j][k] with FP32 accumulation
  * (Robots Atlas, "FP4", How it works: FP4 products accumulated in higher
  * precision; "Quartet", one-line summary: forward, dgrad and wgrad all run as
@@ -346,7 +363,8 @@ size_t fp4_gemm_workspace_bytes(const fp4_operand* A, const fp4_operand* B);
  * stream before the product; ws: device, 256-byte aligned, ws_bytes at least
  * fp4_gemm_workspace_bytes(A, B) (FP4_ERR_WORKSPACE otherwise; ws may be NULL
  * when neither operand is RAW). The workspace holds the quantized operands
- * when the call's work has run.
+ * when the call's work has run. With fp4_gemm_splitk_bytes(A, B) more bytes
+ * the last partial wave of output tiles is split along K (see there).
  * C: device, M x N row-major, leading dimension ldc >= N, FP32 or bf16
  * (rounded to nearest even once, after alpha).
  * Requires: same fmt, had_on and had_signs on both operands
@@ -376,7 +394,8 @@ fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t,
  * FP4_GEMM_NOALLOC_MAX_BYTES (nothing enqueued). Every call on a GPU shares
  * that GPU's array and leaves its quantized operands there: calls with RAW
  * operands that overlap on one GPU (other streams, other threads) race on it,
- * so the caller serializes them. Otherwise as fp4_gemm. */
+ * so the caller serializes them. It never splits along K (the array holds
+ * only the RAW operands). Otherwise as fp4_gemm. */
 fp4_status fp4_gemm_noalloc(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t, void* C,
                             int64_t ldc, fp4_stream_t stream);
 

@@ -288,6 +288,51 @@ def test_gemm_workspace_bytes(fp4):
     assert L.fp4_gemm_workspace_bytes(None, ctypes.byref(qb)) == 0
 
 
+
+def _splitk(fp4, M, N, K, fmt=0):
+    L = fp4.lib()
+    a = _q_op(fp4, _t(fp4, rows=M, cols=K, fmt=fmt))
+    b = _q_op(fp4, _t(fp4, rows=N, cols=K, fmt=fmt))
+    return L.fp4_gemm_splitk_bytes(ctypes.byref(a), ctypes.byref(b))
+
+
+def test_gemm_splitk_bytes(fp4):
+    """The split-K area: the tiles of the last, partial wave (tiles mod 256)
+    times the pieces the plan chooses times one FP32 256 x 256 tile. The plan
+    prices a wave of n tiles at max(n / 256, 1.7 / 2.4) of a full one (the
+    clock rises when fewer CUs run) against the partial tiles' traffic."""
+    tile = 256 * 256 * 4
+    # Llama-7B: wgrad's last wave of 176 of its 688 tiles already runs at the
+    # higher clock; forward (5504 tiles, K = 4096) and dgrad (2048) neither
+    assert _splitk(fp4, 11008, 4096, 32768) == 0
+    assert _splitk(fp4, 11008, 4096, 32768, fmt=1) == 0
+    assert _splitk(fp4, 32768, 11008, 4096) == 0
+    assert _splitk(fp4, 32768, 4096, 11008) == 0
+    # the large layer: 7168, 2048 and 3584 tiles, all whole waves
+    assert _splitk(fp4, 16384, 28672, 8192) == 0
+    assert _splitk(fp4, 16384, 8192, 28672) == 0
+    assert _splitk(fp4, 28672, 8192, 16384) == 0
+    # few tiles: 6 tiles with K = 8192 (32 K tiles) in 4 pieces of 8, with 4096 in 2
+    assert _splitk(fp4, 520, 300, 8192) == 6 * 4 * tile
+    assert _splitk(fp4, 520, 300, 4096) == 6 * 2 * tile
+    assert _splitk(fp4, 520, 300, 7936) == 6 * 3 * tile
+    # K % 256 != 0 counts 128-wide K tiles: 8064 = 63 of them, 7 pieces of 9
+    assert _splitk(fp4, 520, 300, 8064) == 6 * 7 * tile
+    # 272 tiles: the 16 of the second wave in 4 pieces
+    assert _splitk(fp4, 4352, 4096, 8192) == 16 * 4 * tile
+    # a 2048 x 2048 weight gradient over 32768 tokens: 64 tiles in 3 pieces
+    assert _splitk(fp4, 2048, 2048, 32768) == 64 * 3 * tile
+    # too short for a piece of 8 K tiles
+    assert _splitk(fp4, 520, 300, 3840) == 0
+    assert _splitk(fp4, 200, 136, 256) == 0
+    # invalid pairs
+    L = fp4.lib()
+    qa = _q_op(fp4, _t(fp4, rows=64, cols=8192))
+    qb = _q_op(fp4, _t(fp4, rows=64, cols=4096))
+    assert L.fp4_gemm_splitk_bytes(ctypes.byref(qa), ctypes.byref(qb)) == 0
+    assert L.fp4_gemm_splitk_bytes(None, ctypes.byref(qb)) == 0
+
+
 RAW_BAD = [
     # (A overrides (raw), ws, ws_bytes, expected): B is a valid quantized NVFP4 64 x 128 operand
     ({}, None, 0, 7),                                   # no workspace

@@ -325,3 +325,54 @@ def test_raw_and_quantized_operands_mixed(fp4, orc):
     ref, S = orc.gemm_ref(orc.quantize(dyh, rnd=1, seed=5), orc.quantize(wh, axis=1, rnd=1, seed=6))
     ok, worst = orc.gemm_check(orc.bf16_bits_to_f32(to_host(dx)), ref, S, "bf16")
     assert ok, worst
+
+
+# Split along K of the last, partial wave of output tiles (fp4_gemm_splitk_bytes).
+@pytest.mark.parametrize("fmt,out", [(0, "fp32"), (0, "bf16"), (1, "fp32"), (1, "bf16")])
+def test_split_k_gemm(fp4, orc, fmt, out):
+    """520 x 300 x 8192 (6 output tiles, 32 K tiles): with the split-K area
+    each tile is computed in 4 K ranges whose FP32 partial tiles a second
+    kernel adds, ragged edges included. Within the oracle's tolerance, the
+    same bits on a second call, and the unsplit product (no workspace) within
+    the same tolerance: the two differ only in the order of FP32 additions."""
+    import torch
+    M, N, K = 520, 300, 8192
+    say("split-k gemm fmt", fmt, "out", out)
+    qa = orc.quantize(_data((M, K), 61, outliers=True), fmt=fmt)
+    qb = orc.quantize(_data((N, K), 62, std=0.02), fmt=fmt)
+    A, B = q_from_oracle(qa), q_from_oracle(qb)
+    assert fp4.fp4_gemm_splitk_bytes(A, B) == 6 * 4 * 256 * 256 * 4
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    y1 = fp4.gemm(A, B, dtype=dt)
+    y2 = fp4.gemm(A, B, dtype=dt)
+    iv = torch.int16 if out == "bf16" else torch.int32
+    assert torch.equal(y1.view(iv), y2.view(iv))
+    y0 = torch.empty_like(y1)
+    fp4.fp4_gemm(A, B, y0)
+    ref, S = orc.gemm_ref(qa, qb)
+    for what, y in (("split", y1), ("unsplit", y0)):
+        yh = to_host(y)
+        if out == "bf16":
+            yh = orc.bf16_bits_to_f32(yh)
+        ok, worst = orc.gemm_check(yh, ref, S, out)
+        say(what, "worst error / bound", worst)
+        assert ok, (what, worst)
+
+
+def test_split_k_gemm_after_whole_tiles(fp4, orc):
+    """4352 x 4096 x 8192: 272 tiles, the first 256 computed whole and the
+    last 16 split in 4; sampled rows cover every tile row, all columns."""
+    import torch
+    M, N, K = 4352, 4096, 8192
+    say("split-k gemm after a whole wave")
+    qa = orc.quantize(_data((M, K), 63), rnd=1, seed=7)
+    qb = orc.quantize(_data((N, K), 64, std=0.02), rnd=1, seed=8)
+    A, B = q_from_oracle(qa), q_from_oracle(qb)
+    assert fp4.fp4_gemm_splitk_bytes(A, B) == 16 * 4 * 256 * 256 * 4
+    y = fp4.gemm(A, B, dtype=torch.float32)
+    rows = _sample_rows(M, 23, 16)
+    yh = to_host(y[torch.from_numpy(rows).cuda()])
+    ref, S = orc.gemm_ref(_rows_of(qa, rows), qb)
+    ok, worst = orc.gemm_check(yh, ref, S, "fp32")
+    say("worst error / bound", worst)
+    assert ok, worst

@@ -12,11 +12,11 @@ def _names(steps, warmup):
     # written out independently of the tables under test.
     step = ["k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
             "k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
-            "k_gemm<0, 256, true>",
+            "k_gemm<0, 256, true, false>",
             "k_amax<true, false>", "k_quant_dual<0, 1, 1, true, false, false, false>",
-            "k_gemm<0, 256, false>", "k_gemm<0, 256, false>",
+            "k_gemm<0, 256, false, false>", "k_gemm<0, 256, false, false>",
             "k_quant_cols<1, 0, true, true, false>", "k_quant_cols<1, 0, true, true, false>",
-            "k_gemm<1, 256, true>"]
+            "k_gemm<1, 256, true, false>"]
     extras = ["k_amax_rot_rows<true>", "k_amax_pair<true, false, true>",
               "k_quant_dual<0, 0, 1, true, false, true, false>", "k_amax_pair<true, false, true>",
               "k_quant_dual<0, 1, 1, true, false, true, false>", "k_amax<true, false>",
@@ -99,7 +99,7 @@ def test_summarize_on_synthetic_counters(tmp_path):
                                                                     "End_Timestamp"], trace)
     _write_csv(str(out / "prof_bench" / "bench_kernel_stats.csv"),
                ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
-               [[_raw("k_gemm<0, 256, true>"), 13, 2e6, 1.9e6, 2.1e6, 30.0]])
+               [[_raw("k_gemm<0, 256, true, false>"), 13, 2e6, 1.9e6, 2.1e6, 30.0]])
     p.summarize(str(out), str(prof))
 
     q = (prof / "quantize_llama7b_hbm_traffic.md").read_text()
@@ -117,9 +117,9 @@ def test_summarize_on_synthetic_counters(tmp_path):
 def _large_names(steps, warmup):
     step = ["k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
             "k_amax<true, false>", "k_quant_dual<0, 0, 1, true, false, false, false>",
-            "k_gemm<0, 256, true>",
+            "k_gemm<0, 256, true, false>",
             "k_amax<true, false>", "k_quant_dual<0, 1, 1, true, false, false, false>",
-            "k_gemm<0, 256, false>", "k_gemm<0, 256, false>"]
+            "k_gemm<0, 256, false, false>", "k_gemm<0, 256, false, false>"]
     return step * (warmup + steps)
 
 
@@ -130,13 +130,13 @@ def test_trace_split_into_llama_ceilings_and_large_step(tmp_path):
     ceil = ["k_mfma_f16", "k_mfma_fp4"] + ["k_stream_read", "k_stream_copy", "k_stream_read4_write1"]
     names = _names(p.STEPS, p.WARMUP) + ["__amd_rocclr_copyBuffer"] + ceil + ["fill"] + \
         _large_names(p.STEPS, p.WARMUP)
-    dur = {"k_gemm<0, 256, true>": 5_000_000, "k_gemm<0, 256, false>": 6_000_000}
+    dur = {"k_gemm<0, 256, true, false>": 5_000_000, "k_gemm<0, 256, false, false>": 6_000_000}
     trace, t = [], 0
     n_large = len(_large_names(p.STEPS, p.WARMUP))
     first_large = len(names) - n_large
     for k, n in enumerate(names):
         d = dur.get(n, 100_000) if k >= first_large else 1000
-        if k >= first_large and n == "k_gemm<0, 256, false>":
+        if k >= first_large and n == "k_gemm<0, 256, false, false>":
             d = 6_000_000 if (k - first_large) % 9 == 7 else 7_000_000   # dgrad, then wgrad
         trace.append([_raw(n), t, t + d])
         t += d + 10
