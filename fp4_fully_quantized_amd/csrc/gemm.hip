@@ -39,6 +39,11 @@
 // accumulator holds four consecutive columns of one output row; after the K
 // loop each wave stages its outputs through the idle LDS tiles, 32 rows at a
 // time, and every store instruction writes whole rows in 16-byte pieces.
+//
+// Split-K (optional, with caller workspace): when the tiles do not fill the
+// last wave of workgroups and K is long enough to pay for it (split_plan), the
+// whole tiles run first, then the remaining tiles as pieces over K ranges
+// that write FP32 partial tiles, which k_split_reduce adds in piece order.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 

@@ -67,17 +67,31 @@ def counter_per_dispatch(csv_path: str, counter: str, name_regex: str):
     return out
 
 
-def source_digest() -> str:
-    """Digest of the GEMM sources: a traffic figure is valid for this digest only."""
+def code_digest(texts) -> str:
+    """Digest of C++/HIP sources with comments and whitespace removed, so that
+    only a change of the code itself (not of its comments) changes it."""
     import hashlib
-    import os
+    import re
 
     h = hashlib.sha256()
-    here = os.path.dirname(os.path.abspath(__file__))
-    for fn in ("gemm.hip", "fp4_device.hpp"):
-        with open(os.path.join(here, "csrc", fn), "rb") as f:
-            h.update(f.read())
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
+
+
+def source_digest() -> str:
+    """Digest of the GEMM sources' code: a traffic figure is valid for this digest only."""
+    import os
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    texts = []
+    for fn in ("gemm.hip", "fp4_device.hpp"):
+        with open(os.path.join(here, "csrc", fn)) as f:
+            texts.append(f.read())
+    return code_digest(texts)
 
 
 # ---------------------------------------------------------------- the profile set

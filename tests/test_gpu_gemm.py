@@ -376,3 +376,29 @@ def test_split_k_gemm_after_whole_tiles(fp4, orc):
     ok, worst = orc.gemm_check(yh, ref, S, "fp32")
     say("worst error / bound", worst)
     assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("out,pad", [("fp32", 0), ("fp32", 19), ("bf16", 0), ("bf16", 19)])
+def test_split_k_gemm_into_a_strided_output(fp4, orc, fmt, out, pad):
+    """Split-K into an output of 301 columns (not a multiple of 4) with
+    ldc = 301 + pad: pad 19 gives 16-byte aligned fp32 rows (ldc 320), so the
+    reduction stores whole 4-column pieces and the last columns element by
+    element; pad 0 stores every element alone. The padding stays untouched."""
+    import torch
+    M, N, K = 300, 301, 8192
+    say("split-k gemm strided output", fmt, out, pad)
+    qa = orc.quantize(_data((M, K), 71, outliers=True), fmt=fmt)
+    qb = orc.quantize(_data((N, K), 72, std=0.02), fmt=fmt)
+    A, B = q_from_oracle(qa), q_from_oracle(qb)
+    assert fp4.fp4_gemm_splitk_bytes(A, B) > 0
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    full = torch.full((M, N + pad), 7.0, dtype=dt, device="cuda")
+    fp4.gemm(A, B, out=full[:, :N])
+    yh = to_host(full)
+    if out == "bf16":
+        yh = orc.bf16_bits_to_f32(yh)
+    assert (yh[:, N:] == 7.0).all()
+    ref, S = orc.gemm_ref(qa, qb)
+    ok, worst = orc.gemm_check(yh[:, :N], ref, S, out)
+    assert ok, worst

@@ -156,3 +156,14 @@ def test_trace_split_into_llama_ceilings_and_large_step(tmp_path):
     assert "| tensor amax (X, W, dY) | 39 | 100.0 |" in text
     p._write_ceilings(ce, "CMD", str(prof))
     assert "| f16 MFMA loop" in (prof / "chip_ceilings_kernel_stats.md").read_text()
+
+
+def test_code_digest_ignores_comments_only():
+    from fp4_fully_quantized_amd.profiling import code_digest
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    b = "/* f: the successor */\nint f(int x) {\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert code_digest([a]) == code_digest([b])
+    assert code_digest([a]) != code_digest([c])
+    # the files are hashed as separate texts
+    assert code_digest([a, c]) != code_digest([c, a])
