@@ -27,7 +27,7 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
            "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_noise_ratio", "fp4_quantize_2d",
-           "fp4_dequantize", "fp4_gemm_workspace_bytes", "fp4_gemm_splitk_bytes", "fp4_gemm",
+           "fp4_dequantize", "fp4_dequantize_unrotated", "fp4_gemm_workspace_bytes", "fp4_gemm_splitk_bytes", "fp4_gemm",
            "fp4_gemm_noalloc"]
 # The allocation-free GEMM's workspace limit (FP4_GEMM_NOALLOC_MAX_BYTES).
 FP4_GEMM_NOALLOC_MAX_BYTES = 128 << 20
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
                                       c.c_uint64, c.c_uint64, c.c_int, c.POINTER(fp4_tensor),
                                       c.POINTER(fp4_tensor), c.c_void_p]
         L.fp4_dequantize.restype = c.c_int
+        L.fp4_dequantize_unrotated.restype = c.c_int
+        L.fp4_dequantize_unrotated.argtypes = [c.POINTER(fp4_tensor), c.c_int, c.c_void_p, c.c_int64,
+                                               c.c_void_p]
         L.fp4_dequantize.argtypes = [c.POINTER(fp4_tensor), c.c_int, c.c_void_p, c.c_int64,
                                      c.c_void_p]
         L.fp4_noise_ratio.restype = c.c_int
@@ -386,13 +389,23 @@ def noise_ratio(noise, stream=None):
 
 
 def fp4_dequantize(q: QTensor, dst, stream=None) -> None:
+    _dequantize("fp4_dequantize", q, dst, stream)
+
+
+def fp4_dequantize_unrotated(q: QTensor, dst, stream=None) -> None:
+    """fp4_dequantize, then the inverse of the quantization's block rotation
+    (when q.had_on): the values in the tensor's own domain."""
+    _dequantize("fp4_dequantize_unrotated", q, dst, stream)
+
+
+def _dequantize(name, q, dst, stream):
     _check_qtensor(q, "q")
     _check_matrix(dst, "dst", q.codes.device)
     if tuple(dst.shape) != (q.rows, q.cols):
         raise ValueError(f"dst is {tuple(dst.shape)}, q is {q.rows} x {q.cols}")
     d = q.desc()
-    _check(lib().fp4_dequantize(ctypes.byref(d), _dtype_code(dst), dst.data_ptr(), dst.stride(0),
-                                _stream(stream)), "fp4_dequantize")
+    _check(getattr(lib(), name)(ctypes.byref(d), _dtype_code(dst), dst.data_ptr(), dst.stride(0),
+                                _stream(stream)), name)
 
 
 class RawOperand:
@@ -550,10 +563,12 @@ def quantize_dual(src, fmt: int = FP4_NVFP4, rnd_cols: int = FP4_RTN, seed_cols:
     return qc, qr
 
 
-def dequantize(q: QTensor, dtype=None, stream=None):
+def dequantize(q: QTensor, dtype=None, stream=None, unrotate=False):
+    """Allocate the output and run fp4_dequantize (fp4_dequantize_unrotated
+    with unrotate=True)."""
     import torch
     dst = torch.empty((q.rows, q.cols), dtype=dtype or torch.float32, device=q.codes.device)
-    fp4_dequantize(q, dst, stream)
+    (fp4_dequantize_unrotated if unrotate else fp4_dequantize)(q, dst, stream)
     return dst
 
 

@@ -370,6 +370,19 @@ fp4_status gemm_impl(const fp4_operand* A, const fp4_operand* B, fp4_dtype out_t
   return hip_status();
 }
 
+// Every check of a dequantization (both entry points).
+fp4_status check_dequant(const fp4_tensor* q, fp4_dtype dst_t, const void* dst, int64_t ld) {
+  if (!q || !dst) return FP4_ERR_NULL;
+  if (!valid_dtype(dst_t) || !valid_fmt(q->fmt)) return FP4_ERR_ARG;
+  if (!q->codes || !q->scales) return FP4_ERR_NULL;
+  if (q->fmt == FP4_NVFP4 && !q->tscale) return FP4_ERR_NULL;
+  if (q->rows <= 0 || q->cols <= 0 || q->cols % block_of(q->fmt) != 0 || ld < q->cols)
+    return FP4_ERR_SHAPE;
+  if (!fits_tasks(q->rows, q->cols)) return FP4_ERR_SHAPE;
+  if (!aligned16(dst) || ld % 8 != 0 || !aligned16(q->codes)) return FP4_ERR_ALIGN;
+  return FP4_OK;
+}
+
 // The address of `scratch` on each device, looked up once per device with
 // that device current (each GPU holds its own copy at its own address).
 constexpr int kMaxDevices = 64;
@@ -549,16 +562,24 @@ fp4_status fp4_quantize_2d(const void* src, fp4_dtype src_t, int64_t R, int64_t 
   return hip_status();
 }
 
+fp4_status fp4_dequantize_unrotated(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
+                                    fp4_stream_t stream) {
+  const fp4_status st = check_dequant(q, dst_t, dst, ld);
+  if (st != FP4_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (q->had_on)
+    fp4i_launch_dequant_unrot(q->codes, q->scales, q->tscale, q->fmt, q->rows, q->cols, q->had_signs,
+                              dst_t == FP4_DTYPE_BF16, dst, ld, s);
+  else
+    fp4i_launch_dequant(q->codes, q->scales, q->tscale, q->fmt, q->rows, q->cols,
+                        dst_t == FP4_DTYPE_BF16, dst, ld, s);
+  return hip_status();
+}
+
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
                           fp4_stream_t stream) {
-  if (!q || !dst) return FP4_ERR_NULL;
-  if (!valid_dtype(dst_t) || !valid_fmt(q->fmt)) return FP4_ERR_ARG;
-  if (!q->codes || !q->scales) return FP4_ERR_NULL;
-  if (q->fmt == FP4_NVFP4 && !q->tscale) return FP4_ERR_NULL;
-  if (q->rows <= 0 || q->cols <= 0 || q->cols % block_of(q->fmt) != 0 || ld < q->cols)
-    return FP4_ERR_SHAPE;
-  if (!fits_tasks(q->rows, q->cols)) return FP4_ERR_SHAPE;
-  if (!aligned16(dst) || ld % 8 != 0 || !aligned16(q->codes)) return FP4_ERR_ALIGN;
+  const fp4_status st = check_dequant(q, dst_t, dst, ld);
+  if (st != FP4_OK) return st;
   fp4i_launch_dequant(q->codes, q->scales, q->tscale, q->fmt, q->rows, q->cols,
                       dst_t == FP4_DTYPE_BF16, dst, ld, reinterpret_cast<hipStream_t>(stream));
   return hip_status();

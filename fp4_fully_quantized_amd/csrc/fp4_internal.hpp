@@ -92,6 +92,11 @@ void fp4i_launch_quant_2d(const Quant2dArgs& a, hipStream_t s);
 void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
                          int64_t rows, int64_t cols, bool bf16out, void* dst, int64_t ld,
                          hipStream_t s);
+// Dequantize, then the inverse of the block rotation with sign mask `signs`
+// (B = 16 for NVFP4, 32 for MXFP4) on every block of each row.
+void fp4i_launch_dequant_unrot(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
+                               int64_t rows, int64_t cols, uint32_t signs, bool bf16out, void* dst,
+                               int64_t ld, hipStream_t s);
 bool fp4i_gemm_fits(int64_t M, int64_t N, int64_t K);
 // Bytes of the split-K area the GEMM of this shape can use (0: it never splits).
 size_t fp4i_gemm_split_bytes(int64_t M, int64_t N, int64_t K);

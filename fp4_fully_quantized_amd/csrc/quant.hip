@@ -32,6 +32,7 @@
 //                  columns, and the codes leave through an LDS staging area
 //                  in whole 128-byte lines.
 //  * k_dequant     8 elements per lane.
+//  * k_dequant_unrot  one block per lane, then the inverse block rotation.
 // Both orientations from one read are in quant_dual.hip.
 #include "fp4_internal.hpp"
 #include "quant_common.hpp"
@@ -604,6 +605,75 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   }
 }
 
+// Dequantize and undo the quantization's block rotation: one block per lane
+// (16 or 32 values), decoded as k_dequant does, then the FWHT stages and the
+// normalisation (fwht_block) and the signs: D H c, the transpose of the
+// rotation c H D.
+template <int FMT, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dequant_unrot(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        const float* __restrict__ tscale, int64_t cols,
+                                                        uint64_t nblocks, uint32_t signs, void* dst,
+                                                        int64_t ld) {
+  constexpr int B = FMT == NV ? 16 : 32;
+  const int64_t bpr = cols / B;
+  const float sg = (FMT == NV) ? *tscale : 1.0f;
+  for (uint64_t blk = (uint64_t)blockIdx.x * 256u + threadIdx.x; blk < nblocks;
+       blk += (uint64_t)gridDim.x * 256u) {
+    const int64_t r = (int64_t)(blk / (uint64_t)bpr);
+    const int64_t cb = (int64_t)blk - r * bpr;
+    const uint8_t* cp = codes + r * (cols / 2) + cb * (B / 2);
+    uint32_t w[B / 8];
+    if constexpr (B == 16) {
+      const uint2 v = *reinterpret_cast<const uint2*>(cp);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(cp);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    const uint32_t sb = scales[r * bpr + cb];
+    float x[B];
+#pragma unroll
+    for (int g = 0; g < B / 8; ++g) {
+      const auto q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[g], 1.0f, 0);
+      const auto q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[g], 1.0f, 1);
+      const auto q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[g], 1.0f, 2);
+      const auto q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[g], 1.0f, 3);
+      x[8 * g + 0] = q0[0]; x[8 * g + 1] = q0[1]; x[8 * g + 2] = q1[0]; x[8 * g + 3] = q1[1];
+      x[8 * g + 4] = q2[0]; x[8 * g + 5] = q2[1]; x[8 * g + 6] = q3[0]; x[8 * g + 7] = q3[1];
+    }
+    if constexpr (FMT == NV) {
+      const float sdec = e4m3_decode(sb);
+#pragma unroll
+      for (int i = 0; i < B; ++i) x[i] = (x[i] * sdec) * sg;
+    } else {
+#pragma unroll
+      for (int i = 0; i < B; ++i) x[i] = __builtin_ldexpf(x[i], (int)sb - 127);
+    }
+    fwht_block<B>(x);
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if ((signs >> i) & 1u) x[i] = -x[i];
+    if constexpr (BF16OUT) {
+      uint32_t o[B / 2];
+#pragma unroll
+      for (int i = 0; i < B / 2; ++i) {
+        uint32_t a = __float_as_uint(x[2 * i]), b = __float_as_uint(x[2 * i + 1]);
+        a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+        b = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+        o[i] = a | (b << 16);
+      }
+      uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + r * ld + cb * B);
+#pragma unroll
+      for (int i = 0; i < B / 8; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    } else {
+      float4* d = reinterpret_cast<float4*>(static_cast<float*>(dst) + r * ld + cb * B);
+#pragma unroll
+      for (int i = 0; i < B / 4; ++i) d[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    }
+  }
+}
+
 constexpr uint32_t kMaxGrid = 256 * 16;
 
 uint32_t strided_grid(uint64_t ntasks) {
@@ -768,5 +838,20 @@ void fp4i_launch_dequant(const uint8_t* codes, const uint8_t* scales, const floa
   } else {
     if (bf16out) hipLaunchKernelGGL((k_dequant<MX, true>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
     else hipLaunchKernelGGL((k_dequant<MX, false>), g, b, 0, s, codes, scales, tscale, cols, spr, ntasks, dst, ld);
+  }
+}
+
+void fp4i_launch_dequant_unrot(const uint8_t* codes, const uint8_t* scales, const float* tscale, int fmt,
+                               int64_t rows, int64_t cols, uint32_t signs, bool bf16out, void* dst,
+                               int64_t ld, hipStream_t s) {
+  const uint64_t nblocks = (uint64_t)rows * (uint64_t)(cols / (fmt == NV ? 16 : 32));
+  const uint64_t wgs = (nblocks + 255) / 256;
+  const dim3 g((uint32_t)(wgs < 8192 ? wgs : 8192)), b(256);
+  if (fmt == NV) {
+    if (bf16out) hipLaunchKernelGGL((k_dequant_unrot<NV, true>), g, b, 0, s, codes, scales, tscale, cols, nblocks, signs, dst, ld);
+    else hipLaunchKernelGGL((k_dequant_unrot<NV, false>), g, b, 0, s, codes, scales, tscale, cols, nblocks, signs, dst, ld);
+  } else {
+    if (bf16out) hipLaunchKernelGGL((k_dequant_unrot<MX, true>), g, b, 0, s, codes, scales, tscale, cols, nblocks, signs, dst, ld);
+    else hipLaunchKernelGGL((k_dequant_unrot<MX, false>), g, b, 0, s, codes, scales, tscale, cols, nblocks, signs, dst, ld);
   }
 }

@@ -276,6 +276,21 @@ fp4_status fp4_quantize_2d(const void* src, fp4_dtype src_t, int64_t R, int64_t 
 fp4_status fp4_dequantize(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
                           fp4_stream_t stream);
 
+/* fp4_dequantize, then, when q->had_on, the inverse of the block rotation the
+ * quantization applied (Quartet, Approach: block-wise Hadamard rotations;
+ * Robots Atlas, "FP4", How it works: random Hadamard transforms), so the
+ * values are read back in the tensor's own domain rather than the rotated
+ * one. The rotation of a block was y = c H D x (D = diag(+-1) from
+ * q->had_signs, H the Sylvester Hadamard matrix, c = 2^-2.5 rounded to FP32
+ * for MXFP4's 32-value blocks, 1/4 for NVFP4's 16); its inverse, the
+ * transpose D H c, is applied to each block of dequantized values in the
+ * quantized orientation: the butterfly stages h = 1, 2, 4, ... (each sum and
+ * difference one FP32 operation), the product with c, then the signs. With
+ * had_on == 0 the result equals fp4_dequantize's. Requirements and errors as
+ * fp4_dequantize. */
+fp4_status fp4_dequantize_unrotated(const fp4_tensor* q, fp4_dtype dst_t, void* dst, int64_t ld,
+                                    fp4_stream_t stream);
+
 /* GEMM operands. Each operand stands for a rows x K matrix (A: M x K,
  * B: N x K) whose values the GEMM contracts along K. It is either already
  * quantized, or a raw matrix that fp4_gemm quantizes into the caller's

@@ -259,6 +259,43 @@ void o_fwht16(float x[16], uint32_t signs)
     for (int j = 0; j < 16; ++j) x[j] = x[j] * 0.25f;
 }
 
+/* The inverse rotation. c*H*D is orthonormal (up to the rounding of c), so */
+/* its inverse is its transpose D*H*c (H is symmetric): the same butterfly   */
+/* stages on y, the product with c, then the signs. Used to read a rotated   */
+/* quantization back in the tensor's own domain.                             */
+void o_unfwht32(float y[32], uint32_t signs)
+{
+    const float c = (float)ldexp(sqrt(2.0), -3); /* 2^-2.5 */
+    for (int h = 1; h < 32; h <<= 1) {
+        for (int i = 0; i < 32; ++i) {
+            if ((i & h) == 0) {
+                float a = y[i], b = y[i + h];
+                y[i] = a + b;
+                y[i + h] = a - b;
+            }
+        }
+    }
+    for (int j = 0; j < 32; ++j) y[j] = y[j] * c;
+    for (int j = 0; j < 32; ++j)
+        if ((signs >> j) & 1u) y[j] = -y[j];
+}
+
+void o_unfwht16(float y[16], uint32_t signs)
+{
+    for (int h = 1; h < 16; h <<= 1) {
+        for (int i = 0; i < 16; ++i) {
+            if ((i & h) == 0) {
+                float a = y[i], b = y[i + h];
+                y[i] = a + b;
+                y[i + h] = a - b;
+            }
+        }
+    }
+    for (int j = 0; j < 16; ++j) y[j] = y[j] * 0.25f;
+    for (int j = 0; j < 16; ++j)
+        if ((signs >> j) & 1u) y[j] = -y[j];
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tensors.                                                                  */
 /* ------------------------------------------------------------------------ */
@@ -576,6 +613,25 @@ int o_dequantize_f64(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
             double q = o_e2m1_value(code);
             double s = scale_value(scales, r * (cols / B) + c / B, fmt);
             out[pos] = (fmt == O_FMT_NVFP4) ? q * s * (double)sg : q * s;
+        }
+    return 0;
+}
+
+/* Dequantize, then undo the block rotation the quantization applied        */
+/* (had_on): each block of B values in the quantized orientation goes        */
+/* through o_unfwht (B = 16 for NVFP4, 32 for MXFP4), so the result          */
+/* approximates the source tensor itself rather than its rotation.           */
+int o_dequantize_unrotated_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                               int fmt, float sg, uint32_t had_signs, float* out)
+{
+    const int B = (fmt == O_FMT_NVFP4) ? 16 : 32;
+    int rc = o_dequantize_f32(codes, scales, rows, cols, fmt, sg, out);
+    if (rc != 0) return rc;
+#pragma omp parallel for
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; c += B) {
+            if (B == 16) o_unfwht16(out + r * cols + c, had_signs);
+            else o_unfwht32(out + r * cols + c, had_signs);
         }
     return 0;
 }

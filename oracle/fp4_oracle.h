@@ -54,6 +54,9 @@ uint32_t o_hadamard_signs(uint64_t seed);
 /* ---- rotation ---- */
 void     o_fwht32(float x[32], uint32_t signs);        /* signs, Sylvester FWHT, times 2^-2.5 */
 void     o_fwht16(float x[16], uint32_t signs);        /* bits 0..15, Sylvester FWHT, times 1/4 */
+/* inverses (transposes): FWHT stages, times 2^-2.5 (1/4), then the signs */
+void     o_unfwht32(float y[32], uint32_t signs);
+void     o_unfwht16(float y[16], uint32_t signs);
 
 /* ---- tensors ---- */
 /* max |x| over an R x C matrix with leading dimension ld (elements). */
@@ -99,6 +102,10 @@ int o_dequantize_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
 /* Exact dequantized values in FP64 (e2m1 * scale * tensor_scale is exact in FP64). */
 int o_dequantize_f64(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int fmt, float sg, double* out);
+/* o_dequantize_f32, then each block of the quantized orientation through the
+ * inverse rotation (NVFP4: o_unfwht16, MXFP4: o_unfwht32) with had_signs. */
+int o_dequantize_unrotated_f32(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                               int fmt, float sg, uint32_t had_signs, float* out);
 
 int o_num_threads(void);
 

@@ -70,6 +70,10 @@ def lib():
         L.o_fwht32.argtypes = [c.POINTER(c.c_float), c.c_uint32]
         L.o_fwht16.restype = None
         L.o_fwht16.argtypes = [c.POINTER(c.c_float), c.c_uint32]
+        L.o_unfwht32.restype = None
+        L.o_unfwht32.argtypes = [c.POINTER(c.c_float), c.c_uint32]
+        L.o_unfwht16.restype = None
+        L.o_unfwht16.argtypes = [c.POINTER(c.c_float), c.c_uint32]
         L.o_tensor_amax.restype = c.c_float
         L.o_tensor_amax.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64]
         L.o_quantize.restype = c.c_int
@@ -90,6 +94,9 @@ def lib():
         L.o_dequantize_f64.restype = c.c_int
         L.o_dequantize_f64.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                        c.c_float, c.c_void_p]
+        L.o_dequantize_unrotated_f32.restype = c.c_int
+        L.o_dequantize_unrotated_f32.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
+                                                 c.c_float, c.c_uint32, c.c_void_p]
         L.o_num_threads.restype = c.c_int
         _lib = L
     return _lib
@@ -155,6 +162,22 @@ def fwht16(x, signs: int) -> np.ndarray:
     buf = np.ascontiguousarray(np.asarray(x, dtype=np.float32).copy())
     assert buf.shape == (16,)
     lib().o_fwht16(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), signs)
+    return buf
+
+
+def unfwht32(y, signs: int) -> np.ndarray:
+    """The inverse (transpose) of fwht32: FWHT stages, times 2^-2.5, then the signs."""
+    buf = np.ascontiguousarray(np.asarray(y, dtype=np.float32).copy())
+    assert buf.shape == (32,)
+    lib().o_unfwht32(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), signs)
+    return buf
+
+
+def unfwht16(y, signs: int) -> np.ndarray:
+    """The inverse of fwht16: FWHT stages, times 1/4, then the signs."""
+    buf = np.ascontiguousarray(np.asarray(y, dtype=np.float32).copy())
+    assert buf.shape == (16,)
+    lib().o_unfwht16(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), signs)
     return buf
 
 
@@ -264,6 +287,19 @@ def dequantize_f32(q: dict) -> np.ndarray:
     rc = lib().o_dequantize_f32(np.ascontiguousarray(q["codes"]).ctypes.data,
                                 np.ascontiguousarray(q["scales"]).ctypes.data,
                                 q["rows"], q["cols"], q["fmt"], q["sg"], out.ctypes.data)
+    assert rc == 0
+    return out
+
+
+def dequantize_unrotated_f32(q: dict, had_signs: int) -> np.ndarray:
+    """dequantize_f32 followed by the inverse of the quantization's block
+    rotation (16-wide for NVFP4, 32-wide for MXFP4) with the same sign mask:
+    the values read back in the tensor's own domain (quantized orientation)."""
+    out = np.zeros((q["rows"], q["cols"]), dtype=np.float32)
+    rc = lib().o_dequantize_unrotated_f32(np.ascontiguousarray(q["codes"]).ctypes.data,
+                                          np.ascontiguousarray(q["scales"]).ctypes.data,
+                                          q["rows"], q["cols"], q["fmt"], q["sg"], had_signs,
+                                          out.ctypes.data)
     assert rc == 0
     return out
 

@@ -414,10 +414,11 @@ DEQ_BAD = [
 
 
 @pytest.mark.parametrize("case", DEQ_BAD)
-def test_dequantize_rejects_bad_arguments(fp4, case):
+@pytest.mark.parametrize("entry", ["fp4_dequantize", "fp4_dequantize_unrotated"])
+def test_dequantize_rejects_bad_arguments(fp4, case, entry):
     over, dt, dst, ld, want = case
     q = _t(fp4, **over)
-    assert fp4.lib().fp4_dequantize(ctypes.byref(q), dt, dst, ld, None) == want
+    assert getattr(fp4.lib(), entry)(ctypes.byref(q), dt, dst, ld, None) == want
 
 
 def test_amax_rejects_bad_arguments(fp4):

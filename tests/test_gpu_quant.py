@@ -147,6 +147,45 @@ def test_dequantize_matches_oracle(fp4, orc, fmt, bf16out):
         assert np.array_equal(to_host(y), want)
 
 
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("bf16out", [False, True])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_dequantize_unrotated_matches_oracle(fp4, orc, fmt, bf16out, axis):
+    """fp4_dequantize_unrotated of a rotated quantization (MXFP4 32-wide,
+    NVFP4 16-wide; either axis, the blocks lying along the quantized
+    orientation's rows): bit-equal to the oracle's dequantization followed by
+    its inverse rotation, bf16 rounded once at the end; without a rotation it
+    equals fp4_dequantize."""
+    import torch
+    xh = _mixed((96, 1056), 6)
+    signs = orc.hadamard_signs(21)
+    say("dequantize unrotated fmt", fmt, "axis", axis, "bf16", bf16out)
+    qo = orc.quantize(xh, axis=axis, fmt=fmt, had_on=True, had_signs=signs)
+    q = q_from_oracle(qo, had_signs=signs)
+    dt = torch.bfloat16 if bf16out else torch.float32
+    y = to_host(fp4.dequantize(q, dtype=dt, unrotate=True))
+    want = orc.dequantize_unrotated_f32(qo, signs)
+    assert np.array_equal(y, orc.f32_to_bf16_bits(want) if bf16out else want)
+    qo0 = orc.quantize(xh, axis=axis, fmt=fmt)
+    q0 = q_from_oracle(qo0)
+    iv = torch.int16 if bf16out else torch.int32
+    assert torch.equal(fp4.dequantize(q0, dtype=dt, unrotate=True).view(iv), fp4.dequantize(q0, dtype=dt).view(iv))
+
+
+def test_dequantize_unrotated_strided_output(fp4, orc):
+    """Into rows of ld = cols + 8 (16-byte aligned): the padding stays untouched."""
+    import torch
+    xh = _mixed((40, 256), 7)
+    signs = orc.hadamard_signs(22)
+    qo = orc.quantize(xh, fmt=1, had_on=True, had_signs=signs)
+    q = q_from_oracle(qo, had_signs=signs)
+    full = torch.full((40, 264), 5.0, dtype=torch.float32, device="cuda")
+    fp4.fp4_dequantize_unrotated(q, full[:, :256])
+    yh = to_host(full)
+    assert (yh[:, 256:] == 5.0).all()
+    assert np.array_equal(yh[:, :256], orc.dequantize_unrotated_f32(qo, signs))
+
 # ------------------------------------------------ both orientations in one read
 DUAL = []
 for fmt in (0, 1):

@@ -358,6 +358,58 @@ def test_fwht16_inverse_is_exact(orc):
                           rtol=1e-12)
 
 
+
+def test_unfwht_is_the_transposed_rotation(orc):
+    """unfwht = D H c, the transpose of c H D: on integer inputs every
+    butterfly is exact, so the result is the integer product H y, rounded once
+    by the product with c, then signed (a dropped sign, a wrong stage or the
+    signs applied before H fail this)."""
+    from scipy.linalg import hadamard
+    c = np.float32(2.0 ** -2.5)
+    for n, fn, k in ((32, orc.unfwht32, c), (16, orc.unfwht16, np.float32(0.25))):
+        H = hadamard(n).astype(np.int64)
+        rng = np.random.default_rng(40 + n)
+        for trial in range(200):
+            signs = int(rng.integers(0, 2 ** 32))
+            y = rng.integers(-(2 ** 18), 2 ** 18, n).astype(np.int64)
+            D = np.array([-1 if (signs >> j) & 1 else 1 for j in range(n)], dtype=np.float32)
+            expect = (H @ y).astype(np.float32) * k * D
+            assert np.array_equal(fn(y.astype(np.float32), signs), expect), (n, trial)
+
+
+def test_unfwht_undoes_the_rotation(orc):
+    rng = np.random.default_rng(42)
+    for _ in range(100):
+        signs = int(rng.integers(0, 2 ** 32))
+        x = rng.standard_normal(32).astype(np.float32)
+        back = orc.unfwht32(orc.fwht32(x, signs), signs).astype(np.float64)
+        # two FP32 transforms of a norm-preserving map (c rounded to FP32)
+        assert np.max(np.abs(back - x)) <= 1e-5 * np.linalg.norm(x.astype(np.float64))
+        x16 = rng.integers(-(2 ** 12), 2 ** 12, 16).astype(np.float32)
+        assert np.array_equal(orc.unfwht16(orc.fwht16(x16, signs), signs), x16)   # exact
+
+
+def test_dequantize_unrotated(orc):
+    """Read back in the source's domain: each block is the inverse rotation of
+    the plain dequantization's block, and the result approximates the source
+    as closely as the rotated dequantization approximates the rotated source
+    (an orthonormal map keeps the error's norm)."""
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((48, 256)).astype(np.float32)
+    for fmt, B, fn, fwd in ((1, 32, orc.unfwht32, orc.fwht32), (0, 16, orc.unfwht16, orc.fwht16)):
+        signs = orc.hadamard_signs(11)
+        q = orc.quantize(x, fmt=fmt, had_on=True, had_signs=signs)
+        rot = orc.dequantize_f32(q)
+        got = orc.dequantize_unrotated_f32(q, signs)
+        for r in (0, 17, 47):
+            for c0 in range(0, 256, B):
+                assert np.array_equal(got[r, c0:c0 + B], fn(rot[r, c0:c0 + B], signs))
+        xr = np.stack([np.concatenate([fwd(x[r, c0:c0 + B], signs) for c0 in range(0, 256, B)])
+                       for r in range(48)]).astype(np.float64)
+        e_rot = np.linalg.norm(rot.astype(np.float64) - xr)
+        e_src = np.linalg.norm(got.astype(np.float64) - x.astype(np.float64))
+        assert abs(e_src - e_rot) <= 1e-4 * np.linalg.norm(x.astype(np.float64)), (fmt, e_src, e_rot)
+
 def test_hadamard_mask_is_a_separate_philox_counter(orc):
     # word 0 of counter (0,0,0,1), which the element stream (c2 = c3 = 0) never uses
     for seed in (0, 1, 3, 2 ** 40 + 5):
