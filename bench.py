@@ -27,6 +27,9 @@ on the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded
 sample of the same step and scales it to the same unit.
 `large_step` times the large-layer step the same way (hidden 8192, MLP 28672,
 16384 tokens: NVFP4 fwd + bwd, RTN forward, SR on the backward operands).
+`dp8_shard_step` times the NVFP4 step on one GPU's share of 8-way data
+parallelism over the Llama-7B layer's tokens (4096 tokens: X [4096, 4096],
+dY [4096, 11008], W whole), the shape each GPU would run.
 `measured_ceilings` puts what the chip reaches on this machine beside the
 data-sheet peaks: loops of the two MFMA instructions the GEMMs issue, and
 streaming passes (read only, copy, and a quantize-like 4:1 read:write pass)
@@ -47,7 +50,7 @@ if ROOT not in sys.path:
 TOKENS, D_IN, D_OUT = 32768, 4096, 11008
 GEMM_FLOP = 2.0 * TOKENS * D_IN * D_OUT          # each of fwd, dgrad, wgrad
 L_TOKENS, L_IN, L_OUT = 16384, 8192, 28672       # the large layer
-L_GEMM_FLOP = 2.0 * L_TOKENS * L_IN * L_OUT
+SHARD_TOKENS = TOKENS // 8                       # one GPU's share of 8-way data parallelism
 PEAK_F16_TFLOPS = 2500.0                         # dense MFMA, MI355X
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
@@ -187,18 +190,20 @@ def make_extras(fp4, X, W, dY, signs16):
     return ops, q
 
 
-def make_large_step(fp4, X, W, dY):
-    """The large layer's NVFP4 step: each tensor's amax pass and one fused
-    pass for both of its orientations (X, W: RTN along K + SR along the other
-    axis; dY: SR along both), then the three GEMMs (fwd bf16 out, dgrad and
-    wgrad fp32 out)."""
+def make_large_step(fp4, X, W, dY, cfg=4):
+    """The NVFP4 step of a layer (the large layer's, or a shard's): each
+    tensor's amax pass and one fused pass for both of its orientations (X, W:
+    RTN along K + SR along the other axis; dY: SR along both), then the three
+    GEMMs (fwd bf16 out, dgrad and wgrad fp32 out). Shapes from the tensors;
+    SR seeds (cfg << 8) | role."""
     import torch
 
-    T, I, O = L_TOKENS, L_IN, L_OUT
+    (T, I), O = X.shape, W.shape[0]
+    gf = 2.0 * T * I * O
     Q = fp4.QTensor
     NV = fp4.FP4_NVFP4
     RTN, SR = fp4.FP4_RTN, fp4.FP4_SR
-    seed = lambda role: (4 << 8) | role
+    seed = lambda role: (cfg << 8) | role
     q = {"X": Q(T, I, NV), "Xt": Q(I, T, NV), "W": Q(O, I, NV), "Wt": Q(I, O, NV),
          "dY": Q(T, O, NV), "dYt": Q(O, T, NV)}
     for a, b in (("Xt", "X"), ("Wt", "W"), ("dYt", "dY")):
@@ -206,17 +211,19 @@ def make_large_step(fp4, X, W, dY):
     outs = {"Y": torch.empty((T, O), dtype=torch.bfloat16, device="cuda"),
             "dX": torch.empty((T, I), dtype=torch.float32, device="cuda"),
             "dW": torch.empty((O, I), dtype=torch.float32, device="cuda")}
+    ws = {"fwd": gemm_workspace(fp4, q["X"], q["W"]), "dgrad": gemm_workspace(fp4, q["dY"], q["Wt"]),
+          "wgrad": gemm_workspace(fp4, q["dYt"], q["Xt"])}
     dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
     ops = [
         ("quant X nv dual (rtn K, sr tokens)", "q", lambda: dual(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
          algorithmic_bytes(T * I, 2, 16, True, 2)),
         ("quant W nv dual (rtn K, sr out)", "q", lambda: dual(W, RTN, 0, SR, seed(4), q["W"], q["Wt"]),
          algorithmic_bytes(O * I, 2, 16, True, 2)),
-        ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"]), L_GEMM_FLOP),
+        ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"], ws["fwd"]), gf),
         ("quant dY nv dual (sr both)", "q", lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
          algorithmic_bytes(T * O, 2, 16, True, 2)),
-        ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"]), L_GEMM_FLOP),
-        ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"]), L_GEMM_FLOP),
+        ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"], ws["dgrad"]), gf),
+        ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"], ws["wgrad"]), gf),
     ]
     return ops, outs, q
 
@@ -255,31 +262,59 @@ def large_step_record(fp4, steps, warmup):
     X = workloads.device_tensor("large", "X")
     W = workloads.device_tensor("large", "W")
     dY = workloads.device_tensor("large", "dY")
-    ops, outs, q = make_large_step(fp4, X, W, dY)
+    rec = nv_step_record(fp4, X, W, dY, 4, steps, warmup)
+    del X, W, dY
+    torch.cuda.empty_cache()
+    return {
+        "workload": ("large-layer step: hidden 8192, MLP 28672, 16384 tokens; NVFP4 amax + one fused "
+                     "quantize pass per tensor (RTN fwd, SR bwd), fwd (bf16 out), dgrad and wgrad (fp32 out)"),
+        **rec,
+        "targets": {
+            "quantize_ms": 1.067,     # 5976.9 MB of separate passes at 70% of 8 TB/s
+            "gemm_nv_ms_at_60pct_f16_peak": 5.097,
+            "gemm_ms_at_60pct_fp4_peak": 1.274,
+        },
+    }
+
+
+def shard_step_record(fp4, X, W, dY, steps, warmup):
+    """Time the NVFP4 step on one GPU's share of 8-way data parallelism over
+    the Llama-7B layer's tokens (the rows of X and dY, W whole)."""
+    import torch
+
+    rec = nv_step_record(fp4, X, W, dY, 5, steps, warmup)
+    torch.cuda.empty_cache()
+    return {
+        "workload": (f"one GPU's share of 8-way data parallelism over the Llama-7B layer: {X.shape[0]} "
+                     f"tokens, X [{X.shape[0]}, {X.shape[1]}], W [{W.shape[0]}, {W.shape[1]}], dY "
+                     f"[{dY.shape[0]}, {dY.shape[1]}]; NVFP4 amax + one fused quantize pass per tensor (RTN "
+                     "fwd, SR bwd), fwd (bf16 out), dgrad and wgrad (fp32 out); the tensor amaxes would be "
+                     "all-reduced (4 bytes each) and dW all-reduced across the 8 GPUs, not done here"),
+        **rec,
+    }
+
+
+def nv_step_record(fp4, X, W, dY, cfg, steps, warmup):
+    import torch
+
+    ops, outs, q = make_large_step(fp4, X, W, dY, cfg)
     torch.cuda.synchronize()
     ms, per_op = run_step(ops, steps, warmup)
     gemms = [r for r, o in zip(per_op, ops) if o[1] == "g_nv"]
     quant = [(r, o) for r, o in zip(per_op, ops) if o[1] == "q"]
     q_ms = sum(r["avg_ms"] for r, _ in quant)
     q_bytes = sum(o[3] for _, o in quant)
-    del X, W, dY, ops, outs, q
-    torch.cuda.empty_cache()
+    gf = 2.0 * X.shape[0] * X.shape[1] * W.shape[0]
+    del ops, outs, q
     return {
-        "workload": ("large-layer step: hidden 8192, MLP 28672, 16384 tokens; NVFP4 amax + one fused "
-                     "quantize pass per tensor (RTN fwd, SR bwd), fwd (bf16 out), dgrad and wgrad (fp32 out)"),
         "ms_per_step": round(ms, 3),
-        "TFLOPs": round(3 * L_GEMM_FLOP / (ms * 1e-3) / 1e12, 1),
+        "TFLOPs": round(3 * gf / (ms * 1e-3) / 1e12, 1),
         "gemm_avg_ms": round(sum(r["avg_ms"] for r in gemms) / len(gemms), 4),
         "gemm_frac_f16_peak": round(sum(r["frac_f16_peak"] for r in gemms) / len(gemms), 4),
         "gemm_frac_fp4_peak": round(sum(r["frac_fp4_peak"] for r in gemms) / len(gemms), 4),
         "quantize_ms": round(q_ms, 4),
         "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "quantize_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
-        "targets": {
-            "quantize_ms": 1.067,     # 5976.9 MB of separate passes at 70% of 8 TB/s
-            "gemm_nv_ms_at_60pct_f16_peak": 5.097,
-            "gemm_ms_at_60pct_fp4_peak": 1.274,
-        },
         "per_op": per_op,
     }
 
@@ -524,6 +559,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large-step", action="store_true",
                     help="skip the large layer's step (timed after the Llama-7B step)")
+    ap.add_argument("--no-shard-step", action="store_true",
+                    help="skip the 8-way data-parallel shard's step (timed after the large layer's)")
     ap.add_argument("--separate-passes", action="store_true",
                     help="quantize each orientation with its own pass instead of one read per tensor")
     args = ap.parse_args()
@@ -635,10 +672,17 @@ def main():
     host = None
     if not args.no_cpu_baseline:
         host = {k: to_host_bits(v) for k, v in (("X", X), ("W", W), ("dY", dY))}
+    shard = None
+    if not args.no_shard_step:
+        shard = (X[:SHARD_TOKENS].clone(), W, dY[:SHARD_TOKENS].clone())
     del X, W, dY, ops, outs, q
     torch.cuda.empty_cache()
     if not args.no_large_step:
         out["large_step"] = large_step_record(fp4, args.steps, args.warmup)
+    if shard is not None:
+        out["dp8_shard_step"] = shard_step_record(fp4, *shard, args.steps, args.warmup)
+        del shard
+        torch.cuda.empty_cache()
     if host is not None:
         out["cpu_baseline"] = cpu_baseline(host)
     print(json.dumps(out), flush=True)

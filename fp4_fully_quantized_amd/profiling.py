@@ -102,14 +102,14 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
              "-d OUT/pmc_fetch -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
-             "--no-large-step",
+             "--no-large-step --no-shard-step",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
              "-d OUT/pmc_write -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
-             "--no-large-step",
+             "--no-large-step --no-shard-step",
     "util": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA "
             "GRBM_GUI_ACTIVE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
             "-d OUT/pmc_util -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
-            "--no-large-step",
+            "--no-large-step --no-shard-step",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o copy -- "
                   "python3 -m fp4_fully_quantized_amd.profiling copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o copy -- "
@@ -274,31 +274,81 @@ LARGE_GROUPS = [
 ]
 
 
+def _split_after_steps(dispatches, per_step: int):
+    """(the dispatches up to the last library dispatch of WARMUP + STEPS steps
+    of `per_step` library dispatches each, the rest)."""
+    import re
+
+    lib = re.compile(r"^k_(amax|quant|gemm|split)")
+    need, seen = per_step * (WARMUP + STEPS), 0
+    for i, (name, _) in enumerate(dispatches):
+        if lib.search(name):
+            seen += 1
+            if seen == need:
+                return dispatches[:i + 1], dispatches[i + 1:]
+    return dispatches, []
+
+
+def _write_nv_step(dispatches, groups, pair_label, dgrad_label, wgrad_label, title, intro, path):
+    """Kernel-time table of an NVFP4 step (amax + dual passes + three GEMMs);
+    dgrad and wgrad run the same kernel and are told apart by launch order."""
+    g = _group(dispatches, groups)
+    d = g.pop(pair_label)
+    g[dgrad_label] = d[0::2]
+    g[wgrad_label] = d[1::2]
+    with open(path, "w") as f:
+        f.write("\n".join([f"# {title}", ""] + intro + [""] + _stats_lines(g) + [""]))
+
+
+def _command_lines(command):
+    return ["Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; "
+            "`OUT` = the folder the run writes its CSV files to):", "", "```", command, "```", ""]
+
+
 def _write_large_step(dispatches, command, profiles_dir):
     import os
 
-    groups = _group(dispatches, LARGE_GROUPS)
-    # The X and W dual passes share a kernel; split dgrad / wgrad by launch order.
-    g = groups.pop("NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)")
-    groups["NVFP4 GEMM dgrad 16384x8192x28672 (fp32 out)"] = g[0::2]
-    groups["NVFP4 GEMM wgrad 28672x8192x16384 (fp32 out)"] = g[1::2]
-    lines = [
-        "# Kernel time of the large layer's step (bench.py `large_step`)",
-        "",
-        "Command (run from the repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; "
-        "`OUT` = the folder the run writes its CSV files to):",
-        "",
-        "```", command, "```",
-        "",
+    intro = _command_lines(command) + [
         f"The large layer: hidden {L_IN}, MLP {L_OUT}, {L_TOKENS} tokens. One step = for each of X, W and dY "
         "an amax pass and one pass that quantizes both orientations (NVFP4; X and W: RTN along K, SR along "
         "the other axis; dY: SR along both), the fwd GEMM (bf16 out), dgrad and wgrad (fp32 out); "
         f"{WARMUP} warm-up + {STEPS} timed steps, after the rest of the run. `avg us (timed)` leaves out the "
         "warm-up steps. X's and W's dual passes run the same kernel (the group holds both).",
-        "",
-    ] + _stats_lines(groups) + [""]
-    with open(os.path.join(profiles_dir, "large_layer_step_kernel_stats.md"), "w") as f:
-        f.write("\n".join(lines))
+    ]
+    _write_nv_step(dispatches, LARGE_GROUPS,
+                   "NVFP4 GEMM dgrad 16384x8192x28672 / wgrad 28672x8192x16384 (fp32 out)",
+                   "NVFP4 GEMM dgrad 16384x8192x28672 (fp32 out)", "NVFP4 GEMM wgrad 28672x8192x16384 (fp32 out)",
+                   "Kernel time of the large layer's step (bench.py `large_step`)", intro,
+                   os.path.join(profiles_dir, "large_layer_step_kernel_stats.md"))
+
+
+# One GPU's share of 8-way data parallelism over the Llama-7B layer's tokens.
+S_TOKENS = TOKENS // 8
+SHARD_GROUPS = [
+    ("tensor amax (X, W, dY)", r"^k_amax(_flat)?<"),
+    ("quantize X and W, both orientations (RTN along K, SR along the other axis)", r"^k_quant_dual<0, 0, 1,"),
+    ("quantize dY, both orientations (SR)", r"^k_quant_dual<0, 1, 1,"),
+    (f"NVFP4 GEMM fwd {S_TOKENS}x{D_OUT}x{D_IN} (bf16 out)", r"^k_gemm<0, 256, true, false>"),
+    (f"NVFP4 GEMM dgrad {S_TOKENS}x{D_IN}x{D_OUT} / wgrad {D_OUT}x{D_IN}x{S_TOKENS} (fp32 out)",
+     r"^k_gemm<0, 256, false, false>"),
+]
+
+
+def _write_shard_step(dispatches, command, profiles_dir):
+    import os
+
+    intro = _command_lines(command) + [
+        f"One GPU's share of 8-way data parallelism over the Llama-7B layer's tokens: X [{S_TOKENS}, {D_IN}], "
+        f"dY [{S_TOKENS}, {D_OUT}], W [{D_OUT}, {D_IN}] whole (bench.py `dp8_shard_step`, timed after the "
+        "large layer's step). One step = amax + one dual pass for each of X, W and dY (RTN along K, SR on the "
+        f"backward orientations), the fwd GEMM (bf16 out), dgrad and wgrad (fp32 out); {WARMUP} warm-up + "
+        f"{STEPS} timed steps. `avg us (timed)` leaves out the warm-up steps.",
+    ]
+    _write_nv_step(dispatches, SHARD_GROUPS, SHARD_GROUPS[-1][0],
+                   f"NVFP4 GEMM dgrad {S_TOKENS}x{D_IN}x{D_OUT} (fp32 out)",
+                   f"NVFP4 GEMM wgrad {D_OUT}x{D_IN}x{S_TOKENS} (fp32 out)",
+                   "Kernel time of one 8-way data-parallel shard's step (bench.py `dp8_shard_step`)", intro,
+                   os.path.join(profiles_dir, "dp8_shard_step_kernel_stats.md"))
 
 
 def _write_ceilings(dispatches, command, profiles_dir):
@@ -365,7 +415,8 @@ def summarize_trace(out_dir: str, profiles_dir: str) -> None:
         "2 + 10 calls each, and a 1 GiB device copy (`__amd_rocclr_copyBuffer`, 13 launches) that measures "
         "the copy bandwidth; the other torch kernels are the one-time input generation. The same run then "
         "measures the chip's ceilings (`chip_ceilings_kernel_stats.md`) and times the large layer's step "
-        "(`large_layer_step_kernel_stats.md`); this table covers the dispatches before those.",
+        "(`large_layer_step_kernel_stats.md`) and an 8-way data-parallel shard's step "
+        "(`dp8_shard_step_kernel_stats.md`); this table covers the dispatches before those.",
         "",
         "`avg us (timed)` (GEMMs, which only the step launches) leaves out the warm-up steps' launches (the "
         "first launches of a run are slower while the clock settles); that is the figure to set against the "
@@ -393,8 +444,11 @@ def summarize_trace(out_dir: str, profiles_dir: str) -> None:
     lines += ["", "## Per kernel over the whole run (`--stats` summary)", "", kernel_stats_table(stats_csv), ""]
     with open(os.path.join(profiles_dir, "llama7b_step_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines))
+    large, shard = _split_after_steps(large, 9)
     if large:
         _write_large_step(large, cmd("stats"), profiles_dir)
+    if shard:
+        _write_shard_step(shard, cmd("stats"), profiles_dir)
     if ceil:
         _write_ceilings(ceil, cmd("stats"), profiles_dir)
 

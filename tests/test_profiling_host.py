@@ -158,6 +158,29 @@ def test_trace_split_into_llama_ceilings_and_large_step(tmp_path):
     assert "| f16 MFMA loop" in (prof / "chip_ceilings_kernel_stats.md").read_text()
 
 
+def test_trace_tail_split_into_large_and_shard_steps(tmp_path):
+    """After the ceilings: the large layer's step (9 library dispatches a
+    step), then the data-parallel shard's step; each gets its own table."""
+    large = _large_names(p.STEPS, p.WARMUP)
+    tail = ["fill"] + large + ["copy", "copy"] + large
+    trace = []
+    for k, n in enumerate(tail):
+        shard = k > len(large) + 2
+        d = 1000 if not n.startswith("k_gemm") else (500_000 if shard else 5_000_000)
+        trace.append((n, d))
+    big, shard = p._split_after_steps(trace, 9)
+    assert len(big) == len(large) + 1 and len(shard) == len(large) + 2
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    p._write_shard_step(shard, "CMD", str(prof))
+    text = (prof / "dp8_shard_step_kernel_stats.md").read_text()
+    assert "| NVFP4 GEMM fwd 4096x11008x4096 (bf16 out) | 13 | 500.0 | 500.0 |" in text
+    assert "| NVFP4 GEMM dgrad 4096x4096x11008 (fp32 out) | 13 | 500.0 |" in text
+    assert "| NVFP4 GEMM wgrad 11008x4096x4096 (fp32 out) | 13 | 500.0 |" in text
+    # a run without the shard step leaves nothing after the large step
+    assert p._split_after_steps(trace[:len(large) + 1], 9)[1] == []
+
+
 def test_code_digest_ignores_comments_only():
     from fp4_fully_quantized_amd.profiling import code_digest
     a = "int f(int x) {\n  return x + 1;  // one more\n}\n"
