@@ -29,7 +29,8 @@ sample of the same step and scales it to the same unit.
 16384 tokens: NVFP4 fwd + bwd, RTN forward, SR on the backward operands).
 `dp8_shard_step` times the NVFP4 step on one GPU's share of 8-way data
 parallelism over the Llama-7B layer's tokens (4096 tokens: X [4096, 4096],
-dY [4096, 11008], W whole), the shape each GPU would run.
+dY [4096, 11008], W whole), the shape each GPU would run, X and dY quantized
+with the whole batch's SR indices (tokens 12288 .. 16383).
 `measured_ceilings` puts what the chip reaches on this machine beside the
 data-sheet peaks: loops of the two MFMA instructions the GEMMs issue, and
 streaming passes (read only, copy, and a quantize-like 4:1 read:write pass)
@@ -51,6 +52,7 @@ TOKENS, D_IN, D_OUT = 32768, 4096, 11008
 GEMM_FLOP = 2.0 * TOKENS * D_IN * D_OUT          # each of fwd, dgrad, wgrad
 L_TOKENS, L_IN, L_OUT = 16384, 8192, 28672       # the large layer
 SHARD_TOKENS = TOKENS // 8                       # one GPU's share of 8-way data parallelism
+SHARD_RANK = 3                                   # the share timed: tokens 12288 .. 16383
 PEAK_F16_TFLOPS = 2500.0                         # dense MFMA, MI355X
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
@@ -190,12 +192,14 @@ def make_extras(fp4, X, W, dY, signs16):
     return ops, q
 
 
-def make_large_step(fp4, X, W, dY, cfg=4):
+def make_large_step(fp4, X, W, dY, cfg=4, shard=None):
     """The NVFP4 step of a layer (the large layer's, or a shard's): each
     tensor's amax pass and one fused pass for both of its orientations (X, W:
     RTN along K + SR along the other axis; dY: SR along both), then the three
     GEMMs (fwd bf16 out, dgrad and wgrad fp32 out). Shapes from the tensors;
-    SR seeds (cfg << 8) | role."""
+    SR seeds (cfg << 8) | role. `shard` = (row_offset, rows_total): X and dY
+    are rows row_offset .. of the whole token batch, quantized with the whole
+    batch's SR indices (fp4_quantize_dual_shard)."""
     import torch
 
     (T, I), O = X.shape, W.shape[0]
@@ -214,13 +218,17 @@ def make_large_step(fp4, X, W, dY, cfg=4):
     ws = {"fwd": gemm_workspace(fp4, q["X"], q["W"]), "dgrad": gemm_workspace(fp4, q["dY"], q["Wt"]),
           "wgrad": gemm_workspace(fp4, q["dYt"], q["Xt"])}
     dual = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual(src, rc, sc, 0, rr, sr, 0, False, qc, qr)
+    tok = dual
+    if shard is not None:
+        tok = lambda src, rc, sc, rr, sr, qc, qr: fp4.fp4_quantize_dual_shard(src, *shard, rc, sc, 0, rr, sr, 0,
+                                                                              False, qc, qr)
     ops = [
-        ("quant X nv dual (rtn K, sr tokens)", "q", lambda: dual(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
+        ("quant X nv dual (rtn K, sr tokens)", "q", lambda: tok(X, RTN, 0, SR, seed(3), q["X"], q["Xt"]),
          algorithmic_bytes(T * I, 2, 16, True, 2)),
         ("quant W nv dual (rtn K, sr out)", "q", lambda: dual(W, RTN, 0, SR, seed(4), q["W"], q["Wt"]),
          algorithmic_bytes(O * I, 2, 16, True, 2)),
         ("gemm fwd nv", "g_nv", lambda: fp4.fp4_gemm(q["X"], q["W"], outs["Y"], ws["fwd"]), gf),
-        ("quant dY nv dual (sr both)", "q", lambda: dual(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
+        ("quant dY nv dual (sr both)", "q", lambda: tok(dY, SR, seed(1), SR, seed(2), q["dY"], q["dYt"]),
          algorithmic_bytes(T * O, 2, 16, True, 2)),
         ("gemm dgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dY"], q["Wt"], outs["dX"], ws["dgrad"]), gf),
         ("gemm wgrad nv", "g_nv", lambda: fp4.fp4_gemm(q["dYt"], q["Xt"], outs["dW"], ws["wgrad"]), gf),
@@ -277,27 +285,30 @@ def large_step_record(fp4, steps, warmup):
     }
 
 
-def shard_step_record(fp4, X, W, dY, steps, warmup):
+def shard_step_record(fp4, X, W, dY, row_offset, steps, warmup):
     """Time the NVFP4 step on one GPU's share of 8-way data parallelism over
-    the Llama-7B layer's tokens (the rows of X and dY, W whole)."""
+    the Llama-7B layer's tokens (rows row_offset .. of X and dY, W whole; SR
+    indices those of the whole batch)."""
     import torch
 
-    rec = nv_step_record(fp4, X, W, dY, 5, steps, warmup)
+    rec = nv_step_record(fp4, X, W, dY, 5, steps, warmup, shard=(row_offset, TOKENS))
     torch.cuda.empty_cache()
     return {
         "workload": (f"one GPU's share of 8-way data parallelism over the Llama-7B layer: {X.shape[0]} "
                      f"tokens, X [{X.shape[0]}, {X.shape[1]}], W [{W.shape[0]}, {W.shape[1]}], dY "
-                     f"[{dY.shape[0]}, {dY.shape[1]}]; NVFP4 amax + one fused quantize pass per tensor (RTN "
-                     "fwd, SR bwd), fwd (bf16 out), dgrad and wgrad (fp32 out); the tensor amaxes would be "
+                     f"[{dY.shape[0]}, {dY.shape[1]}] (tokens {row_offset} .. {row_offset + X.shape[0] - 1} of "
+                     f"{TOKENS}); NVFP4 amax + one fused quantize pass per tensor (RTN fwd, SR bwd; X and dY "
+                     "with the whole batch's SR indices), fwd (bf16 out), dgrad and wgrad (fp32 out); the "
+                     "tensor amaxes would be "
                      "all-reduced (4 bytes each) and dW all-reduced across the 8 GPUs, not done here"),
         **rec,
     }
 
 
-def nv_step_record(fp4, X, W, dY, cfg, steps, warmup):
+def nv_step_record(fp4, X, W, dY, cfg, steps, warmup, shard=None):
     import torch
 
-    ops, outs, q = make_large_step(fp4, X, W, dY, cfg)
+    ops, outs, q = make_large_step(fp4, X, W, dY, cfg, shard)
     torch.cuda.synchronize()
     ms, per_op = run_step(ops, steps, warmup)
     gemms = [r for r, o in zip(per_op, ops) if o[1] == "g_nv"]
@@ -674,7 +685,8 @@ def main():
         host = {k: to_host_bits(v) for k, v in (("X", X), ("W", W), ("dY", dY))}
     shard = None
     if not args.no_shard_step:
-        shard = (X[:SHARD_TOKENS].clone(), W, dY[:SHARD_TOKENS].clone())
+        r0 = SHARD_RANK * SHARD_TOKENS
+        shard = (X[r0:r0 + SHARD_TOKENS].clone(), W, dY[r0:r0 + SHARD_TOKENS].clone(), r0)
     del X, W, dY, ops, outs, q
     torch.cuda.empty_cache()
     if not args.no_large_step:

@@ -26,7 +26,7 @@ BLOCK = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTS = ["fp4_codes_bytes", "fp4_scales_bytes", "fp4_hadamard_signs", "fp4_status_str",
            "fp4_tensor_amax", "fp4_tensor_amax_hadamard16", "fp4_quantize", "fp4_quantize_dual",
-           "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_noise_ratio", "fp4_quantize_2d",
+           "fp4_quantize_shard", "fp4_quantize_dual_shard", "fp4_quantize_noise", "fp4_quantize_dual_noise", "fp4_noise_ratio", "fp4_quantize_2d",
            "fp4_dequantize", "fp4_dequantize_unrotated", "fp4_gemm_workspace_bytes", "fp4_gemm_splitk_bytes", "fp4_gemm",
            "fp4_gemm_noalloc"]
 # The allocation-free GEMM's workspace limit (FP4_GEMM_NOALLOC_MAX_BYTES).
@@ -88,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.fp4_quantize_dual.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_int64,
                                         c.c_int, c.c_uint64, c.c_uint64, c.c_int, c.c_uint64, c.c_uint64,
                                         c.c_int, c.POINTER(fp4_tensor), c.POINTER(fp4_tensor), c.c_void_p]
+        L.fp4_quantize_shard.restype = c.c_int
+        L.fp4_quantize_shard.argtypes = (L.fp4_quantize.argtypes[:5] + [c.c_int64, c.c_int64]
+                                         + L.fp4_quantize.argtypes[5:])
+        L.fp4_quantize_dual_shard.restype = c.c_int
+        L.fp4_quantize_dual_shard.argtypes = (L.fp4_quantize_dual.argtypes[:5] + [c.c_int64, c.c_int64]
+                                              + L.fp4_quantize_dual.argtypes[5:])
         L.fp4_quantize_noise.restype = c.c_int
         L.fp4_quantize_noise.argtypes = L.fp4_quantize.argtypes[:-1] + [c.c_void_p, c.c_void_p]
         L.fp4_quantize_dual_noise.restype = c.c_int
@@ -293,6 +299,37 @@ def fp4_quantize_dual(src, rnd_cols: int, seed_cols: int, index_offset_cols: int
                                    seed_cols, index_offset_cols, rnd_rows, seed_rows, index_offset_rows,
                                    int(bool(amax_ready)), ctypes.byref(dc), ctypes.byref(dr),
                                    _stream(stream)), "fp4_quantize_dual")
+    out_cols.rows, out_cols.cols = dc.rows, dc.cols
+    out_rows.rows, out_rows.cols = dr.rows, dr.cols
+
+
+def fp4_quantize_shard(src, row_offset: int, rows_total: int, axis: int, rnd: int, seed: int,
+                       index_offset: int, amax_ready: bool, out: QTensor, stream=None) -> None:
+    """fp4_quantize of rows row_offset .. of a rows_total-row tensor, with the
+    whole tensor's stochastic-rounding indices."""
+    _check_matrix(src, "src")
+    _check_quant_out(src, out, axis)
+    R, C = src.shape
+    d = out.desc()
+    _check(lib().fp4_quantize_shard(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), row_offset,
+                                    rows_total, axis, rnd, seed, index_offset, int(bool(amax_ready)),
+                                    ctypes.byref(d), _stream(stream)), "fp4_quantize_shard")
+    out.rows, out.cols = d.rows, d.cols
+
+
+def fp4_quantize_dual_shard(src, row_offset: int, rows_total: int, rnd_cols: int, seed_cols: int,
+                            index_offset_cols: int, rnd_rows: int, seed_rows: int, index_offset_rows: int,
+                            amax_ready: bool, out_cols: QTensor, out_rows: QTensor, stream=None) -> None:
+    """fp4_quantize_dual of a row shard, with the whole tensor's stochastic-rounding indices."""
+    _check_matrix(src, "src")
+    _check_quant_out(src, out_cols, FP4_AXIS_COLS, "out_cols")
+    _check_quant_out(src, out_rows, FP4_AXIS_ROWS, "out_rows")
+    R, C = src.shape
+    dc, dr = out_cols.desc(), out_rows.desc()
+    _check(lib().fp4_quantize_dual_shard(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), row_offset,
+                                         rows_total, rnd_cols, seed_cols, index_offset_cols, rnd_rows,
+                                         seed_rows, index_offset_rows, int(bool(amax_ready)), ctypes.byref(dc),
+                                         ctypes.byref(dr), _stream(stream)), "fp4_quantize_dual_shard")
     out_cols.rows, out_cols.cols = dc.rows, dc.cols
     out_rows.rows, out_rows.cols = dr.rows, dr.cols
 

@@ -9,6 +9,8 @@
 
 #include "fp4_internal.hpp"
 
+#include <cstdint>
+
 // Workspace of fp4_gemm_noalloc: a device array each GPU holds from the
 // library's load until the process ends. Host code never uses this name as a
 // device address (on the host it is a stand-in); it uses the address
@@ -66,9 +68,10 @@ fp4_status check_quant(const void* src, fp4_dtype src_t, int64_t R, int64_t C, i
 }
 
 // Enqueue a quantization that check_quant accepted.
+// idx_rows: the row count of the ROWS orientation's SR index (0: R).
 fp4_status launch_quant(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld, fp4_axis axis,
                         fp4_rounding rnd, uint64_t seed, uint64_t index_offset, int amax_ready,
-                        fp4_tensor* out, double* noise, hipStream_t s) {
+                        fp4_tensor* out, double* noise, hipStream_t s, int64_t idx_rows = 0) {
   const bool nv = out->fmt == FP4_NVFP4;
   if (nv && !amax_ready) {
     if (out->had_on)
@@ -90,6 +93,7 @@ fp4_status launch_quant(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
   a.sr = rnd == FP4_SR;
   a.seed = seed;
   a.offset = index_offset;
+  a.idx_rows = idx_rows;
   a.had_on = out->had_on != 0;
   a.signs = out->had_signs;
   a.codes = out->codes;
@@ -110,6 +114,21 @@ fp4_status quantize_impl(const void* src, fp4_dtype src_t, int64_t R, int64_t C,
   if (st != FP4_OK) return st;
   return launch_quant(src, src_t, R, C, ld, axis, rnd, seed, index_offset, amax_ready, out, noise,
                       reinterpret_cast<hipStream_t>(stream));
+}
+
+// A row shard (rows row_offset .. row_offset + R - 1 of a rows_total-row
+// tensor): every check that depends on where the shard lies. Blocks along
+// rows (axis ROWS, or the dual's second orientation) must not straddle
+// shards; the ROWS index c * rows_total + row must keep 8-element Philox
+// calls aligned.
+fp4_status check_shard(int64_t R, int64_t C, int64_t row_offset, int64_t rows_total, bool blocks_along_rows,
+                       int B) {
+  if (row_offset < 0 || rows_total <= 0 || R <= 0 || C <= 0) return FP4_ERR_SHAPE;
+  if (row_offset > rows_total || R > rows_total - row_offset) return FP4_ERR_SHAPE;
+  if (rows_total > INT64_MAX / C) return FP4_ERR_SHAPE;
+  if (rows_total % 8 != 0) return FP4_ERR_ALIGN;
+  if (blocks_along_rows && row_offset % B != 0) return FP4_ERR_ALIGN;
+  return FP4_OK;
 }
 
 // ---------------------------------------------------------------- GEMM operands
@@ -243,7 +262,8 @@ fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64
                               fp4_rounding rnd_cols, uint64_t seed_cols, uint64_t index_offset_cols,
                               fp4_rounding rnd_rows, uint64_t seed_rows, uint64_t index_offset_rows,
                               int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
-                              double* noise_cols, double* noise_rows, fp4_stream_t stream) {
+                              double* noise_cols, double* noise_rows, fp4_stream_t stream,
+                              int64_t idx_rows = 0) {
   if (!out_cols || !out_rows) return FP4_ERR_NULL;
   fp4_status st = check_matrix(src, src_t, R, C, ld);
   if (st != FP4_OK) return st;
@@ -295,6 +315,7 @@ fp4_status quantize_dual_impl(const void* src, fp4_dtype src_t, int64_t R, int64
   a.offset_c = index_offset_cols;
   a.seed_r = seed_rows;
   a.offset_r = index_offset_rows;
+  a.idx_rows_r = idx_rows;
   a.signs_c = out_cols->had_signs;
   a.signs_r = out_rows->had_signs;
   a.codes_c = out_cols->codes;
@@ -477,6 +498,39 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream) {
   return quantize_impl(src, src_t, R, C, ld, axis, rnd, seed, index_offset, amax_ready, out, nullptr,
                        stream);
+}
+
+fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                              int64_t row_offset, int64_t rows_total, fp4_axis axis, fp4_rounding rnd,
+                              uint64_t seed, uint64_t index_offset, int amax_ready, fp4_tensor* out,
+                              fp4_stream_t stream) {
+  if (!out) return FP4_ERR_NULL;
+  if (!valid_fmt(out->fmt)) return FP4_ERR_ARG;
+  if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
+  fp4_status st = check_shard(R, C, row_offset, rows_total, axis == FP4_AXIS_ROWS, block_of(out->fmt));
+  if (st != FP4_OK) return st;
+  // COLS: (row_offset + r) * C + c; ROWS: c * rows_total + row_offset + r.
+  const uint64_t off = index_offset + (axis == FP4_AXIS_COLS ? (uint64_t)row_offset * (uint64_t)C
+                                                             : (uint64_t)row_offset);
+  st = check_quant(src, src_t, R, C, ld, axis, rnd, off, out);
+  if (st != FP4_OK) return st;
+  return launch_quant(src, src_t, R, C, ld, axis, rnd, seed, off, amax_ready, out, nullptr,
+                      reinterpret_cast<hipStream_t>(stream), rows_total);
+}
+
+fp4_status fp4_quantize_dual_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                                   int64_t row_offset, int64_t rows_total, fp4_rounding rnd_cols,
+                                   uint64_t seed_cols, uint64_t index_offset_cols, fp4_rounding rnd_rows,
+                                   uint64_t seed_rows, uint64_t index_offset_rows, int amax_ready,
+                                   fp4_tensor* out_cols, fp4_tensor* out_rows, fp4_stream_t stream) {
+  if (!out_cols) return FP4_ERR_NULL;
+  if (!valid_fmt(out_cols->fmt)) return FP4_ERR_ARG;
+  const fp4_status st = check_shard(R, C, row_offset, rows_total, true, block_of(out_cols->fmt));
+  if (st != FP4_OK) return st;
+  return quantize_dual_impl(src, src_t, R, C, ld, rnd_cols, seed_cols,
+                            index_offset_cols + (uint64_t)row_offset * (uint64_t)C, rnd_rows, seed_rows,
+                            index_offset_rows + (uint64_t)row_offset, amax_ready, out_cols, out_rows, nullptr,
+                            nullptr, stream, rows_total);
 }
 
 fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,

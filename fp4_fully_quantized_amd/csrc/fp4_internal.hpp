@@ -12,6 +12,10 @@ struct QuantArgs {
   int fmt;               // 0 NVFP4, 1 MXFP4
   bool sr;
   uint64_t seed, offset;
+  // SR element index along rows_axis: c * idx_rows + r + offset (0: R). A row
+  // shard of a taller tensor passes the tensor's row count and puts its first
+  // row in offset, so its draws are those of the whole tensor's quantization.
+  int64_t idx_rows;
   bool had_on;
   uint32_t signs;
   uint8_t* codes;
@@ -31,6 +35,7 @@ struct DualArgs {
   bool had_c, had_r;               // rotation of each orientation
   bool sr_c, sr_r;
   uint64_t seed_c, offset_c, seed_r, offset_r;
+  int64_t idx_rows_r;              // SR index of the *_r orientation: c * idx_rows_r + r (0: R)
   uint32_t signs_c, signs_r;
   uint8_t *codes_c, *scales_c, *codes_r, *scales_r;
   const float* amax_c;             // NVFP4: tensor amax of each orientation's values

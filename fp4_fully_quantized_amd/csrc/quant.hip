@@ -323,8 +323,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
                                                      const float* __restrict__ amax, float* tscale,
-                                                     uint64_t seed, uint64_t offset, uint32_t signs,
-                                                     uint32_t scale_words, double* noise) {
+                                                     uint64_t seed, uint64_t offset, uint64_t idx_rows,
+                                                     uint32_t signs, uint32_t scale_words, double* noise) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
   constexpr int TR = 256, TC = 64;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
           cw = e2m1_rtn_pack8(v);
         } else {
           uint32_t h[4];
-          sr_draws8(seed, (offset + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+          sr_draws8(seed, (offset + (uint64_t)cg * idx_rows + (uint64_t)rg) / 8 + g, h);
           cw = e2m1_sr_pack8(v, h);
         }
         sc[g] = cw;
@@ -709,7 +709,7 @@ void launch_rows_mon(const QuantArgs& a, hipStream_t s) {
   const uint32_t grid = MON ? noise_grid(k_quant_rows<FMT, RND, BF16, HAD, MON>, ntiles) : ntiles;
   hipLaunchKernelGGL((k_quant_rows<FMT, RND, BF16, HAD, MON>), dim3(grid), dim3(256), 0, s, a.src, a.R,
                      a.C, a.ld, tiles_c, ntiles, a.codes, a.scales, a.amax, a.tscale, a.seed, a.offset,
-                     a.signs, scale_words, a.noise);
+                     (uint64_t)(a.idx_rows ? a.idx_rows : a.R), a.signs, scale_words, a.noise);
 }
 
 template <int FMT, int RND, bool BF16, bool HAD>

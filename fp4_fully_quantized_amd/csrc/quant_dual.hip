@@ -29,7 +29,7 @@ __device__ __forceinline__ void quant_dual_body(
     const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
     float* tscale_r, float* amax_copy,
     uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
-    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    uint64_t idx_rows, uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
     double* noise_r) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int B = FMT == NV ? 16 : 32;
@@ -229,7 +229,7 @@ __device__ __forceinline__ void quant_dual_body(
             cw = e2m1_rtn_pack8(v);
           } else {
             uint32_t h[4];
-            sr_draws8(seed_r, (off_r + (uint64_t)cg * (uint64_t)R + (uint64_t)rg) / 8 + g, h);
+            sr_draws8(seed_r, (off_r + (uint64_t)cg * idx_rows + (uint64_t)rg) / 8 + g, h);
             cw = e2m1_sr_pack8(v, h);
           }
           sc[g] = cw;
@@ -295,11 +295,11 @@ __global__ __launch_bounds__(256) void k_quant_dual(
     const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
     float* tscale_r, float* amax_copy,
     uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
-    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    uint64_t idx_rows, uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
     double* noise_r) {
   quant_dual_body<FMT, RC, RR, BF16, HC, HR, MON>(src, R, C, ld, tiles_c, ntiles, codes_c, scales_c, codes_r, scales_r,
                                                   amax_c, amax_r, tscale_c, tscale_r, amax_copy, seed_c, off_c,
-                                                  signs_c, seed_r, off_r, signs_r, scale_words_c, scale_words_r,
+                                                  signs_c, seed_r, off_r, idx_rows, signs_r, scale_words_c, scale_words_r,
                                                   noise_c, noise_r);
 }
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
@@ -310,11 +310,11 @@ __global__ __launch_bounds__(256, 3) void k_quant_dual_w3(
     const float* __restrict__ amax_c, const float* __restrict__ amax_r, float* tscale_c,
     float* tscale_r, float* amax_copy,
     uint64_t seed_c, uint64_t off_c, uint32_t signs_c, uint64_t seed_r, uint64_t off_r,
-    uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
+    uint64_t idx_rows, uint32_t signs_r, uint32_t scale_words_c, uint32_t scale_words_r, double* noise_c,
     double* noise_r) {
   quant_dual_body<FMT, RC, RR, BF16, HC, HR, MON>(src, R, C, ld, tiles_c, ntiles, codes_c, scales_c, codes_r, scales_r,
                                                   amax_c, amax_r, tscale_c, tscale_r, amax_copy, seed_c, off_c,
-                                                  signs_c, seed_r, off_r, signs_r, scale_words_c, scale_words_r,
+                                                  signs_c, seed_r, off_r, idx_rows, signs_r, scale_words_c, scale_words_r,
                                                   noise_c, noise_r);
 }
 
@@ -335,7 +335,8 @@ void launch_dual(const DualArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0,
                      s, a.src, a.R, a.C, a.ld, tiles_c, ntiles, a.codes_c, a.scales_c, a.codes_r, a.scales_r,
                      a.amax_c, a.amax_r, a.tscale_c, a.tscale_r, a.amax_copy, a.seed_c, a.offset_c,
-                     a.signs_c, a.seed_r, a.offset_r, a.signs_r, words_c, words_r, a.noise_c,
+                     a.signs_c, a.seed_r, a.offset_r, (uint64_t)(a.idx_rows_r ? a.idx_rows_r : a.R), a.signs_r,
+                     words_c, words_r, a.noise_c,
                      a.noise_r);
 }
 

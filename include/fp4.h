@@ -200,6 +200,36 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
                              int amax_ready, fp4_tensor* out_cols, fp4_tensor* out_rows,
                              fp4_stream_t stream);
 
+/* One row shard of a tensor split by rows (tokens) across data-parallel ranks
+ * ("FP4 All the Way", Key points: the 7B model is trained on 256
+ * accelerators; the split over tokens is this library's reading): src holds rows
+ * row_offset .. row_offset + R - 1 of a rows_total x C tensor. Quantized as
+ * fp4_quantize does, except that every element's stochastic-rounding index is
+ * the one it has in the quantization of the whole tensor:
+ *   axis COLS: (row_offset + r) * C + c + index_offset
+ *   axis ROWS: c * rows_total + row_offset + r + index_offset
+ * With the whole tensor's amax (NVFP4: amax_ready = 1 after an all-reduce(max)
+ * of the ranks' fp4_tensor_amax, or of fp4_tensor_amax_hadamard16 with the
+ * rotation), the shard's codes and scales are exactly rows row_offset ..
+ * (COLS) or columns row_offset .. (ROWS) of the whole tensor's quantization.
+ * Requires 0 <= row_offset, row_offset + R <= rows_total, rows_total % 8 == 0,
+ * and for axis ROWS row_offset % B == 0 (blocks do not straddle shards)
+ * (FP4_ERR_SHAPE / FP4_ERR_ALIGN); otherwise as fp4_quantize. */
+fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                              int64_t row_offset, int64_t rows_total, fp4_axis axis, fp4_rounding rnd,
+                              uint64_t seed, uint64_t index_offset, int amax_ready, fp4_tensor* out,
+                              fp4_stream_t stream);
+
+/* fp4_quantize_dual of a row shard, each orientation's stochastic-rounding
+ * index that of the whole tensor (as fp4_quantize_shard with axis COLS for
+ * out_cols and axis ROWS for out_rows). Requires row_offset % B == 0 and the
+ * other conditions of fp4_quantize_shard; otherwise as fp4_quantize_dual. */
+fp4_status fp4_quantize_dual_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
+                                   int64_t row_offset, int64_t rows_total, fp4_rounding rnd_cols,
+                                   uint64_t seed_cols, uint64_t index_offset_cols, fp4_rounding rnd_rows,
+                                   uint64_t seed_rows, uint64_t index_offset_rows, int amax_ready,
+                                   fp4_tensor* out_cols, fp4_tensor* out_rows, fp4_stream_t stream);
+
 /* Gradient-noise monitor ("FP4 All the Way", Summary: a threshold relating the
  * gradient norm to the quantization noise marks where quantized training stops
  * paying off). fp4_quantize, plus, in the same pass:

@@ -146,6 +146,53 @@ def test_quantize_dual_rejects_null_descriptors(fp4):
                                        ctypes.byref(d), None) == 1
 
 
+SHARD_BAD = [
+    # (R, C, row_offset, rows_total, axis, tensor overrides, expected status)
+    (64, 128, -16, 128, 0, {}, 2),          # negative offset
+    (64, 128, 80, 128, 0, {}, 2),           # shard runs past the whole tensor
+    (64, 128, 0, 0, 0, {}, 2),              # no whole tensor
+    (64, 128, 0, (1 << 62), 0, {}, 2),      # rows_total * C overflows the index
+    (64, 128, 0, 132, 0, {}, 3),            # rows_total % 8
+    (64, 128, 8, 128, 1, {}, 3),            # ROWS shard starts inside a block
+    (64, 128, 16, 128, 1, {"fmt": 1}, 3),   # ... an MXFP4 block
+    (64, 128, 0, 128, 2, {}, 5),            # bad axis
+    (64, 128, 0, 128, 0, {"fmt": 3}, 5),    # bad format
+    (40, 128, 0, 128, 1, {}, 2),            # ROWS shard rows not a multiple of 16 (as fp4_quantize)
+    (64, 100, 0, 128, 0, {}, 2),            # C % 8 (as fp4_quantize)
+]
+
+
+@pytest.mark.parametrize("case", SHARD_BAD)
+def test_quantize_shard_rejects_bad_arguments(fp4, case):
+    R, C, off, total, axis, over, want = case
+    d = _t(fp4, **over)
+    st = fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, ctypes.byref(d), None)
+    assert st == want
+    assert fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, None, None) == 1
+
+
+DUAL_SHARD_BAD = [
+    # (R, C, row_offset, rows_total, cols overrides, expected status)
+    (64, 128, 8, 128, {}, 3),               # the row blocks straddle shards
+    (64, 128, 96, 128, {}, 2),              # past the end
+    (64, 128, 0, 36, {}, 2),                # shard larger than the whole tensor
+    (64, 128, 0, 132, {}, 3),               # rows_total % 8
+    (64, 128, 0, 128, {"fmt": 3}, 5),
+    (40, 128, 0, 128, {}, 2),               # shard rows not a multiple of 16 (as fp4_quantize_dual)
+]
+
+
+@pytest.mark.parametrize("case", DUAL_SHARD_BAD)
+def test_quantize_dual_shard_rejects_bad_arguments(fp4, case):
+    R, C, off, total, over, want = case
+    dc, dr = _t(fp4, **over), _t(fp4)
+    st = fp4.lib().fp4_quantize_dual_shard(0x1000, 1, R, C, C, off, total, 0, 0, 0, 1, 0, 0, 1,
+                                           ctypes.byref(dc), ctypes.byref(dr), None)
+    assert st == want
+    assert fp4.lib().fp4_quantize_dual_shard(0x1000, 1, R, C, C, off, total, 0, 0, 0, 1, 0, 0, 1,
+                                             None, ctypes.byref(dr), None) == 1
+
+
 def test_noise_entry_points_reject_bad_arguments(fp4):
     L = fp4.lib()
     d = _t(fp4)
