@@ -90,10 +90,11 @@ def lib() -> ctypes.CDLL:
                                         c.c_int, c.POINTER(fp4_tensor), c.POINTER(fp4_tensor), c.c_void_p]
         L.fp4_quantize_shard.restype = c.c_int
         L.fp4_quantize_shard.argtypes = (L.fp4_quantize.argtypes[:5] + [c.c_int64, c.c_int64]
-                                         + L.fp4_quantize.argtypes[5:])
+                                         + L.fp4_quantize.argtypes[5:-1] + [c.c_void_p, c.c_void_p])
         L.fp4_quantize_dual_shard.restype = c.c_int
         L.fp4_quantize_dual_shard.argtypes = (L.fp4_quantize_dual.argtypes[:5] + [c.c_int64, c.c_int64]
-                                              + L.fp4_quantize_dual.argtypes[5:])
+                                              + L.fp4_quantize_dual.argtypes[5:-1]
+                                              + [c.c_void_p, c.c_void_p, c.c_void_p])
         L.fp4_quantize_noise.restype = c.c_int
         L.fp4_quantize_noise.argtypes = L.fp4_quantize.argtypes[:-1] + [c.c_void_p, c.c_void_p]
         L.fp4_quantize_dual_noise.restype = c.c_int
@@ -304,32 +305,42 @@ def fp4_quantize_dual(src, rnd_cols: int, seed_cols: int, index_offset_cols: int
 
 
 def fp4_quantize_shard(src, row_offset: int, rows_total: int, axis: int, rnd: int, seed: int,
-                       index_offset: int, amax_ready: bool, out: QTensor, stream=None) -> None:
+                       index_offset: int, amax_ready: bool, out: QTensor, noise=None, stream=None) -> None:
     """fp4_quantize of rows row_offset .. of a rows_total-row tensor, with the
-    whole tensor's stochastic-rounding indices."""
+    whole tensor's stochastic-rounding indices (noise: None, or the float64
+    device tensor of 2 sums of fp4_quantize_noise)."""
+    import torch
     _check_matrix(src, "src")
     _check_quant_out(src, out, axis)
+    if noise is not None:
+        _check_scalar(noise, "noise", torch.float64, 2, src.device)
     R, C = src.shape
     d = out.desc()
     _check(lib().fp4_quantize_shard(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), row_offset,
                                     rows_total, axis, rnd, seed, index_offset, int(bool(amax_ready)),
-                                    ctypes.byref(d), _stream(stream)), "fp4_quantize_shard")
+                                    ctypes.byref(d), _ptr(noise), _stream(stream)), "fp4_quantize_shard")
     out.rows, out.cols = d.rows, d.cols
 
 
 def fp4_quantize_dual_shard(src, row_offset: int, rows_total: int, rnd_cols: int, seed_cols: int,
                             index_offset_cols: int, rnd_rows: int, seed_rows: int, index_offset_rows: int,
-                            amax_ready: bool, out_cols: QTensor, out_rows: QTensor, stream=None) -> None:
+                            amax_ready: bool, out_cols: QTensor, out_rows: QTensor, noise_cols=None,
+                            noise_rows=None, stream=None) -> None:
     """fp4_quantize_dual of a row shard, with the whole tensor's stochastic-rounding indices."""
+    import torch
     _check_matrix(src, "src")
     _check_quant_out(src, out_cols, FP4_AXIS_COLS, "out_cols")
     _check_quant_out(src, out_rows, FP4_AXIS_ROWS, "out_rows")
+    for nm, t in (("noise_cols", noise_cols), ("noise_rows", noise_rows)):
+        if t is not None:
+            _check_scalar(t, nm, torch.float64, 2, src.device)
     R, C = src.shape
     dc, dr = out_cols.desc(), out_rows.desc()
     _check(lib().fp4_quantize_dual_shard(src.data_ptr(), _dtype_code(src), R, C, src.stride(0), row_offset,
                                          rows_total, rnd_cols, seed_cols, index_offset_cols, rnd_rows,
                                          seed_rows, index_offset_rows, int(bool(amax_ready)), ctypes.byref(dc),
-                                         ctypes.byref(dr), _stream(stream)), "fp4_quantize_dual_shard")
+                                         ctypes.byref(dr), _ptr(noise_cols), _ptr(noise_rows), _stream(stream)),
+           "fp4_quantize_dual_shard")
     out_cols.rows, out_cols.cols = dc.rows, dc.cols
     out_rows.rows, out_rows.cols = dr.rows, dr.cols
 

@@ -503,9 +503,10 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
 fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                               int64_t row_offset, int64_t rows_total, fp4_axis axis, fp4_rounding rnd,
                               uint64_t seed, uint64_t index_offset, int amax_ready, fp4_tensor* out,
-                              fp4_stream_t stream) {
+                              double* noise, fp4_stream_t stream) {
   if (!out) return FP4_ERR_NULL;
   if (!valid_fmt(out->fmt)) return FP4_ERR_ARG;
+  if (!aligned8(noise)) return FP4_ERR_ALIGN;
   if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ARG;
   fp4_status st = check_shard(R, C, row_offset, rows_total, axis == FP4_AXIS_ROWS, block_of(out->fmt));
   if (st != FP4_OK) return st;
@@ -514,7 +515,7 @@ fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64
                                                              : (uint64_t)row_offset);
   st = check_quant(src, src_t, R, C, ld, axis, rnd, off, out);
   if (st != FP4_OK) return st;
-  return launch_quant(src, src_t, R, C, ld, axis, rnd, seed, off, amax_ready, out, nullptr,
+  return launch_quant(src, src_t, R, C, ld, axis, rnd, seed, off, amax_ready, out, noise,
                       reinterpret_cast<hipStream_t>(stream), rows_total);
 }
 
@@ -522,15 +523,17 @@ fp4_status fp4_quantize_dual_shard(const void* src, fp4_dtype src_t, int64_t R, 
                                    int64_t row_offset, int64_t rows_total, fp4_rounding rnd_cols,
                                    uint64_t seed_cols, uint64_t index_offset_cols, fp4_rounding rnd_rows,
                                    uint64_t seed_rows, uint64_t index_offset_rows, int amax_ready,
-                                   fp4_tensor* out_cols, fp4_tensor* out_rows, fp4_stream_t stream) {
+                                   fp4_tensor* out_cols, fp4_tensor* out_rows, double* noise_cols,
+                                   double* noise_rows, fp4_stream_t stream) {
   if (!out_cols) return FP4_ERR_NULL;
   if (!valid_fmt(out_cols->fmt)) return FP4_ERR_ARG;
+  if (!aligned8(noise_cols) || !aligned8(noise_rows)) return FP4_ERR_ALIGN;
   const fp4_status st = check_shard(R, C, row_offset, rows_total, true, block_of(out_cols->fmt));
   if (st != FP4_OK) return st;
   return quantize_dual_impl(src, src_t, R, C, ld, rnd_cols, seed_cols,
                             index_offset_cols + (uint64_t)row_offset * (uint64_t)C, rnd_rows, seed_rows,
-                            index_offset_rows + (uint64_t)row_offset, amax_ready, out_cols, out_rows, nullptr,
-                            nullptr, stream, rows_total);
+                            index_offset_rows + (uint64_t)row_offset, amax_ready, out_cols, out_rows, noise_cols,
+                            noise_rows, stream, rows_total);
 }
 
 fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,

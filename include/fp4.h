@@ -212,23 +212,30 @@ fp4_status fp4_quantize_dual(const void* src, fp4_dtype src_t, int64_t R, int64_
  * of the ranks' fp4_tensor_amax, or of fp4_tensor_amax_hadamard16 with the
  * rotation), the shard's codes and scales are exactly rows row_offset ..
  * (COLS) or columns row_offset .. (ROWS) of the whole tensor's quantization.
+ * noise: NULL, or the two device doubles of fp4_quantize_noise, accumulated
+ * into with this shard's sums (summed across the ranks, they are the whole
+ * tensor's, up to the order of FP64 additions).
  * Requires 0 <= row_offset, row_offset + R <= rows_total, rows_total % 8 == 0,
  * and for axis ROWS row_offset % B == 0 (blocks do not straddle shards)
- * (FP4_ERR_SHAPE / FP4_ERR_ALIGN); otherwise as fp4_quantize. */
+ * (FP4_ERR_SHAPE / FP4_ERR_ALIGN), noise 8-byte aligned (FP4_ERR_ALIGN);
+ * otherwise as fp4_quantize. */
 fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                               int64_t row_offset, int64_t rows_total, fp4_axis axis, fp4_rounding rnd,
                               uint64_t seed, uint64_t index_offset, int amax_ready, fp4_tensor* out,
-                              fp4_stream_t stream);
+                              double* noise, fp4_stream_t stream);
 
 /* fp4_quantize_dual of a row shard, each orientation's stochastic-rounding
  * index that of the whole tensor (as fp4_quantize_shard with axis COLS for
- * out_cols and axis ROWS for out_rows). Requires row_offset % B == 0 and the
- * other conditions of fp4_quantize_shard; otherwise as fp4_quantize_dual. */
+ * out_cols and axis ROWS for out_rows); noise_cols, noise_rows: NULL or the
+ * sums of fp4_quantize_dual_noise for either orientation. Requires
+ * row_offset % B == 0 and the other conditions of fp4_quantize_shard;
+ * otherwise as fp4_quantize_dual. */
 fp4_status fp4_quantize_dual_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                                    int64_t row_offset, int64_t rows_total, fp4_rounding rnd_cols,
                                    uint64_t seed_cols, uint64_t index_offset_cols, fp4_rounding rnd_rows,
                                    uint64_t seed_rows, uint64_t index_offset_rows, int amax_ready,
-                                   fp4_tensor* out_cols, fp4_tensor* out_rows, fp4_stream_t stream);
+                                   fp4_tensor* out_cols, fp4_tensor* out_rows, double* noise_cols,
+                                   double* noise_rows, fp4_stream_t stream);
 
 /* Gradient-noise monitor ("FP4 All the Way", Summary: a threshold relating the
  * gradient norm to the quantization noise marks where quantized training stops

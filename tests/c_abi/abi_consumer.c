@@ -9,8 +9,11 @@
  * roundings, with and without the rotation, and each operand stored K-major
  * (layout N) or transposed (layout T), the product and the workspace's codes
  * and scale bytes must equal those of fp4_quantize followed by a GEMM of the
- * quantized operands, bit for bit. Exit status 0 and "abi consumer ok" on
- * success.
+ * quantized operands, bit for bit. Last, X as two 32-row shards (the
+ * transposed quantization with stochastic rounding, the shards' amaxes
+ * reduced by max on the host): each shard's codes and scale bytes must be its
+ * columns of the oracle's quantization of the whole X. Exit status 0 and
+ * "abi consumer ok" on success.
  */
 #include <math.h>
 #include <stdint.h>
@@ -256,6 +259,64 @@ static int raw_operand_cases(const float* x, const float* w)
     return cases == 32 ? 0 : 15;
 }
 
+/* X (M x K) in two row shards, quantized along the rows (out: K x rows) with
+ * SR and the whole tensor's indices and amax. */
+static int shard_case(const float* x)
+{
+    enum { SH = M / 2 };
+    float* dx;
+    float* damax;
+    CHECK_HIP(hipMalloc((void**)&dx, sizeof(float) * M * K));
+    CHECK_HIP(hipMemcpy(dx, x, sizeof(float) * M * K, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMalloc((void**)&damax, 2 * sizeof(float)));
+    for (int h = 0; h < 2; ++h)
+        CHECK_FP4(fp4_tensor_amax(dx + h * SH * K, FP4_DTYPE_F32, SH, K, K, damax + h, NULL));
+    float am[2];
+    CHECK_HIP(hipMemcpy(am, damax, sizeof(am), hipMemcpyDeviceToHost));
+    const float amax = am[0] > am[1] ? am[0] : am[1]; /* the all-reduce(max) */
+
+    static uint8_t wc[K * M / 2], ws[K * M / 16];
+    float wam, wsg;
+    if (o_quantize(x, 0, M, K, K, O_AXIS_ROWS, O_FMT_NVFP4, O_SR, 11, 0, 0, 0, 0, 0.0f, wc, ws, &wam, &wsg) != 0)
+        return 20;
+    int bad = 0;
+    for (int h = 0; h < 2; ++h) {
+        dev_q d;
+        CHECK_HIP(hipMalloc((void**)&d.codes, fp4_codes_bytes(K, SH)));
+        CHECK_HIP(hipMalloc((void**)&d.scales, fp4_scales_bytes(K, SH, FP4_NVFP4)));
+        CHECK_HIP(hipMalloc((void**)&d.amax, 4));
+        CHECK_HIP(hipMalloc((void**)&d.tscale, 4));
+        CHECK_HIP(hipMemcpy(d.amax, &amax, 4, hipMemcpyHostToDevice));
+        fp4_tensor t;
+        memset(&t, 0, sizeof(t));
+        t.codes = d.codes;
+        t.scales = d.scales;
+        t.amax = d.amax;
+        t.tscale = d.tscale;
+        t.fmt = FP4_NVFP4;
+        CHECK_FP4(fp4_quantize_shard(dx + h * SH * K, FP4_DTYPE_F32, SH, K, K, h * SH, M, FP4_AXIS_ROWS, FP4_SR,
+                                     11, 0, 1, &t, NULL, NULL));
+        static uint8_t gc[K * SH / 2], gs[K * SH / 16];
+        float gsg;
+        CHECK_HIP(hipMemcpy(gc, d.codes, sizeof(gc), hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(gs, d.scales, sizeof(gs), hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(&gsg, d.tscale, 4, hipMemcpyDeviceToHost));
+        for (int r = 0; r < K; ++r) {
+            bad |= memcmp(gc + r * (SH / 2), wc + r * (M / 2) + h * (SH / 2), SH / 2) != 0;
+            bad |= memcmp(gs + r * (SH / 16), ws + r * (M / 16) + h * (SH / 16), SH / 16) != 0;
+        }
+        bad |= gsg != wsg;
+        hipFree(d.codes); hipFree(d.scales); hipFree(d.amax); hipFree(d.tscale);
+    }
+    hipFree(dx);
+    hipFree(damax);
+    if (bad) {
+        fprintf(stderr, "a shard differs from its slice of the whole tensor's quantization\n");
+        return 21;
+    }
+    return 0;
+}
+
 int main(void)
 {
     static float x[M * K], w[N * K];
@@ -312,10 +373,11 @@ int main(void)
         return 6;
     }
     if ((rc = raw_operand_cases(x, w))) return rc;
+    if ((rc = shard_case(x))) return rc;
     hipFree(sx); hipFree(sw); hipFree(dy);
     hipFree(dx.codes); hipFree(dx.scales); hipFree(dx.amax); hipFree(dx.tscale);
     hipFree(dw.codes); hipFree(dw.scales); hipFree(dw.amax); hipFree(dw.tscale);
     printf("abi consumer ok (GEMM worst error %.3g of the bound; 32 raw-operand GEMMs equal to "
-           "quantize-then-GEMM)\n", worst);
+           "quantize-then-GEMM; two SR shards equal to their slices)\n", worst);
     return 0;
 }

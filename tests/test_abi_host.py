@@ -166,9 +166,20 @@ SHARD_BAD = [
 def test_quantize_shard_rejects_bad_arguments(fp4, case):
     R, C, off, total, axis, over, want = case
     d = _t(fp4, **over)
-    st = fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, ctypes.byref(d), None)
+    st = fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, ctypes.byref(d), None,
+                                      None)
     assert st == want
-    assert fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, None, None) == 1
+    assert fp4.lib().fp4_quantize_shard(0x1000, 1, R, C, C, off, total, axis, 1, 0, 0, 1, None, None, None) == 1
+
+
+def test_quantize_shard_rejects_a_misaligned_noise_buffer(fp4):
+    d = _t(fp4)
+    assert fp4.lib().fp4_quantize_shard(0x1000, 1, 64, 128, 128, 0, 128, 0, 1, 0, 0, 1, ctypes.byref(d),
+                                        0x50004, None) == 3
+    dc, dr = _t(fp4), _t(fp4)
+    for nc, nr in ((0x50004, None), (None, 0x50004)):
+        assert fp4.lib().fp4_quantize_dual_shard(0x1000, 1, 64, 128, 128, 0, 128, 0, 0, 0, 1, 0, 0, 1,
+                                                 ctypes.byref(dc), ctypes.byref(dr), nc, nr, None) == 3
 
 
 DUAL_SHARD_BAD = [
@@ -187,10 +198,10 @@ def test_quantize_dual_shard_rejects_bad_arguments(fp4, case):
     R, C, off, total, over, want = case
     dc, dr = _t(fp4, **over), _t(fp4)
     st = fp4.lib().fp4_quantize_dual_shard(0x1000, 1, R, C, C, off, total, 0, 0, 0, 1, 0, 0, 1,
-                                           ctypes.byref(dc), ctypes.byref(dr), None)
+                                           ctypes.byref(dc), ctypes.byref(dr), None, None, None)
     assert st == want
     assert fp4.lib().fp4_quantize_dual_shard(0x1000, 1, R, C, C, off, total, 0, 0, 0, 1, 0, 0, 1,
-                                             None, ctypes.byref(dr), None) == 1
+                                             None, ctypes.byref(dr), None, None, None) == 1
 
 
 def test_noise_entry_points_reject_bad_arguments(fp4):

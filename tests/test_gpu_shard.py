@@ -4,7 +4,8 @@ tensor's amax (the per-shard amaxes reduced by max, as an all-reduce would)
 and its global offsets, gives exactly the slices of the oracle's quantization
 of the whole tensor: codes, scale bytes, amax and tensor scale, for both
 formats, RTN and SR, with and without the rotation, on both axes and in the
-one-read dual pass."""
+one-read dual pass; with the noise monitor, the shards' sums add up to the
+whole tensor's."""
 import numpy as np
 import pytest
 
@@ -174,3 +175,65 @@ def test_full_size_gradient_shard(fp4, orc):
     assert_same_quant(got_c, _slice(orc.quantize(xh, axis=0, rnd=1, seed=5), o, n, 0, 16), "dY shard, cols")
     want_r = orc.quantize(xh, axis=1, rnd=1, seed=6)
     assert_same_quant(got_r, _slice(want_r, o, n, 1, 16), "dY shard, rows")
+
+
+# Noise-monitor sums of shards, added into one buffer (as an all-reduce(sum)
+# across ranks would): the whole tensor's sums. Each partial is formed in FP32
+# over at most 32 elements (relative error <= 33 * 2^-24 of a sum of
+# non-negative terms) and added in FP64, as in one call on the whole tensor.
+NOISE_RTOL = 1e-5
+
+
+def _assert_noise(got, want, what):
+    got = got.cpu().numpy()
+    for k in (0, 1):
+        assert abs(got[k] - want[k]) <= NOISE_RTOL * want[k], (what, k, got[k], want[k])
+
+
+@pytest.mark.parametrize("fmt,rnd,axis", [(0, 1, 0), (0, 1, 1), (1, 0, 0), (1, 1, 1)])
+def test_monitored_shards_add_up_to_the_whole_tensor(fp4, orc, fmt, rnd, axis):
+    import torch
+    B = 16 if fmt == 0 else 32
+    sizes = SIZES[axis]
+    total, C = sum(sizes), 544
+    say("quantize_shard with noise", (total, C), sizes, "fmt", fmt, "rnd", rnd, "axis", axis)
+    xh = _data((total, C), 80 + fmt + 2 * axis)
+    want = orc.quantize(xh, axis=axis, fmt=fmt, rnd=rnd, seed=9, index_offset=0, noise=True)
+    x = to_device(xh)
+    shards = [x[o:o + n] for o, n in _bounds(sizes)]
+    amax = _global_amax(fp4, shards, fmt, axis, 0)
+    noise = torch.zeros(2, dtype=torch.float64, device="cuda")
+    for (o, n), xs in zip(_bounds(sizes), shards):
+        q = fp4.QTensor(*((C, n) if axis == 1 else (n, C)), fmt)
+        if amax is not None:
+            q.amax.copy_(amax)
+        fp4.fp4_quantize_shard(xs, o, total, axis, rnd, 9, 0, True, q, noise=noise)
+        assert_same_quant(q_to_host(q), _slice(want, o, n, axis, B), f"monitored shard at row {o}")
+    _assert_noise(noise, want["noise"], "shards")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_monitored_dual_shards_add_up_to_the_whole_tensor(fp4, orc, fmt):
+    import torch
+    B = 16 if fmt == 0 else 32
+    sizes = [96, 224, 32, 64]
+    total, C = sum(sizes), 544
+    say("quantize_dual_shard with noise", (total, C), sizes, "fmt", fmt)
+    xh = _data((total, C), 90 + fmt)
+    want_c = orc.quantize(xh, axis=0, fmt=fmt, rnd=1, seed=3, noise=True)
+    want_r = orc.quantize(xh, axis=1, fmt=fmt, rnd=1, seed=4, noise=True)
+    x = to_device(xh)
+    shards = [x[o:o + n] for o, n in _bounds(sizes)]
+    amax = _global_amax(fp4, shards, fmt, 0, 0)
+    nc = torch.zeros(2, dtype=torch.float64, device="cuda")
+    nr = torch.zeros(2, dtype=torch.float64, device="cuda")
+    for (o, n), xs in zip(_bounds(sizes), shards):
+        qc, qr = fp4.QTensor(n, C, fmt), fp4.QTensor(C, n, fmt)
+        if amax is not None:
+            qc.amax.copy_(amax)
+            qr.amax = qc.amax
+        fp4.fp4_quantize_dual_shard(xs, o, total, 1, 3, 0, 1, 4, 0, True, qc, qr, noise_cols=nc, noise_rows=nr)
+        assert_same_quant(q_to_host(qc), _slice(want_c, o, n, 0, B), f"monitored dual shard at row {o}, cols")
+        assert_same_quant(q_to_host(qr), _slice(want_r, o, n, 1, B), f"monitored dual shard at row {o}, rows")
+    _assert_noise(nc, want_c["noise"], "dual shards, cols")
+    _assert_noise(nr, want_r["noise"], "dual shards, rows")
