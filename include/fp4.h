@@ -35,7 +35,7 @@
  *              (>= -127); byte = e + 127; v = x * 2^-e.
  *   RTN        nearest E2M1 magnitude, ties to even, saturating at 6.
  *   SR         a grid value is kept; else lo < |v| < hi rounds up iff
- *              h / 65536 < (|v| - lo) / (hi - lo), with h the 16-bit draw of
+ *              h + floor(65536 * (|v| - lo) / (hi - lo)) >= 65536, with h the 16-bit draw of
  *              the element: Philox4x32-10, key = seed, counter = (i / 8, 0, 0)
  *              as (lo32, hi32, 0, 0), word (i / 2) % 4, low half for even i;
  *              i = row-major index in the quantized orientation + index_offset.

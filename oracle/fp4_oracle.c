@@ -64,9 +64,10 @@ unsigned o_e2m1_rtn_mag(float a)
 
 /* Stochastic rounding onto the E2M1 magnitudes. A value on the grid is kept.
  * Otherwise, with lo < a < hi its grid neighbours and p = (a-lo)/(hi-lo),
- * the result is hi when the uniform draw u = h16 / 2^16 satisfies u < p,
- * else lo; so P(hi) = p up to the 2^-16 resolution of the draw and the
- * expected result equals a. */
+ * the result is hi when the 16-bit draw and p's first 16 fraction bits carry
+ * out of a 16-bit add, h16 + floor(p * 2^16) >= 2^16, else lo; so
+ * P(hi) = floor(p * 2^16) / 2^16, at most 2^-16 below p, and the expected
+ * result equals a up to 2^-16 of a grid step. */
 unsigned o_e2m1_sr_mag(float a, uint32_t h16)
 {
     unsigned lo = 0;
@@ -78,9 +79,9 @@ unsigned o_e2m1_sr_mag(float a, uint32_t h16)
     if (lo == 7) return 7; /* a > 6 does not occur: callers clamp to 6 */
     unsigned hi = lo + 1;
     double glo = o_e2m1_value(lo), ghi = o_e2m1_value(hi);
-    double p = ((double)a - glo) / (ghi - glo);
-    double u = (double)(h16 & 0xFFFFu) / 65536.0;
-    return (u < p) ? hi : lo;
+    double p = ((double)a - glo) / (ghi - glo); /* exact: a power-of-two step */
+    double pf = floor(p * 65536.0);
+    return ((double)(h16 & 0xFFFFu) + pf >= 65536.0) ? hi : lo;
 }
 
 /* ------------------------------------------------------------------------ */

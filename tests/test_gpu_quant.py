@@ -237,8 +237,10 @@ def _sr_boundary_input(orc, R, C, axis, seed, offset):
     """fp32 [R, C] whose MXFP4 block exponents are all 0 (element 0 of every
     block along the blocked axis is 5.5), so the scaled values equal the
     inputs, and whose other values sit on or next to the stochastic-rounding
-    boundary of their own draw h: p * 2^22 = 64 h - 1, 64 h, 64 h + 1/2,
-    64 h + 1, in each binade of the E2M1 grid, plus values far below the
+    boundary of their own draw h, where p's first 16 fraction bits reach
+    2^16 - h: p * 2^22 = B - 1, B - 1/2, B, B + 1/2, B + 1 with
+    B = 64 (2^16 - h), in each binade of the E2M1 grid (the integer ones
+    where a binade's values give only integers), plus values far below the
     first grid step. The draw is the one of the element's index in the
     quantized orientation."""
     rng = np.random.default_rng(seed)
@@ -253,17 +255,17 @@ def _sr_boundary_input(orc, R, C, axis, seed, offset):
             idx = offset + (r * C + c if axis == 0 else c * R + r)
             h = orc.sr_draw16(seed, idx)
             kind = kinds[(r * 7 + c * 3) % len(kinds)]
-            d = [-1.0, 0.0, 0.5, 1.0][(r + c) % 4]
-            g = 64 * h + d                     # target p * 2^22
+            d = [-1.0, -0.5, 0.0, 0.5, 1.0][(r + c) % 5]
+            g = min(64.0 * (65536 - h) + d, 4194303.0)   # target p * 2^22 (p < 1)
             if kind in ("a1", "a2", "a4"):     # [1,2), [2,4), [4,6): p * 2^22 = rem (22 bits)
                 lo = {"a1": 1.0, "a2": 2.0, "a4": 4.0}[kind]
                 q = {"a1": 0.5, "a2": 1.0, "a4": 2.0}[kind]
-                g = np.floor(g) if g >= 0 else 0.0   # these binades hold integer p * 2^22 only
+                g = np.floor(g)                # these binades hold integer p * 2^22 only
                 a = lo + q * g / 4194304.0
             elif kind == "half":               # [0.5, 1): p * 2^22 = m / 2
-                a = 0.5 + 0.5 * max(g, 0.0) / 4194304.0
+                a = 0.5 + 0.5 * g / 4194304.0
             elif kind == "tiny":               # below 0.5: p * 2^22 = a * 2^23
-                a = max(g, 0.25) / 8388608.0
+                a = g / 8388608.0
             else:
                 a = float(rng.choice([2.0 ** -30, 3.0 * 2 ** -40, 2.0 ** -24]))
             x[r, c] = np.float32(a) * (1.0 if rng.random() < 0.5 else -1.0)

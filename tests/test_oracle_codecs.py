@@ -277,14 +277,17 @@ def test_sr_support_and_fixed_points(orc):
 
 def test_sr_is_unbiased(orc):
     # Over N draws of the element stream the mean of the rounded value equals
-    # a within 5 standard errors (plus the 2^-16 resolution of the draw).
+    # a within 5 standard errors, plus the 2^-16 resolution of the draw (of
+    # the grid step between a's neighbours: below 2^-16 of a step, as for
+    # 1e-6, the value never rounds up).
     n = 40000
+    grid = [orc.e2m1_value(c) for c in range(8)]
     for a in [0.25, 0.1, 0.75, 1.1, 1.75, 2.5, 3.3, 5.0, 5.99, 1e-6]:
         a = f32(a)
         vals = np.array([orc.e2m1_value(orc.e2m1_sr_mag(a, orc.sr_draw16(3, i)))
                          for i in range(n)])
         sd = max(vals.std(), 1e-12)
-        step = max(vals) - min(vals)
+        step = min(g for g in grid if g > a) - max(g for g in grid if g <= a)
         assert abs(vals.mean() - a) <= 5 * sd / math.sqrt(n) + step * 2 ** -16 + 1e-12, a
 
 
