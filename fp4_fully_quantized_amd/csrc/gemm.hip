@@ -71,11 +71,13 @@ constexpr int kSchedDsWrite = 0x200;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
 }
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// off: the lane's byte offset; soff: a part common to the workgroup (held in
+// the instruction's scalar offset, so it costs no vector add per load).
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
 }
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0));
 }
 
 // Scaled FP4 MFMA; S selects the byte of the lanes' scale words (op_sel).
@@ -209,21 +211,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   // kt counts the K tiles of this workgroup's range (from kb).
   auto gload_code = [&](int j, int kt) {
     const uint32_t kc = (uint32_t)(kb + kt) * C::ROWB;
-    if (j < JA) creg[j] = bload16(ra, goff_a + (uint32_t)(j * C::RPL) * kb_row + kc);
-    else creg[j] = bload16(rb, goff_b + (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
+    if (j < JA) creg[j] = bload16(ra, goff_a, (uint32_t)(j * C::RPL) * kb_row + kc);
+    else creg[j] = bload16(rb, goff_b, (uint32_t)((j - JA) * C::RPL) * kb_row + kc);
   };
   auto gload_scales = [&](int kt) {
     const uint32_t ks = (uint32_t)(kb + kt) * C::SCB;
     if constexpr (C::SCB == 16) {
-      sreg[0] = bload16(rsa, soff_a + ks);
-      sreg[1] = bload16(rsb, soff_b + ks);
+      sreg[0] = bload16(rsa, soff_a, ks);
+      sreg[1] = bload16(rsb, soff_b, ks);
     } else if constexpr (C::SCB == 8) {
-      uint2 x = bload8(rsa, soff_a + ks), y = bload8(rsb, soff_b + ks);
+      uint2 x = bload8(rsa, soff_a, ks), y = bload8(rsb, soff_b, ks);
       sreg[0] = make_uint4(x.x, x.y, 0, 0);
       sreg[1] = make_uint4(y.x, y.y, 0, 0);
     } else {
-      sreg[0] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(soff_a + ks), 0, 0), 0, 0, 0);
-      sreg[1] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsb, (int)(soff_b + ks), 0, 0), 0, 0, 0);
+      sreg[0] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsa, (int)soff_a, (int)ks, 0), 0, 0, 0);
+      sreg[1] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rsb, (int)soff_b, (int)ks, 0), 0, 0, 0);
     }
   };
   auto lstore_code = [&](int j, int buf) {
@@ -266,8 +268,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   for (int i = 0; i < FM; ++i) arow[i] = wm * WM + i * 32 + lr;
 #pragma unroll
   for (int j = 0; j < FN; ++j) brow[j] = BM + wn * WN + j * 32 + lr;
-  auto frag = [&](const uint8_t* L, int row, int chunk) {
-    return *reinterpret_cast<const uint4*>(L + row * C::ROWB + ((chunk ^ ((row >> 1) & (C::CPR - 1))) * 16));
+  // Fragment f (A fragments 0 .. FM-1, then B) at chunk 2k + g. Every row
+  // this lane reads is lr plus a multiple of 32, so its swizzle key
+  // (row / 2) % CPR is the lane's own and the chunk's swizzled position,
+  // 16 ((2k + g) ^ key) = 32k ^ T, is shared by all its fragments, which then
+  // differ by constants (immediate offsets of the LDS reads).
+  const int T = (g ^ ((lr >> 1) & (C::CPR - 1))) * 16;
+  const int a_lane = (wm * WM + lr) * C::ROWB, b_lane = (BM + wn * WN + lr) * C::ROWB;
+  auto frag = [&](const uint8_t* L, int f, int k) {
+    const int sw = T ^ (32 * k);
+    return f < FM ? *reinterpret_cast<const uint4*>(L + a_lane + sw + f * 32 * C::ROWB)
+                  : *reinterpret_cast<const uint4*>(L + b_lane + sw + (f - FM) * 32 * C::ROWB);
   };
 
   // Pipeline: tile 0 in LDS buffer 0 and tile 1 in the staging registers
@@ -304,9 +315,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
     };
     auto read_frags = [&](const uint8_t* L, int s, int dst) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[dst][i] = frag(L, arow[i], 2 * s + g);
+      for (int i = 0; i < FM; ++i) a[dst][i] = frag(L, i, s);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[dst][j] = frag(L, brow[j], 2 * s + g);
+      for (int j = 0; j < FN; ++j) b[dst][j] = frag(L, FM + j, s);
     };
     read_scales(lds_s[0]);
     read_frags(lds_c[0], 0, 0);
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
     };
     auto read_raw = [&](const uint8_t* L, int c2, int dst) {
 #pragma unroll
-      for (int f = 0; f < FM + FN; ++f) raw[dst][f] = frag(L, f < FM ? arow[f] : brow[f - FM], g + 2 * c2);
+      for (int f = 0; f < FM + FN; ++f) raw[dst][f] = frag(L, f, c2);
     };
     // The two E4M3 scales of chunk pair c2 (blocks 2c, 2c+1 of chunk c) as one
     // exact f16 pair per fragment; the multiplies broadcast one half.
