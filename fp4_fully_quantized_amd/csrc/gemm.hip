@@ -23,7 +23,9 @@
 //   64-value group, so each lane reads 16 contiguous bytes per group.
 //
 // Tiling: 256 threads = 4 waves (2 x 2), workgroup tile 256 x 256 (each wave
-// owns 128 x 128 = 4 x 4 MFMA fragments, accumulators in AGPRs), K tile BK
+// owns 128 x 128 = 4 x 4 MFMA fragments, accumulators in AGPRs; the MXFP4
+// whole tiles at K tile 256 run k_gemm_mx8: 8 waves of 128 x 64, two per
+// SIMD, since that kernel is bound by LDS and barrier waits, not VALU), K tile BK
 // (256 values when K allows, else 128). Global loads are buffer loads (the
 // descriptor's size bound turns rows past M or N into zeros), issued one K
 // tile ahead into VGPRs and written to the other half of a double-buffered
@@ -570,6 +572,235 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
   }
 }
 
+// MXFP4, K tile 256, whole output tiles: 512 threads = 8 waves, two per SIMD.
+// Wave (wm, wn), wm = wave / 4, wn = wave % 4, owns 128 x 64 outputs (4 x 2
+// fragments, 128 accumulators, so two waves fit a SIMD's registers), and one
+// wave's barrier and LDS waits overlap the other's MFMAs. The staging, LDS
+// layout, pipeline and epilogue are k_gemm's, for 512 threads.
+template <bool BF16OUT>
+__global__ __launch_bounds__(512, 1) void k_gemm_mx8(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+                                                      const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
+                                                      uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_m,
+                                                      uint32_t tiles_n, uint32_t group_m, uint32_t nfull,
+                                                      void* __restrict__ cout, int64_t ldc, uint32_t vec_ok) {
+  constexpr int ROWB = 128, CPR = 8, SCB = 8, NS = 4;
+  constexpr int ROWS = BM + BN;                  // 512 staged rows per K tile
+  constexpr int LDS_CODES = ROWS * ROWB, LDS_SCALES = ROWS * SCB;
+  constexpr int NT = 512;
+  constexpr int RPL = NT / CPR;                  // rows per load round (64)
+  constexpr int CODE_LOADS = ROWS / RPL;         // 8 per thread
+  constexpr int JA = BM / RPL;                   // loads that cover A rows (4)
+  constexpr int PER = (CODE_LOADS + NS - 2) / (NS - 1);  // staging pieces per substep (3)
+  constexpr int WM8 = 128, WN8 = 64, FM8 = 4, FN8 = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (LDS_CODES + LDS_SCALES)];
+  uint8_t (*lds_c)[LDS_CODES] = reinterpret_cast<uint8_t (*)[LDS_CODES]>(lds);
+  uint8_t (*lds_s)[LDS_SCALES] = reinterpret_cast<uint8_t (*)[LDS_SCALES]>(lds + 2 * LDS_CODES);
+
+  const uint32_t gfull = (nfull + NXCD - 1) / NXCD * NXCD;
+  const uint32_t t = (blockIdx.x % NXCD) * (gfull / NXCD) + blockIdx.x / NXCD;
+  if (t >= nfull) return;
+  uint32_t tm, tn;
+  tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+  const uint32_t m0 = tm * BM, n0 = tn * BN;
+  const int nk = (int)(K / 256);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the scale rows' descriptor is scalar
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 5;
+  const int lr = lane & 31;
+  const uint32_t kb_row = K / 2;
+  const uint32_t ks_row = K / 32;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ac, M * kb_row);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(bc, N * kb_row);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as, M * ks_row);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs, N * ks_row);
+
+  // Code loads: load j covers tile rows RPL*j + tid/CPR (A rows, then B), chunk tid%CPR.
+  const int lrow = tid / CPR, lchk = tid % CPR;
+  const uint32_t goff_a = (m0 + lrow) * kb_row + lchk * 16;
+  const uint32_t goff_b = (n0 + lrow) * kb_row + lchk * 16;
+  const int lds_w = lrow * ROWB + ((lchk ^ ((lrow >> 1) & (CPR - 1))) * 16);
+  // Scale loads: one row per thread (A rows for tid < 256, then B rows).
+  const bool srow_a = wave < BM / 64;
+  const uint32_t soff = srow_a ? (m0 + tid) * ks_row : (n0 + tid - BM) * ks_row;
+  const __amdgpu_buffer_rsrc_t rs = srow_a ? rsa : rsb;
+
+  uint4 creg[CODE_LOADS];
+  uint2 sreg;
+  auto gload_code = [&](int j, int kt) {
+    const uint32_t kc = (uint32_t)kt * ROWB;
+    if (j < JA) creg[j] = bload16(ra, goff_a, (uint32_t)(j * RPL) * kb_row + kc);
+    else creg[j] = bload16(rb, goff_b, (uint32_t)((j - JA) * RPL) * kb_row + kc);
+  };
+  auto gload_scales = [&](int kt) { sreg = bload8(rs, soff, (uint32_t)kt * SCB); };
+  auto stage = [&](int j, int buf, int kt_next) {
+    *reinterpret_cast<uint4*>(&lds_c[buf][lds_w + j * RPL * ROWB]) = creg[j];
+    gload_code(j, kt_next);
+  };
+  auto stage_scales = [&](int buf, int kt_next) {
+    *reinterpret_cast<uint2*>(&lds_s[buf][tid * SCB]) =
+        make_uint2(__builtin_amdgcn_perm(sreg.y, sreg.x, 0x06040200u), __builtin_amdgcn_perm(sreg.y, sreg.x, 0x07050301u));
+    gload_scales(kt_next);
+  };
+
+  v16f acc[FM8][FN8];
+#pragma unroll
+  for (int i = 0; i < FM8; ++i)
+#pragma unroll
+    for (int j = 0; j < FN8; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Fragment reads as k_gemm's: every row a lane reads is lr plus a multiple
+  // of 32, so one swizzled chunk position serves all its fragments.
+  const int T = (g ^ ((lr >> 1) & (CPR - 1))) * 16;
+  const int a_lane = (wm * WM8 + lr) * ROWB, b_lane = (BM + wn * WN8 + lr) * ROWB;
+  auto frag = [&](const uint8_t* L, int f, int k) {
+    const int sw = T ^ (32 * k);
+    return f < FM8 ? *reinterpret_cast<const uint4*>(L + a_lane + sw + f * 32 * ROWB)
+                   : *reinterpret_cast<const uint4*>(L + b_lane + sw + (f - FM8) * 32 * ROWB);
+  };
+  const int arow0 = wm * WM8 + lr, brow0 = BM + wn * WN8 + lr;
+  uint32_t sa[FM8], sb[FN8];
+  uint4 a[2][FM8], b[2][FN8];
+  auto read_scales = [&](const uint8_t* S) {
+#pragma unroll
+    for (int i = 0; i < FM8; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(S + (arow0 + 32 * i) * SCB + 4 * g);
+#pragma unroll
+    for (int j = 0; j < FN8; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(S + (brow0 + 32 * j) * SCB + 4 * g);
+  };
+  auto read_frags = [&](const uint8_t* L, int s, int dst) {
+#pragma unroll
+    for (int i = 0; i < FM8; ++i) a[dst][i] = frag(L, i, s);
+#pragma unroll
+    for (int j = 0; j < FN8; ++j) b[dst][j] = frag(L, FM8 + j, s);
+  };
+
+#pragma unroll
+  for (int j = 0; j < CODE_LOADS; ++j) gload_code(j, 0);
+  gload_scales(0);
+#pragma unroll
+  for (int j = 0; j < CODE_LOADS; ++j) stage(j, 0, nk > 1 ? 1 : 0);
+  stage_scales(0, nk > 1 ? 1 : 0);
+  __syncthreads();
+
+  read_scales(lds_s[0]);
+  read_frags(lds_c[0], 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+    uint32_t sa_keep[FM8], sb_keep[FN8];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int cur = s & 1;
+      if (s == NS - 1) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM8; ++i) sa_keep[i] = sa[i];
+#pragma unroll
+        for (int j = 0; j < FN8; ++j) sb_keep[j] = sb[j];
+        read_scales(lds_s[buf ^ 1]);
+        read_frags(lds_c[buf ^ 1], 0, cur ^ 1);
+      } else {
+        read_frags(lds_c[buf], s + 1, cur ^ 1);
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (s * PER + q < CODE_LOADS) stage(s * PER + q, buf ^ 1, kn);
+        if (s == NS - 2) stage_scales(buf ^ 1, kn);
+      }
+      const uint32_t* SA = (s == NS - 1) ? sa_keep : sa;
+      const uint32_t* SB = (s == NS - 1) ? sb_keep : sb;
+#pragma unroll
+      for (int i = 0; i < FM8; ++i) {
+        const v8i av = {(int)a[cur][i].x, (int)a[cur][i].y, (int)a[cur][i].z, (int)a[cur][i].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < FN8; ++j) {
+          const v8i bv = {(int)b[cur][j].x, (int)b[cur][j].y, (int)b[cur][j].z, (int)b[cur][j].w, 0, 0, 0, 0};
+          acc[i][j] = mfma_mx_sel(s, bv, av, acc[i][j], (int)SB[j], (int)SA[i]);
+        }
+      }
+      if (s < NS - 1) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FM8 + FN8, 0);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM8 * FN8 - 2 * PER > 0 ? FM8 * FN8 - 2 * PER : 0, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * (FM8 + FN8), 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FM8 * FN8, 0);
+      }
+    }
+  }
+
+  // Epilogue: lane l of fragment (i, j) holds output row 32 i + l % 32 of the
+  // wave's 128 and columns 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 of its 64.
+  constexpr int ES = BF16OUT ? 2 : 4;
+  const uint32_t row0 = m0 + wm * WM8, col0 = n0 + wn * WN8;
+  auto out_at = [&](uint32_t row, uint32_t col) {
+    return static_cast<uint8_t*>(cout) + ((int64_t)row * ldc + col) * ES;
+  };
+  if (vec_ok && m0 + BM <= M && n0 + BN <= N) {
+    constexpr int PITCH = 68 * ES;
+    static_assert(8 * 32 * PITCH <= 2 * (LDS_CODES + LDS_SCALES), "output staging exceeds the LDS tiles");
+    __syncthreads();
+    uint8_t* stg = lds + wave * 32 * PITCH;
+#pragma unroll
+    for (int i = 0; i < FM8; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN8; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f y = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          uint8_t* d = stg + lr * PITCH + (j * 32 + 8 * q + 4 * g) * ES;
+          if constexpr (BF16OUT) {
+            const v2bf lo = __builtin_convertvector((v2f){y[0], y[1]}, v2bf);
+            const v2bf hi = __builtin_convertvector((v2f){y[2], y[3]}, v2bf);
+            *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          } else {
+            *reinterpret_cast<v4f*>(d) = y;
+          }
+        }
+      }
+      constexpr int LPR = 64 * ES / 16;   // lanes per 64-output row
+      constexpr int RPS = 64 / LPR;       // rows per store instruction
+#pragma unroll
+      for (int k = 0; k < 32 / RPS; ++k) {
+        const int rr = k * RPS + lane / LPR;
+        const int cc = (lane % LPR) * (16 / ES);
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * PITCH + cc * ES);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM8; ++i) {
+      const uint32_t row = row0 + i * 32 + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN8; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t col = col0 + j * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (col >= N) continue;
+          const float y = acc[i][j][r];
+          if constexpr (BF16OUT) {
+            const v2bf bb = __builtin_convertvector((v2f){y, y}, v2bf);
+            *reinterpret_cast<uint16_t*>(out_at(row, col)) = __builtin_bit_cast(uint16_t, bb[0]);
+          } else {
+            *reinterpret_cast<float*>(out_at(row, col)) = y;
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum of the `split` FP32 partial tiles of each split output tile, in split
 // order, times alpha (NVFP4: s_gA * s_gB), converted and stored. Workgroup
 // (tile tt, 32-row slab): lane c of a row holds its columns 4c .. 4c+3, so
@@ -686,7 +917,17 @@ void launch(const GemmArgs& g, hipStream_t s) {
   const int64_t es = g.bf16out ? 2 : 4;
   const uint32_t vec_ok = (g.ldc * es) % 16 == 0 && reinterpret_cast<uintptr_t>(g.c) % 16 == 0;
   float* part = p.ntail ? g.split_ws : nullptr;
-  if (p.nfull) {
+  if (p.nfull && FMT == MX && BK == 256) {
+    const dim3 grid((p.nfull + NXCD - 1) / NXCD * NXCD);
+    if (g.bf16out)
+      hipLaunchKernelGGL((k_gemm_mx8<true>), grid, dim3(512), 0, s, g.a_codes, g.a_scales, g.b_codes, g.b_scales,
+                         (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, p.tiles_m, p.tiles_n, group_m, p.nfull, g.c,
+                         g.ldc, vec_ok);
+    else
+      hipLaunchKernelGGL((k_gemm_mx8<false>), grid, dim3(512), 0, s, g.a_codes, g.a_scales, g.b_codes, g.b_scales,
+                         (uint32_t)g.M, (uint32_t)g.N, (uint32_t)g.K, p.tiles_m, p.tiles_n, group_m, p.nfull, g.c,
+                         g.ldc, vec_ok);
+  } else if (p.nfull) {
     const dim3 grid((p.nfull + NXCD - 1) / NXCD * NXCD);
     if (g.bf16out)
       hipLaunchKernelGGL((k_gemm<FMT, BK, true, false>), grid, block, 0, s, g.a_codes, g.a_scales, g.b_codes,

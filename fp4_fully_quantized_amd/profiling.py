@@ -120,7 +120,7 @@ PROFILE_COMMANDS = {
 # flops per launch is computed by the benchmark itself).
 GROUPS = [
     ("NVFP4 GEMM (fwd bf16 out; dgrad, wgrad fp32 out)", r"^k_gemm<0,"),
-    ("MXFP4 GEMM (fwd, bf16 out)", r"^k_gemm<1,"),
+    ("MXFP4 GEMM (fwd, bf16 out)", r"^k_gemm(<1,|_mx8<)"),
     ("quantize, both orientations from one read", r"^k_quant_dual(_w3)?<"),
     ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
     ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
@@ -173,7 +173,7 @@ STEP_DISPATCHES = [
     ("NVFP4 GEMM wgrad (fp32 out)", r"^k_gemm<0, 256, false, false>", _GF, 0),
     ("MXFP4+Hadamard X", r"^k_quant_cols<1,", _MX * _NX, _NX),
     ("MXFP4+Hadamard W", r"^k_quant_cols<1,", _MX * _NW, _NW),
-    ("MXFP4 GEMM fwd (bf16 out)", r"^k_gemm<1, 256, true, false>", _GF, 0),
+    ("MXFP4 GEMM fwd (bf16 out)", r"^k_gemm_mx8<true>", _GF, 0),
 ]
 EXTRA_DISPATCHES = [
     ("amax dY rotated 16-wide along tokens", r"^k_amax_rot_rows<", 2 * _NY, _NY),
@@ -422,8 +422,9 @@ def summarize_trace(out_dir: str, profiles_dir: str) -> None:
         "first launches of a run are slower while the clock settles); that is the figure to set against the "
         "benchmark's HIP-event times.",
         "",
-        "`k_gemm<0, 256, *, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm<1, 256, *, *>` = MXFP4 GEMM (scaled FP4 MFMA); "
-        "the third template flag = bf16 output, the fourth = a split-K piece (none in this step).",
+        "`k_gemm<0, 256, *, *>` = NVFP4 GEMM (f16 MFMA), `k_gemm_mx8<*>` (whole tiles) and `k_gemm<1, *, *, *>` "
+        "= MXFP4 GEMM (scaled FP4 MFMA); the bf16 flag = bf16 output, the last `k_gemm` flag = a split-K piece "
+        "(none in this step).",
         "",
         "## Kernel groups (from the kernel trace)",
         "",

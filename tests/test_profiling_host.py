@@ -16,7 +16,7 @@ def _names(steps, warmup):
             "k_amax<true, false>", "k_quant_dual<0, 1, 1, true, false, false, false>",
             "k_gemm<0, 256, false, false>", "k_gemm<0, 256, false, false>",
             "k_quant_cols<1, 0, true, true, false>", "k_quant_cols<1, 0, true, true, false>",
-            "k_gemm<1, 256, true, false>"]
+            "k_gemm_mx8<true>"]
     extras = ["k_amax_rot_rows<true>", "k_amax_pair<true, false, true>",
               "k_quant_dual<0, 0, 1, true, false, true, false>", "k_amax_pair<true, false, true>",
               "k_quant_dual<0, 1, 1, true, false, true, false>", "k_amax<true, false>",
