@@ -284,9 +284,10 @@ __device__ __forceinline__ void quant_dual_body(
 }
 
 // The kernels. The NVFP4 bf16 noise-monitored variants ask for 3 waves per
-// SIMD (at most 168 registers, which they fit without spilling), so that 3
-// workgroups run on each CU; the others need about 100 registers, or their
-// LDS (fp32 input) allows only 2 workgroups per CU anyway.
+// SIMD (at most 168 registers; a few loop-invariant 64-bit values then live in
+// scratch, reloaded once per tile), so that 3 workgroups run on each CU; the
+// others need about 100 registers, or their LDS (fp32 input) allows only 2
+// workgroups per CU anyway.
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
 __global__ __launch_bounds__(256) void k_quant_dual(
     const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
