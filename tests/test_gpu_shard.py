@@ -101,6 +101,28 @@ def test_shards_equal_the_whole_tensor_quantization(fp4, orc, fmt, rnd, axis, ha
         assert_same_quant(q_to_host(q), _slice(want, o, n, axis, B), f"shard at row {o}")
 
 
+@pytest.mark.parametrize("had", [False, True])
+def test_nvfp4_row_shards_on_16_row_boundaries(fp4, orc, had):
+    """NVFP4 blocks down the columns are 16 rows: shards may start on any
+    multiple of 16 (here 48, 256), with and without the 16-wide rotation."""
+    import torch
+    sizes = [48, 208, 160]
+    total, C = sum(sizes), 544
+    say("quantize_shard NVFP4 rows on 16-row boundaries", sizes, "had", had)
+    xh = _data((total, C), 95)
+    signs = orc.hadamard_signs(12) if had else 0
+    want = orc.quantize(xh, axis=1, fmt=0, rnd=1, seed=41, index_offset=0, had_on=had, had_signs=signs)
+    x = to_device(xh)
+    shards = [x[o:o + n] for o, n in _bounds(sizes)]
+    amax = _global_amax(fp4, shards, 0, 1, signs)
+    for (o, n), xs in zip(_bounds(sizes), shards):
+        q = fp4.QTensor(C, n, 0, had_signs=signs if had else None)
+        q.amax.copy_(amax)
+        fp4.fp4_quantize_shard(xs, o, total, 1, 1, 41, 0, True, q)
+        torch.cuda.synchronize()
+        assert_same_quant(q_to_host(q), _slice(want, o, n, 1, 16), f"16-row shard at row {o}")
+
+
 def test_single_shard_equals_fp4_quantize(fp4, orc):
     """row_offset 0, rows_total R: the plain quantization, amax computed in the call."""
     xh = _data((128, 512), 5)
