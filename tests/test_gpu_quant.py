@@ -473,6 +473,40 @@ def _tiny(shape, seed, scale):
 TINY = [1e-32, 2.0 ** -99, 1e-38, 3e-39]   # below the NVFP4 floor, just above it, FP32 subnormal range
 
 
+# Large and small tensor scales: amaxes that put s_g = amax / 2688 at exactly
+# 2^-80 and 2^100 and at the bf16 neighbours either side (2688 = 21 * 2^7; the
+# bf16 values next to it are 2672 and 2704), so that the tensor's values reach
+# about 2^111 and its block scales span dozens of binades below s_g.
+SG_EDGES = [2688.0 * 2.0 ** -80, 2672.0 * 2.0 ** -80, 2704.0 * 2.0 ** -80,
+            2688.0 * 2.0 ** 100, 2704.0 * 2.0 ** 100, 2672.0 * 2.0 ** 100]
+
+
+@pytest.mark.parametrize("amax", SG_EDGES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_large_and_small_tensor_scales(fp4, orc, amax, bf16):
+    """NVFP4 tensors with s_g near 2^-80 and 2^100: codes, scale bytes and s_g
+    equal the oracle's for both axes, RTN and SR, and the dual pass."""
+    say("large and small tensor scales", amax, "bf16", bf16)
+    rng = np.random.default_rng(17)
+    x = (rng.uniform(-1.0, 1.0, (64, 256)) * rng.choice([1.0, 2.0 ** -6, 2.0 ** -14], (64, 256))
+         * (0.999 * amax)).astype(np.float32)
+    x[3, 5] = amax
+    x[40, 200] = -amax
+    xh = orc.f32_to_bf16_bits(x) if bf16 else x
+    if bf16:   # the bf16 amax must still be the one chosen
+        assert float(np.max(np.abs(orc.bf16_bits_to_f32(xh)))) == amax
+    for axis in (0, 1):
+        for rnd in (0, 1):
+            want = orc.quantize(xh, axis=axis, fmt=0, rnd=rnd, seed=9)
+            q = fp4.quantize(to_device(xh), axis=axis, fmt=0, rnd=rnd, seed=9)
+            assert_same_quant(q_to_host(q), want, f"axis {axis} rnd {rnd}")
+    want_c = orc.quantize(xh, axis=0, fmt=0, rnd=0)
+    want_r = orc.quantize(xh, axis=1, fmt=0, rnd=1, seed=4)
+    qc, qr = fp4.quantize_dual(to_device(xh), fmt=0, rnd_cols=0, rnd_rows=1, seed_rows=4)
+    assert_same_quant(q_to_host(qc), want_c, "dual, blocks along C")
+    assert_same_quant(q_to_host(qr), want_r, "dual, blocks along R")
+
+
 @pytest.mark.parametrize("scale", TINY)
 @pytest.mark.parametrize("fmt,axis", [(0, 0), (0, 1), (1, 0)])
 @pytest.mark.parametrize("bf16", [False, True])
