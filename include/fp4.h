@@ -170,11 +170,10 @@ fp4_status fp4_quantize(const void* src, fp4_dtype src_t, int64_t R, int64_t C, 
                         fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                         int amax_ready, fp4_tensor* out, fp4_stream_t stream);
 
-/* Both orientations of one R x C source from a single read of it (the
- * "read once, emit both" fusion of the two quantizations that a linear layer's
- * backward pass needs for dY and X; FP4 All the Way, Key points: every GEMM
- * operand blocked along its contraction dimension). Equivalent, bit for bit,
- * to
+/* Both orientations of one R x C source from a single read of it, in place
+ * of the two quantizations a linear layer's backward pass needs for dY and X
+ * (FP4 All the Way, Key points: every GEMM operand blocked along its
+ * contraction dimension). Equivalent, bit for bit, to
  *   fp4_quantize(src, ..., FP4_AXIS_COLS, rnd_cols, seed_cols, index_offset_cols, ..., out_cols)
  *   fp4_quantize(src, ..., FP4_AXIS_ROWS, rnd_rows, seed_rows, index_offset_rows, ..., out_rows)
  * with each call's amax_ready set as below.
@@ -224,12 +223,13 @@ fp4_status fp4_quantize_shard(const void* src, fp4_dtype src_t, int64_t R, int64
                               uint64_t seed, uint64_t index_offset, int amax_ready, fp4_tensor* out,
                               double* noise, fp4_stream_t stream);
 
-/* fp4_quantize_dual of a row shard, each orientation's stochastic-rounding
- * index that of the whole tensor (as fp4_quantize_shard with axis COLS for
- * out_cols and axis ROWS for out_rows); noise_cols, noise_rows: NULL or the
- * sums of fp4_quantize_dual_noise for either orientation. Requires
- * row_offset % B == 0 and the other conditions of fp4_quantize_shard;
- * otherwise as fp4_quantize_dual. */
+/* fp4_quantize_dual of a row shard (the data-parallel split of
+ * fp4_quantize_shard, "FP4 All the Way", Key points), each orientation's
+ * stochastic-rounding index that of the whole tensor (as fp4_quantize_shard
+ * with axis COLS for out_cols and axis ROWS for out_rows); noise_cols,
+ * noise_rows: NULL or the sums of fp4_quantize_dual_noise for either
+ * orientation. Requires row_offset % B == 0 and the other conditions of
+ * fp4_quantize_shard; otherwise as fp4_quantize_dual. */
 fp4_status fp4_quantize_dual_shard(const void* src, fp4_dtype src_t, int64_t R, int64_t C, int64_t ld,
                                    int64_t row_offset, int64_t rows_total, fp4_rounding rnd_cols,
                                    uint64_t seed_cols, uint64_t index_offset_cols, fp4_rounding rnd_rows,
@@ -258,8 +258,9 @@ fp4_status fp4_quantize_noise(const void* src, fp4_dtype src_t, int64_t R, int64
                               fp4_axis axis, fp4_rounding rnd, uint64_t seed, uint64_t index_offset,
                               int amax_ready, fp4_tensor* out, double* noise, fp4_stream_t stream);
 
-/* fp4_quantize_dual with the noise monitor of fp4_quantize_noise on either
- * orientation: noise_cols for out_cols, noise_rows for out_rows (each two
+/* fp4_quantize_dual with the noise monitor of fp4_quantize_noise ("FP4 All
+ * the Way", Summary: the gradient-noise threshold) on either orientation:
+ * noise_cols for out_cols, noise_rows for out_rows (each two
  * device doubles, accumulated into, or NULL to skip; FP4_ERR_NULL if both are
  * NULL). Partials are per block in both orientations. Otherwise as
  * fp4_quantize_dual. */
@@ -371,7 +372,9 @@ typedef struct fp4_operand {
     uint32_t reserved;
 } fp4_operand;
 
-/* Bytes of device workspace fp4_gemm needs for these operands: for each RAW
+/* Bytes of device workspace fp4_gemm needs for these operands (RAW operands
+ * are quantized there first, as every GEMM operand of a fully quantized
+ * linear layer is: Quartet, Approach): for each RAW
  * operand, in the order A then B, its codes, its scale bytes and (NVFP4) its
  * two FP32 scalars, each piece starting on a 256-byte boundary. 0 when
  * neither operand is RAW, or when an operand is NULL or its kind, format,
