@@ -525,15 +525,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
             }
           }
         }
-        // Read back 16 bytes per lane: a row of 128 outputs is 128 * ES / 16 lanes.
+        // Read back 16 bytes per lane: a row of 128 outputs is 128 * ES / 16
+        // lanes. All of the 32 rows' LDS reads go out before the first store
+        // (the scheduling barrier keeps the compiler from pairing each read
+        // with its store, which made every store wait for its own read's
+        // round trip).
         constexpr int LPR = 128 * ES / 16;  // lanes per row
         constexpr int RPS = 64 / LPR;       // rows per store instruction
+        constexpr int NST = 32 / RPS;       // store instructions per 32 rows
+        uint4 v[NST];
 #pragma unroll
-        for (int k = 0; k < 32 / RPS; ++k) {
+        for (int k = 0; k < NST; ++k) {
           const int rr = k * RPS + lane / LPR;
           const int cc = (lane % LPR) * (16 / ES);
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH + cc * ES);
-          __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
+          v[k] = *reinterpret_cast<const uint4*>(stage + rr * PITCH + cc * ES);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+          const int rr = k * RPS + lane / LPR;
+          const int cc = (lane % LPR) * (16 / ES);
+          __builtin_nontemporal_store(__builtin_bit_cast(v4u, v[k]), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
         }
       }
     } else {
@@ -769,12 +781,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx8(const uint8_t* __restrict__
       }
       constexpr int LPR = 64 * ES / 16;   // lanes per 64-output row
       constexpr int RPS = 64 / LPR;       // rows per store instruction
+      constexpr int NST = 32 / RPS;       // store instructions per 32 rows
+      uint4 v[NST];                       // all LDS reads before the stores, as in k_gemm
 #pragma unroll
-      for (int k = 0; k < 32 / RPS; ++k) {
+      for (int k = 0; k < NST; ++k) {
         const int rr = k * RPS + lane / LPR;
         const int cc = (lane % LPR) * (16 / ES);
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * PITCH + cc * ES);
-        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
+        v[k] = *reinterpret_cast<const uint4*>(stg + rr * PITCH + cc * ES);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NST; ++k) {
+        const int rr = k * RPS + lane / LPR;
+        const int cc = (lane % LPR) * (16 / ES);
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v[k]), reinterpret_cast<v4u*>(out_at(row0 + i * 32 + rr, col0 + cc)));
       }
     }
   } else {
