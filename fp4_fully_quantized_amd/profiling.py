@@ -15,6 +15,11 @@ profiles/traffic.json that the benchmark's roofline figure reads.
     python -m fp4_fully_quantized_amd.profiling summarize-trace OUT
 
 writes only the kernel-time summaries, from the kernel-trace run ("stats").
+
+    python -m fp4_fully_quantized_amd.profiling summarize-lds OUT
+
+writes only the GEMMs' LDS summary per K tile, from the "lds" counter run
+(summarize includes it when that run's folder is there).
 """
 import sys
 
@@ -110,6 +115,10 @@ PROFILE_COMMANDS = {
             "GRBM_GUI_ACTIVE --kernel-include-regex \"k_gemm|k_quant|k_amax\" --output-format csv "
             "-d OUT/pmc_util -o bench -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline "
             "--no-large-step --no-shard-step",
+    "lds": "rocprofv3 --pmc SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+           "SQ_WAVE_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE --kernel-include-regex \"k_gemm|k_quant|k_amax\" "
+           "--output-format csv -d OUT/pmc_lds -o bench -- python3 bench.py --steps 1 --warmup 1 "
+           "--no-cpu-baseline --no-large-step --no-shard-step",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o copy -- "
                   "python3 -m fp4_fully_quantized_amd.profiling copy",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o copy -- "
@@ -601,19 +610,90 @@ def summarize_counters(out_dir: str, profiles_dir: str) -> None:
     with open(os.path.join(profiles_dir, "llama7b_step_mfma_valu_utilisation.md"), "w") as f:
         f.write("\n".join(lines))
 
+    if os.path.isdir(os.path.join(out_dir, "pmc_lds")):
+        summarize_lds(out_dir, profiles_dir)
+
     with open(os.path.join(profiles_dir, "traffic.json"), "w") as f:
         json.dump({"nv_gemm_bytes_per_launch": round(avg), "source_digest": source_digest(),
                    "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}, f, indent=1)
         f.write("\n")
 
 
+# The step's GEMMs: (label in STEP_DISPATCHES, K, output tiles of 256 x 256, threads per workgroup).
+_STEP_GEMMS = [
+    ("NVFP4 GEMM fwd (bf16 out)", D_IN, (TOKENS // 256) * -(-D_OUT // 256), 256),
+    ("NVFP4 GEMM dgrad (fp32 out)", D_OUT, (TOKENS // 256) * (D_IN // 256), 256),
+    ("NVFP4 GEMM wgrad (fp32 out)", TOKENS, -(-D_OUT // 256) * (D_IN // 256), 256),
+    ("MXFP4 GEMM fwd (bf16 out)", D_IN, (TOKENS // 256) * -(-D_OUT // 256), 512),
+]
+
+
+def summarize_lds(out_dir: str, profiles_dir: str) -> None:
+    """LDS work and waits of the step's GEMMs per K tile of 256 (one workgroup's
+    256 x 256 output tile over 256 K values), from the "lds" counter run."""
+    import os
+
+    cmd = PROFILE_COMMANDS["lds"]
+    dd = _per_dispatch(os.path.join(out_dir, "pmc_lds", "bench_counter_collection.csv"))
+    labels = label_dispatches([n for n, _, _ in dd], PMC_STEPS, PMC_WARMUP)
+    shapes = {l: (k, t, th) for l, k, t, th in _STEP_GEMMS}
+    agg = {}
+    for (l, _, _), (_, c, dur) in zip(labels, dd):
+        if l not in shapes:
+            continue
+        k, tiles, _ = shapes[l]
+        units = tiles * (k // 256)                   # workgroup K tiles of the dispatch
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        a = agg.setdefault(l, [0] + [0.0] * 9)
+        a[0] += 1
+        a[1] += dur
+        a[2] += cyc * CUS / units                    # CU cycles per K tile
+        a[3] += c["SQ_INSTS_LDS"] / units
+        a[4] += c["SQ_INSTS_MFMA"] / units
+        a[5] += c["SQ_LDS_BANK_CONFLICT"] / units
+        a[6] += c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+        a[7] += c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]
+        a[8] += c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]
+        a[9] += c["SQ_ACTIVE_INST_LDS"] / units
+    lines = [
+        "# LDS work and waits per K tile of the Llama-7B step's GEMMs",
+        "",
+        "Command (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; "
+        "`OUT` = the folder the run writes its CSV files to):",
+        "",
+        "```", cmd, "```",
+        "",
+        "A K tile here is one workgroup's 256 x 256 output tile over 256 values of K: the unit of the GEMMs' "
+        "K loop (staging writes of the next tile's operands, fragment reads, one barrier). Per dispatch, "
+        "averaged over the run's launches: `CU cycles / K tile` = the kernel's cycles (GRBM_GUI_ACTIVE / "
+        f"{XCDS}) x {CUS} CUs / (output tiles x K / 256), so it includes each tile's prologue and epilogue; "
+        "`LDS instr`, `MFMA instr`, `active LDS` (SQ_ACTIVE_INST_LDS) and `conflict` (SQ_LDS_BANK_CONFLICT) "
+        "are the counters' sums over the dispatch divided by its K tiles; `conflict / active LDS` and the "
+        "two wait fractions (SQ_WAIT_INST_LDS and SQ_WAIT_ANY over SQ_WAVE_CYCLES, summed over waves) are "
+        "ratios of the counters as the hardware reports them. The NVFP4 kernel runs 4 waves per workgroup "
+        "(one per SIMD, 128 x 128 outputs each), the MXFP4 kernel 8 (two per SIMD, 128 x 64 each).",
+        "",
+        "| GEMM | launches | avg us | CU cycles / K tile | LDS instr / K tile | MFMA instr / K tile | "
+        "active LDS / K tile | conflict / K tile | conflict / active LDS | LDS wait / wave cycles | "
+        "any wait / wave cycles |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for l, (n, dur, cpk, lds, mfma, conf, cfr, wl, wa, act) in agg.items():
+        lines.append(f"| {l} | {n} | {dur / n / 1e3:.1f} | {cpk / n:.0f} | {lds / n:.0f} | {mfma / n:.0f} | "
+                     f"{act / n:.0f} | {conf / n:.0f} | {cfr / n:.3f} | {wl / n:.3f} | {wa / n:.3f} |")
+    lines.append("")
+    with open(os.path.join(profiles_dir, "gemm_llama7b_lds_per_k_tile.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "copy":
         copy()
-    elif len(sys.argv) > 2 and sys.argv[1] in ("summarize", "summarize-trace"):
+    elif len(sys.argv) > 2 and sys.argv[1] in ("summarize", "summarize-trace", "summarize-lds"):
         import os
 
         prof = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
-        (summarize if sys.argv[1] == "summarize" else summarize_trace)(sys.argv[2], prof)
+        {"summarize": summarize, "summarize-trace": summarize_trace,
+         "summarize-lds": summarize_lds}[sys.argv[1]](sys.argv[2], prof)
     else:
         print(__doc__)

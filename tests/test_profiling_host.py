@@ -190,3 +190,35 @@ def test_code_digest_ignores_comments_only():
     assert code_digest([a]) != code_digest([c])
     # the files are hashed as separate texts
     assert code_digest([a, c]) != code_digest([c, a])
+
+
+def test_summarize_lds_on_synthetic_counters(tmp_path):
+    """summarize_lds() on made-up counters whose per-K-tile figures are known:
+    every GEMM dispatch reports 1000 LDS and 64 MFMA instructions per K tile,
+    2 GHz over 1 ms, and waits of a tenth (LDS) and a fifth (any) of its wave
+    cycles."""
+    out, prof = tmp_path / "out", tmp_path / "profiles"
+    prof.mkdir()
+    names = _names(p.PMC_STEPS, p.PMC_WARMUP)
+    labels = p.label_dispatches(names, p.PMC_STEPS, p.PMC_WARMUP)
+    units = {l: t * (k // 256) for l, k, t, _ in p._STEP_GEMMS}
+    ph = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+          "End_Timestamp"]
+    rows = []
+    cyc, dur = 2_000_000, 1_000_000
+    for i, (n, (l, _, _)) in enumerate(zip(names, labels)):
+        u = units.get(l, 1)
+        t0 = 10_000_000 * (i + 1)
+        row = lambda c, v: [i + 1, _raw(n), 1024, c, v, t0, t0 + dur]
+        rows += [row("GRBM_GUI_ACTIVE", 8 * cyc), row("SQ_INSTS_LDS", 1000.0 * u), row("SQ_INSTS_MFMA", 64.0 * u),
+                 row("SQ_ACTIVE_INST_LDS", 400.0 * u), row("SQ_LDS_BANK_CONFLICT", 40.0 * u),
+                 row("SQ_WAIT_INST_LDS", 10.0), row("SQ_WAIT_ANY", 20.0), row("SQ_WAVE_CYCLES", 100.0)]
+    _write_csv(str(out / "pmc_lds" / "bench_counter_collection.csv"), ph, rows)
+    p.summarize_lds(str(out), str(prof))
+    t = (prof / "gemm_llama7b_lds_per_k_tile.md").read_text()
+    body = [l for l in t.splitlines() if l.startswith("| ") and not l.startswith("| GEMM")]
+    assert len(body) == 4
+    fwd_units = 128 * 43 * 16
+    assert (f"| NVFP4 GEMM fwd (bf16 out) | 2 | 1000.0 | {cyc * 256 / fwd_units:.0f} | 1000 | 64 | 400 | 40 | "
+            "0.100 | 0.100 | 0.200 |") in t
+    assert "| MXFP4 GEMM fwd (bf16 out) | 2 |" in t
