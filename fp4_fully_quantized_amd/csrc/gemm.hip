@@ -468,10 +468,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ ac,
           // The next substep's decode (64 VALU: 8 fragments x 4 converts + 4
           // multiplies) in groups of five after the MFMAs, so it is done by the
           // 13th MFMA and the last ones leave room for the LDS and memory work
-          // (groups of 4 and 6 measured slower, 3 much slower).
+          // (groups of 4 and 6 measured slower, 3 much slower). The chunk
+          // pair's LDS reads (the next chunk pair's fragments; after the K
+          // tile's barrier also the next tile's scales) go one after each MFMA
+          // of its first substep, and the staging of the next K tile (an LDS
+          // write and a global load) after every other MFMA of its second:
+          // placed by the compiler, the reads came late in the chunk pair, each
+          // followed at once by a wait for it, and the staging as one burst.
 #pragma unroll
           for (int m = 0; m < FM * FN; ++m) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (s == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            if (s == 1 && (m & 1) == 0) {
+              __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            }
             __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
           }
 #pragma unroll
