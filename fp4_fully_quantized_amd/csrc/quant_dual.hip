@@ -65,44 +65,67 @@ __device__ __forceinline__ void quant_dual_body(
   }
   double ngc = 0.0, nec = 0.0, ngr = 0.0, ner = 0.0;  // quantization noise, when asked for
   // One tile per workgroup; with the noise monitor (MON) a capped grid loops
-  // over the tiles.
+  // over the tiles: workgroup b takes tiles b, b + grid, ...
+  constexpr int CPR = T * ES / 16;        // 16-byte pieces per tile row
+  constexpr int NLD = T * CPR / 256;      // 16-byte loads per thread and tile
   const uint32_t n_it = MON ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 1u;
-  for (uint32_t it = 0; it < n_it; ++it) {
-    const uint32_t ti = MON ? blockIdx.x + it * gridDim.x : xcd_contiguous_tile(blockIdx.x, ntiles);
+  const uint32_t t_first = MON ? blockIdx.x : xcd_contiguous_tile(blockIdx.x, ntiles);
+  const uint32_t t_step = MON ? gridDim.x : 0u;
+  // The thread index is taken afresh in each iteration through an opaque
+  // move, so that nothing derived from it is hoisted out of the tile loop
+  // and held in registers across it: the monitored kernels needed 155-168
+  // registers and scratch that way, 100-121 and none this way.
+  const int tid0 = threadIdx.x;
+  auto opaque_tid = [&]() {
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(tid0));
+    return t;
+  };
+  uint4 pre[NLD];
+  // Tile ti's source into pre (16 bytes per load; only edge tiles check bounds).
+  auto load_tile = [&](uint32_t ti, int tid) {
     const uint32_t tr = ti / tiles_c;
-    const uint32_t tc = ti - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * T;
-    const int64_t c0 = (int64_t)tc * T;
-    const int tid = threadIdx.x;
-
-    // 1. tile load, 16 bytes per load; only edge tiles check bounds.
-    constexpr int CPR = T * ES / 16;
+    const int64_t c0 = (int64_t)(ti - tr * tiles_c) * T;
     if (r0 + T <= R && c0 + T <= C) {
 #pragma unroll
-      for (int k = 0; k < T * CPR / 256; ++k) {
+      for (int k = 0; k < NLD; ++k) {
         const int idx = k * 256 + tid;
         const int rr = idx / CPR;
         const int cc = idx % CPR;
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
-                                                        ((r0 + rr) * ld + c0 + cc * (16 / ES)) * ES);
-        uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
-        d[0] = make_uint2(v.x, v.y);
-        d[1] = make_uint2(v.z, v.w);
+        pre[k] = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) +
+                                                 ((r0 + rr) * ld + c0 + cc * (16 / ES)) * ES);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < T * CPR / 256; ++k) {
+      for (int k = 0; k < NLD; ++k) {
         const int idx = k * 256 + tid;
         const int rr = idx / CPR;
         const int cc = idx % CPR;
         const int64_t col = c0 + cc * (16 / ES);
-        uint4 v = make_uint4(0, 0, 0, 0);
+        pre[k] = make_uint4(0, 0, 0, 0);
         if (r0 + rr < R && col < C)
-          v = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
-        uint2* d = reinterpret_cast<uint2*>(&tile[rr * PITCH + cc * 16]);
-        d[0] = make_uint2(v.x, v.y);
-        d[1] = make_uint2(v.z, v.w);
+          pre[k] = *reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((r0 + rr) * ld + col) * ES);
       }
+    }
+  };
+#pragma unroll 1
+  for (uint32_t it = 0; it < n_it; ++it) {
+    const uint32_t ti = t_first + it * t_step;
+    const uint32_t tr = ti / tiles_c;
+    const uint32_t tc = ti - tr * tiles_c;
+    const int64_t r0 = (int64_t)tr * T;
+    const int64_t c0 = (int64_t)tc * T;
+    const int tid = opaque_tid();
+
+    // 1. the tile into LDS
+    load_tile(ti, tid);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int idx = k * 256 + tid;
+      uint2* d = reinterpret_cast<uint2*>(&tile[(idx / CPR) * PITCH + (idx % CPR) * 16]);
+      d[0] = make_uint2(pre[k].x, pre[k].y);
+      d[1] = make_uint2(pre[k].z, pre[k].w);
     }
     __syncthreads();
 
@@ -274,7 +297,7 @@ __device__ __forceinline__ void quant_dual_body(
           scales_r[(c0 + cl) * (R / B) + r0 / B + bb] = stage_s[idx];
       }
     }
-    if constexpr (MON) __syncthreads();  // the next tile reuses the LDS buffers
+    __syncthreads();  // the next tile reuses the LDS buffers
   }
   if constexpr (MON) {
     if (noise_c) noise_reduce(ngc, nec, noise_c);
@@ -283,11 +306,10 @@ __device__ __forceinline__ void quant_dual_body(
   }
 }
 
-// The kernels. The NVFP4 bf16 noise-monitored variants ask for 3 waves per
-// SIMD (at most 168 registers; a few loop-invariant 64-bit values then live in
-// scratch, reloaded once per tile), so that 3 workgroups run on each CU; the
-// others need about 100 registers, or their LDS (fp32 input) allows only 2
-// workgroups per CU anyway.
+// The kernels. The NVFP4 bf16 noise-monitored variants ask for 4 waves per
+// SIMD (at most 128 registers), so that as many workgroups run on each CU as
+// their LDS allows (4); the others need about 100 registers, or their LDS
+// (fp32 input) allows only 2 workgroups per CU anyway.
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
 __global__ __launch_bounds__(256) void k_quant_dual(
     const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(256) void k_quant_dual(
                                                   noise_c, noise_r);
 }
 template <int FMT, int RC, int RR, bool BF16, bool HC, bool HR, bool MON>
-__global__ __launch_bounds__(256, 3) void k_quant_dual_w3(
+__global__ __launch_bounds__(256, 4) void k_quant_dual_w4(
     const void* __restrict__ src, int64_t R, int64_t C, int64_t ld, uint32_t tiles_c, uint32_t ntiles,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c,
     uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
@@ -329,7 +351,7 @@ void launch_dual(const DualArgs& a, hipStream_t s) {
   const uint32_t words_r = (a.R / B) % 4 == 0;
   const uint32_t ntiles = tiles_c * tiles_r;
   const auto kernel = [] {
-    if constexpr (MON && FMT == NV && BF16) return k_quant_dual_w3<FMT, RC, RR, BF16, HC, HR, MON>;
+    if constexpr (MON && FMT == NV && BF16) return k_quant_dual_w4<FMT, RC, RR, BF16, HC, HR, MON>;
     else return k_quant_dual<FMT, RC, RR, BF16, HC, HR, MON>;
   }();
   const uint32_t grid = MON ? noise_grid(kernel, ntiles) : ntiles;
