@@ -130,7 +130,7 @@ PROFILE_COMMANDS = {
 GROUPS = [
     ("NVFP4 GEMM (fwd bf16 out; dgrad, wgrad fp32 out)", r"^k_gemm<0,"),
     ("MXFP4 GEMM (fwd, bf16 out)", r"^k_gemm(<1,|_mx8<)"),
-    ("quantize, both orientations from one read", r"^k_quant_dual(_w3)?<"),
+    ("quantize, both orientations from one read", r"^k_quant_dual(_w4)?<"),
     ("quantize, blocks along the contiguous axis", r"^k_quant_cols<"),
     ("quantize, blocks along rows (transposed output)", r"^k_quant_rows<"),
     ("tensor amax", r"^k_amax(_flat)?<"),
@@ -193,7 +193,7 @@ EXTRA_DISPATCHES = [
     ("amax W (2-D)", r"^k_amax(_flat)?<", 2 * _NW, _NW),
     ("2-D 16x16 W", r"^k_quant_2d<", _DUAL * _NW, 2 * _NW),
     ("amax dY (monitored)", r"^k_amax(_flat)?<", 2 * _NY, _NY),
-    ("dual dY + noise monitor", r"^k_quant_dual_w3<0, 1, 1, true, false, false, true>", _DUAL * _NY, 2 * _NY),
+    ("dual dY + noise monitor", r"^k_quant_dual_w4<0, 1, 1, true, false, false, true>", _DUAL * _NY, 2 * _NY),
 ]
 
 
