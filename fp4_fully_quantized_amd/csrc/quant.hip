@@ -357,11 +357,12 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ src
     const uint32_t tc = ti - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * TR;
     const int64_t c0 = (int64_t)tc * TC;
-    // The thread index through an opaque move in each iteration: otherwise the
-    // compiler hoists the thread-dependent addresses out of the tile loop and
-    // keeps them live across it.
-    int tid;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    // With the monitor's tile loop, the thread index through an opaque move in
+    // each iteration: otherwise the compiler hoists the thread-dependent
+    // addresses out of the loop and keeps them live across it. (Without the
+    // loop the plain index lets it use what it knows of the index's range.)
+    int tid = threadIdx.x;
+    if constexpr (MON) asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
 
     // 1. tile load: TR rows of TC * ES bytes, 16 bytes per load; only edge
     //    tiles check bounds.

@@ -71,10 +71,13 @@ __device__ __forceinline__ void quant_dual_body(
   const uint32_t n_it = MON ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 1u;
   const uint32_t t_first = MON ? blockIdx.x : xcd_contiguous_tile(blockIdx.x, ntiles);
   const uint32_t t_step = MON ? gridDim.x : 0u;
-  // The thread index is taken afresh in each iteration through an opaque
-  // move, so that nothing derived from it is hoisted out of the tile loop
-  // and held in registers across it: the monitored kernels needed 155-168
-  // registers and scratch that way, 100-121 and none this way.
+  // With the monitor the thread index is taken afresh in each iteration
+  // through an opaque move, so that nothing derived from it is hoisted out of
+  // the tile loop and held in registers across it: the monitored kernels
+  // needed 155-168 registers and scratch that way, 100-121 and none this way.
+  // (The single-tile kernels keep the plain index, whose known range makes
+  // their address arithmetic cheaper: 1915 against 2212 VALU instructions in
+  // the dY kernel.)
   const int tid0 = threadIdx.x;
   auto opaque_tid = [&]() {
     int t;
@@ -116,7 +119,7 @@ __device__ __forceinline__ void quant_dual_body(
     const uint32_t tc = ti - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * T;
     const int64_t c0 = (int64_t)tc * T;
-    const int tid = opaque_tid();
+    const int tid = MON ? opaque_tid() : tid0;   // (one iteration without the monitor)
 
     // 1. the tile into LDS
     load_tile(ti, tid);
